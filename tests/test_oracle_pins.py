@@ -1,0 +1,304 @@
+"""Pins of the CPU oracle to facts outside itself (no GPU needed).
+
+Each test checks the oracle against something it does not compute itself:
+hand-worked examples (tests/golden/worked_examples.json), closed forms,
+brute force on tiny inputs, library routines with known semantics, and
+invariants the equations imply.  A plausible slip in the oracle (dropped eps,
+wrong tie rule, swapped operand, wrong bit position in the packing, wrong
+order of rescale) fails at least one of them."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from datagen import random_case, gaussian_weights
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+@pytest.fixture(scope="module")
+def gold():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def f32(a):
+    return np.asarray(a, dtype=np.float32)
+
+
+# ----------------------------------------------------------------- weights --
+@pytest.mark.parametrize("case", ["weights_basic", "weights_eps_placement", "weights_ties"])
+def test_weights_worked(gold, case):
+    g = gold[case]
+    w = f32(g["w"])
+    gamma = O.absmean_gamma(w)
+    assert gamma == np.float32(g["gamma"])
+    codes = O.ternary_codes(w, gamma, np.float32(g["eps"]))
+    np.testing.assert_array_equal(codes, np.array(g["codes"], dtype=np.int8))
+    if "codes_if_divisor_max" in g:
+        alt = O.ternary_codes(w, gamma, np.float32(g["eps"]), divisor="max")
+        np.testing.assert_array_equal(alt, np.array(g["codes_if_divisor_max"], dtype=np.int8))
+
+
+def test_gamma_matches_exact_sum():
+    # math.fsum returns the correctly rounded sum; the oracle's fp64 sum must
+    # round to the same fp32 gamma.
+    for seed in range(5):
+        w, _ = random_case(100 + seed, 1, 300, 257)
+        exact = math.fsum(abs(float(v)) for v in w.ravel()) / w.size
+        assert O.absmean_gamma(w) == np.float32(exact)
+
+
+def test_gamma_closed_forms():
+    assert O.absmean_gamma(np.full((3, 5), -0.375, np.float32)) == np.float32(0.375)
+    # mean of |k/64| for k = -32..31 over 64 entries = (32*33/2 + 31*32/2)/64/64
+    w = (np.arange(-32, 32, dtype=np.float32) / 64).reshape(4, 16)
+    assert O.absmean_gamma(w) == np.float32((528 + 496) / 64 / 64)
+
+
+def test_gamma_expectation_gaussian():
+    # E|W| = sigma*sqrt(2/pi) for W ~ N(0, sigma^2)
+    w = gaussian_weights(7, "q", 2560, 2560)
+    g = float(O.absmean_gamma(w))
+    mean = 0.02 * math.sqrt(2 / math.pi)
+    sd = 0.02 * math.sqrt(1 - 2 / math.pi) / math.sqrt(w.size)
+    assert abs(g - mean) < 6 * sd
+
+
+def test_zero_fraction_closed_form():
+    # a weight is zero iff |W| < gamma/2; with gamma -> sigma*sqrt(2/pi) the
+    # fraction is erf(1/(2*sqrt(pi))) = 0.3101, and +1 / -1 split the rest.
+    w = gaussian_weights(2, "q", 2560, 2560)
+    codes = O.ternary_codes(w, O.absmean_gamma(w))
+    n = codes.size
+    p0 = math.erf(1 / (2 * math.sqrt(math.pi)))
+    bound = 5 * math.sqrt(p0 * (1 - p0) / n) + 0.002
+    assert abs((codes == 0).mean() - p0) < bound
+    pp = (1 - p0) / 2
+    assert abs((codes == 1).mean() - pp) < bound
+    assert abs((codes == -1).mean() - pp) < bound
+    assert abs(p0 - 0.31006) < 1e-4
+
+
+def test_codes_are_ternary_and_odd():
+    w, _ = random_case(3, 1, 70, 333, w_sigma=1.0)
+    g = O.absmean_gamma(w)
+    c = O.ternary_codes(w, g)
+    assert set(np.unique(c)) <= {-1, 0, 1}
+    np.testing.assert_array_equal(O.ternary_codes(-w, g), -c)
+
+
+def test_codes_power_of_two_scaling():
+    w, _ = random_case(4, 1, 64, 256)
+    c0 = O.ternary_codes(w, O.absmean_gamma(w), eps=0.0)
+    for j in (-3, 5):
+        ws = w * np.float32(2.0 ** j)
+        assert O.absmean_gamma(ws) == O.absmean_gamma(w) * np.float32(2.0 ** j)
+        np.testing.assert_array_equal(O.ternary_codes(ws, O.absmean_gamma(ws), eps=0.0), c0)
+
+
+def test_codes_boundary_is_half():
+    # fp32(W/d) > 0.5 is the exact condition for a nonzero code; probe fp32
+    # neighbours of d/2 with d = 1 (eps = 0, gamma = 1).
+    d = np.float32(1.0)
+    half = np.float32(0.5)
+    above = np.nextafter(half, np.float32(1))
+    below = np.nextafter(half, np.float32(0))
+    w = f32([[half, above, below, -above, -half, np.float32(1.5), np.float32(2.5)]])
+    c = O.ternary_codes(w, d, eps=0.0)
+    np.testing.assert_array_equal(c, [[0, 1, 0, -1, 0, 1, 1]])
+
+
+def test_all_zero_weights():
+    w = np.zeros((3, 7), np.float32)
+    g = O.absmean_gamma(w)
+    assert g == 0
+    np.testing.assert_array_equal(O.ternary_codes(w, g), 0)
+    np.testing.assert_array_equal(O.ternary_codes(w, g, eps=0.0), 0)
+
+
+# ------------------------------------------------------------- activations --
+def test_activations_worked(gold):
+    g = gold["activations"]
+    xq, s = O.quant_act(f32(g["x"]), np.float32(g["eps"]))
+    np.testing.assert_array_equal(xq, np.array(g["xq"], dtype=np.int8))
+    np.testing.assert_array_equal(s, f32(g["s"]))
+
+
+def test_activation_invariants():
+    _, x = random_case(5, 33, 4, 1000, x_kind="t3")
+    x[3] = 0.0
+    x[4, :] = 0.0
+    x[4, 17] = -5e-4
+    xq, s = O.quant_act(x)
+    assert xq.min() >= -127 and xq.max() <= 127
+    beta = np.abs(x).max(axis=1)
+    for m in range(x.shape[0]):
+        if beta[m] >= O.EPS_DEFAULT:
+            j = int(np.argmax(np.abs(x[m])))
+            assert abs(int(xq[m, j])) == 127
+        # sign preserved or zeroed
+        assert np.all((np.sign(xq[m]) == np.sign(x[m])) | (xq[m] == 0))
+        order = np.argsort(x[m], kind="stable")
+        assert np.all(np.diff(xq[m][order].astype(np.int32)) >= 0)
+    np.testing.assert_array_equal(xq[3], 0)
+    np.testing.assert_array_equal(O.quant_act(-x)[0], -xq)
+
+
+def test_activation_power_of_two_scaling():
+    _, x = random_case(6, 5, 4, 300)
+    xq, s = O.quant_act(x, eps=0.0)
+    for j in (-4, 6):
+        xq2, s2 = O.quant_act(x * np.float32(2.0 ** j), eps=0.0)
+        np.testing.assert_array_equal(xq2, xq)
+        np.testing.assert_array_equal(s2, s / np.float32(2.0 ** j))
+
+
+def test_activation_single_nonzero_and_k1(gold):
+    g = gold["k_equals_1"]
+    xq, s = O.quant_act(f32(g["x"]))
+    np.testing.assert_array_equal(xq, g["xq"])
+    for v in (3.0, -0.01, 1e-3, 77.7):
+        x = np.zeros((1, 9), np.float32)
+        x[0, 4] = v
+        assert O.quant_act(x)[0][0, 4] == (127 if v > 0 else -127)
+
+
+# ------------------------------------------------------------- contraction --
+def test_contraction_brute_force():
+    rng = np.random.default_rng(11)
+    for (m, n, k) in [(1, 1, 1), (3, 5, 7), (4, 9, 64), (2, 3, 300)]:
+        xq = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+        codes = rng.integers(-1, 2, size=(n, k)).astype(np.int8)
+        ref = np.zeros((m, n), dtype=np.int64)
+        for i in range(m):
+            for j in range(n):
+                t = 0
+                for kk in range(k):
+                    t += int(xq[i, kk]) * int(codes[j, kk])
+                ref[i, j] = t
+        np.testing.assert_array_equal(O.contract(xq, codes), ref)
+        np.testing.assert_array_equal(O.contract_addsub(xq, codes), ref)
+
+
+def test_contraction_extremes():
+    # |acc| reaches 127*K when every code matches the sign of a full-scale x~
+    k = 28672
+    xq = np.full((2, k), 127, np.int8)
+    xq[1] = -127
+    codes = np.ones((3, k), np.int8)
+    codes[1] = -1
+    codes[2] = 0
+    acc = O.contract(xq, codes)
+    np.testing.assert_array_equal(acc, [[127 * k, -127 * k, 0], [-127 * k, 127 * k, 0]])
+
+
+def test_forward_worked(gold):
+    gw, ga, gf = gold["weights_basic"], gold["activations"], gold["forward"]
+    w = f32(gw["w"])
+    r = O.forward(f32(ga["x"]), w, eps=np.float32(1e-5), y_dtype="f32")
+    np.testing.assert_array_equal(r["acc"], gf["acc"])
+    np.testing.assert_array_equal(r["y"], f32(gf["y_f32"]))
+    r2 = O.forward(f32(ga["x"]), w, eps=np.float32(1e-5), relu2=True, y_dtype="f32")
+    np.testing.assert_array_equal(r2["y"], f32(gf["y_relu2_f32"]))
+    rb = O.forward(f32(ga["x"]), w, eps=np.float32(1e-5), y_dtype="bf16")
+    np.testing.assert_array_equal(O.bf16_bits_to_f32(rb["y"]), f32(gf["y_bf16"]))
+
+
+def test_forward_k1(gold):
+    g = gold["k_equals_1"]
+    r = O.forward(f32(g["x"]), f32(g["w"]), eps=np.float32(g["eps"]))
+    np.testing.assert_array_equal(r["codes"], g["codes"])
+    np.testing.assert_array_equal(r["acc"], g["acc"])
+    assert r["y64"][0, 0] == -2.0 * float(np.float32(0.3))
+
+
+def test_dequant_matches_page_form():
+    # the page rescales by beta*gamma/Q_b; the oracle divides by s = 127/beta.
+    # They differ only by the fp32 rounding of s (relative 2^-24 each way).
+    w, x = random_case(12, 8, 40, 512, x_kind="t3")
+    r = O.forward(x, w)
+    beta = np.maximum(np.abs(x).max(axis=1), O.EPS_DEFAULT).astype(np.float64)
+    page = r["acc"].astype(np.float64) * beta[:, None] * float(r["gamma"]) / 127.0
+    nz = page != 0
+    rel = np.abs(r["y64"][nz] - page[nz]) / np.abs(page[nz])
+    assert rel.max() <= 2.0 ** -23
+    np.testing.assert_array_equal(r["y64"][~nz], 0.0)
+
+
+def test_dequant_scaling_law():
+    w, x = random_case(13, 3, 16, 256)
+    base = O.forward(x, w, eps=0.0)["y64"]
+    sc = O.forward(x * np.float32(4.0), w * np.float32(0.125), eps=0.0)["y64"]
+    np.testing.assert_array_equal(sc, base * 0.5)
+
+
+def test_relu2():
+    acc = np.array([[5, -5, 0, 127]], np.int32)
+    y = O.dequant(acc, np.float32(0.5), f32([2.0]), relu2=True)
+    np.testing.assert_array_equal(y, [[1.5625, 0.0, 0.0, (127 * 0.25) ** 2]])
+
+
+def test_bf16_rounding_against_torch():
+    import torch
+    rng = np.random.default_rng(3)
+    vals = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * 1000,
+        np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x3F80FFFF, 0x7F7FFFFF, 0x00000001],
+                 dtype=np.uint32).view(np.float32),
+        f32([0.0, -0.0, 1.0, -2.5]),
+    ]).astype(np.float32)
+    ours = O.f32_to_bf16_bits(vals)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    # ties go to even: 1.00390625 -> 1.0, 1.01171875 -> 1.015625
+    assert O.f32_to_bf16_bits(np.array([0x3F808000], np.uint32).view(np.float32))[0] == 0x3F80
+    assert O.f32_to_bf16_bits(np.array([0x3F818000], np.uint32).view(np.float32))[0] == 0x3F82
+
+
+# ----------------------------------------------------------------- packing --
+def test_pack_word_bits(gold):
+    g = gold["pack_word_bits"]
+    codes = np.array([g["codes_row0"]], dtype=np.int8)
+    words = O.pack_ternary(codes).view(np.uint32)
+    assert words.size == g["total_words"]
+    assert words[0] == int(g["word0"], 16)
+    assert np.all(words[1:] == 0)
+
+
+def test_pack_word_index(gold):
+    g = gold["pack_word_index"]
+    n, k = g["n"], g["k"]
+    for e in g["entries"]:
+        codes = np.zeros((n, k), np.int8)
+        codes[e["n"], e["k"]] = e["code"]
+        words = O.pack_ternary(codes).view(np.uint32)
+        assert words.size == g["total_words"]
+        nz = np.nonzero(words)[0]
+        assert list(nz) == [e["word"]]
+        assert words[e["word"]] == int(e["value"], 16)
+        assert O.packed_word_index(e["n"], e["k"], n, k)[0] == e["word"]
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (64, 256), (65, 257), (130, 520), (7, 1000)])
+def test_pack_roundtrip(shape):
+    rng = np.random.default_rng(sum(shape))
+    codes = rng.integers(-1, 2, size=shape).astype(np.int8)
+    packed = O.pack_ternary(codes)
+    assert packed.nbytes == O.packed_bytes(*shape)
+    np.testing.assert_array_equal(O.unpack_ternary(packed, *shape), codes)
+    # padding holds zero codes; 0b10 never appears
+    npad, kpad = O.padded_n(shape[0]), O.padded_k(shape[1])
+    full = O.unpack_ternary(packed, npad, kpad)
+    assert np.all(full[shape[0]:, :] == 0) and np.all(full[:, shape[1]:] == 0)
+    words = packed.view(np.uint32)
+    for sh in range(0, 32, 2):
+        assert not np.any(((words >> np.uint32(sh)) & np.uint32(3)) == 2)
+
+
+def test_pack_rejects_non_ternary():
+    with pytest.raises(ValueError):
+        O.pack_ternary(np.array([[2]], np.int8))
