@@ -1,0 +1,196 @@
+"""Python binding of libbitlinear (BitLinear W1.58A8 forward on MI355X).
+
+Argument marshalling only: every step of the pass runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  The names
+follow the C ABI in include/bitlinear.h:
+
+    pack_weights(w, eps)            -> (packed uint8, gamma fp32[1])
+    quant_act(x, eps)               -> (xq int8 [M, K_pad], scale fp32 [M])
+    forward(xq, scale, packed, gamma, n, k, relu2, out_dtype)  -> y [M, N]
+
+The library must be built (``python -m bit_gemm_int8_amd.build_lib`` or
+``__graft_entry__.build()``); importing fails loudly if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbitlinear.so")
+
+BL_OK = 0
+BL_F32, BL_BF16 = 0, 1
+BL_EPI_NONE, BL_EPI_RELU2 = 0, 1
+BL_MAX_K = 262144
+EPS_DEFAULT = 1e-5
+
+STATUS_NAMES = {0: "BL_OK", 1: "BL_ERR_INVALID_ARG", 2: "BL_ERR_UNSUPPORTED_SHAPE",
+                3: "BL_ERR_MISALIGNED", 4: "BL_ERR_WORKSPACE", 5: "BL_ERR_HIP"}
+
+# Every symbol declared in include/bitlinear.h.
+EXPORTS = [
+    "bitlinear_padded_n", "bitlinear_padded_k", "bitlinear_packed_bytes", "bitlinear_xq_bytes",
+    "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights", "bitlinear_quant_act",
+    "bitlinear_forward_workspace_bytes", "bitlinear_forward", "bitlinear_workspace_init",
+    "bitlinear_status_string", "bitlinear_abi_version",
+]
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)} ({msg})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libbitlinear.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, sz, vp, f32, i32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    sig = {
+        "bitlinear_padded_n": (i64, [i64]),
+        "bitlinear_padded_k": (i64, [i64]),
+        "bitlinear_packed_bytes": (sz, [i64, i64]),
+        "bitlinear_xq_bytes": (sz, [i64, i64]),
+        "bitlinear_pack_workspace_bytes": (sz, [i64, i64]),
+        "bitlinear_pack_weights": (i32, [vp, i32, i64, i64, f32, vp, vp, vp, vp, sz, vp]),
+        "bitlinear_quant_act": (i32, [vp, i32, i64, i64, f32, vp, vp, vp]),
+        "bitlinear_forward_workspace_bytes": (sz, [i64, i64, i64]),
+        "bitlinear_forward": (i32, [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp, sz, vp]),
+        "bitlinear_workspace_init": (i32, [vp, sz, vp]),
+        "bitlinear_status_string": (ctypes.c_char_p, [i32]),
+        "bitlinear_abi_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != BL_OK:
+        raise BitLinearError(fn, status, lib.bitlinear_status_string(status).decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    if dt == torch.float32:
+        return BL_F32
+    if dt == torch.bfloat16:
+        return BL_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+# ------------------------------------------------------------------ sizes --
+def padded_k(k: int) -> int:
+    return int(lib.bitlinear_padded_k(k))
+
+
+def padded_n(n: int) -> int:
+    return int(lib.bitlinear_padded_n(n))
+
+
+def packed_bytes(n: int, k: int) -> int:
+    return int(lib.bitlinear_packed_bytes(n, k))
+
+
+def forward_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(lib.bitlinear_forward_workspace_bytes(m, n, k))
+
+
+# ------------------------------------------------------------ workspaces --
+class Workspace:
+    """A zero-filled forward workspace that grows on demand (device memory
+    from torch).  The library leaves it zero-filled after every call."""
+
+    def __init__(self, device=None):
+        self.buf = None
+        self.device = device
+
+    def get(self, nbytes: int, stream=None):
+        import torch
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            size = max(nbytes, 1 << 20)
+            self.buf = torch.empty(size, dtype=torch.uint8, device=self.device or "cuda")
+            _check("bitlinear_workspace_init",
+                   lib.bitlinear_workspace_init(_ptr(self.buf), size, _stream(stream)))
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace_for(device) -> Workspace:
+    key = str(device)
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(device)
+    return _default_ws[key]
+
+
+# ---------------------------------------------------------------- entries --
+def pack_weights(w, eps: float = EPS_DEFAULT, gamma_in=None, stream=None):
+    """bitlinear_pack_weights: w [N, K] fp32/bf16 (cuda) -> (packed uint8, gamma fp32[1])."""
+    import torch
+    if w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [N, K] tensor")
+    n, k = w.shape
+    packed = torch.empty(max(packed_bytes(n, k), 1), dtype=torch.uint8, device=w.device)
+    gamma = torch.empty(1, dtype=torch.float32, device=w.device)
+    wsb = int(lib.bitlinear_pack_workspace_bytes(n, k))
+    ws = None if gamma_in is not None else torch.empty(max(wsb, 8), dtype=torch.uint8, device=w.device)
+    _check("bitlinear_pack_weights", lib.bitlinear_pack_weights(
+        _ptr(w), _dtype_code(w.dtype), n, k, float(eps), _ptr(gamma_in), _ptr(packed),
+        _ptr(gamma), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return packed, gamma
+
+
+def quant_act(x, eps: float = EPS_DEFAULT, stream=None) -> Tuple:
+    """bitlinear_quant_act: x [M, K] fp32/bf16 -> (xq int8 [M, K_pad], scale fp32 [M])."""
+    import torch
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] tensor")
+    m, k = x.shape
+    kp = padded_k(k)
+    xq = torch.empty((m, kp), dtype=torch.int8, device=x.device)
+    scale = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check("bitlinear_quant_act", lib.bitlinear_quant_act(
+        _ptr(x), _dtype_code(x.dtype), m, k, float(eps), _ptr(xq), _ptr(scale), _stream(stream)))
+    return xq, scale
+
+
+def forward(xq, scale, packed, gamma, n: int, k: int, relu2: bool = False,
+            out_dtype=None, acc_out: bool = False, y=None, workspace: Optional[Workspace] = None,
+            stream=None):
+    """bitlinear_forward: returns y [M, N] (and the int32 accumulator if asked)."""
+    import torch
+    out_dtype = out_dtype or torch.float32
+    m = xq.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=xq.device)
+    acc = torch.empty((m, n), dtype=torch.int32, device=xq.device) if acc_out else None
+    nbytes = forward_workspace_bytes(m, n, k)
+    ws = (workspace or _workspace_for(xq.device)).get(nbytes, stream)
+    _check("bitlinear_forward", lib.bitlinear_forward(
+        _ptr(xq), _ptr(scale), _ptr(packed), _ptr(gamma), m, n, k,
+        BL_EPI_RELU2 if relu2 else BL_EPI_NONE, _dtype_code(y.dtype), _ptr(y), _ptr(acc),
+        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return (y, acc) if acc_out else y

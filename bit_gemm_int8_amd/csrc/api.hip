@@ -1,0 +1,215 @@
+// libbitlinear C ABI: argument checks, dispatch and launches.
+// The entry points and their contracts are declared in include/bitlinear.h.
+#include <math.h>
+
+#include "../../include/bitlinear.h"
+#include "bl_device.h"
+#include "bl_internal.h"
+
+namespace bl {
+
+hipError_t launch_gemv(int m, const int8_t* xq, const float* scale, const uint32_t* packed,
+                       const float* gamma, int64_t n, int64_t k, int splits, bool relu2,
+                       bool bf16, void* y, int32_t* acc_out, int32_t* partial,
+                       uint32_t* counters, hipStream_t stream);
+hipError_t launch_gemm(int variant, const int8_t* xq, const float* scale, const uint32_t* packed,
+                       const float* gamma, int64_t m, int64_t n, int64_t k, int splits,
+                       bool relu2, bool bf16, void* y, int32_t* acc_out, int32_t* partial,
+                       uint32_t* counters, hipStream_t stream);
+void gemm_tile_shape(int variant, int* bm, int* bn);
+
+namespace {
+
+__global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t words) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < words; i += stride) p[i] = 0u;
+}
+
+constexpr int64_t kGemvMaxM = 4;
+constexpr int64_t kGemvTargetWaves = 2048;
+constexpr int64_t kGemmTargetGroups = 512;
+
+inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+}  // namespace
+
+hipError_t launch_fill_zero(uint32_t* p, size_t words, hipStream_t stream) {
+  if (words == 0) return hipSuccess;
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  fill_zero_kernel<<<(unsigned)blocks, 256, 0, stream>>>(p, words);
+  return hipGetLastError();
+}
+
+FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
+  FwdPlan p{};
+  const int64_t nb = cdiv(n, kRowBlock);
+  const int64_t nc = cdiv(k, kSuperK);
+  if (m <= 0) return p;
+  if (m <= kGemvMaxM) {
+    p.kind = 0;
+    p.variant = 0;
+    int64_t s = cdiv(kGemvTargetWaves, nb);
+    if (s > nc) s = nc;
+    if (s < 1) s = 1;
+    p.splits = (int)s;
+    p.tiles = (int)nb;
+    p.partial_ints = s > 1 ? (size_t)(nb * s * m * 64) : 0;
+  } else {
+    p.kind = 1;
+    p.variant = m <= 16 ? 0 : m <= 32 ? 1 : m <= 64 ? 2 : 3;
+    int bm, bn;
+    gemm_tile_shape(p.variant, &bm, &bn);
+    const int64_t tiles = cdiv(m, bm) * cdiv(nb * 64, bn);
+    int64_t s = cdiv(kGemmTargetGroups, tiles);
+    int64_t smax = nc / 2 > 1 ? nc / 2 : 1;
+    if (s > smax) s = smax;
+    if (s < 1) s = 1;
+    p.splits = (int)s;
+    p.tiles = (int)tiles;
+    p.partial_ints = s > 1 ? (size_t)(tiles * s * bm * bn) : 0;
+  }
+  p.ws_bytes = p.splits > 1 ? round_up((size_t)p.tiles * 4, 256) + p.partial_ints * 4 : 0;
+  return p;
+}
+
+hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* scale,
+                          const uint32_t* packed, const float* gamma, int64_t m, int64_t n,
+                          int64_t k, bool relu2, bool bf16, void* y, int32_t* acc_out,
+                          void* workspace, hipStream_t stream) {
+  uint32_t* counters = nullptr;
+  int32_t* partial = nullptr;
+  if (plan.splits > 1) {
+    counters = reinterpret_cast<uint32_t*>(workspace);
+    partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) +
+                                         round_up((size_t)plan.tiles * 4, 256));
+  }
+  if (plan.kind == 0)
+    return launch_gemv((int)m, xq, scale, packed, gamma, n, k, plan.splits, relu2, bf16, y,
+                       acc_out, partial, counters, stream);
+  return launch_gemm(plan.variant, xq, scale, packed, gamma, m, n, k, plan.splits, relu2, bf16,
+                     y, acc_out, partial, counters, stream);
+}
+
+}  // namespace bl
+
+using namespace bl;
+
+namespace {
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+inline bool valid_dtype(int d) { return d == BL_F32 || d == BL_BF16; }
+inline bool valid_eps(float e) { return isfinite(e) && e >= 0.0f; }
+}  // namespace
+
+extern "C" {
+
+int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
+
+const char* bitlinear_status_string(int status) {
+  switch (status) {
+    case BL_OK: return "ok";
+    case BL_ERR_INVALID_ARG: return "invalid argument";
+    case BL_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case BL_ERR_MISALIGNED: return "misaligned pointer";
+    case BL_ERR_WORKSPACE: return "workspace missing or too small";
+    case BL_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int64_t bitlinear_padded_n(int64_t n) { return n <= 0 ? 0 : padded_n(n); }
+int64_t bitlinear_padded_k(int64_t k) { return k <= 0 ? 0 : padded_k(k); }
+
+size_t bitlinear_packed_bytes(int64_t n, int64_t k) {
+  if (n <= 0 || k <= 0) return 0;
+  return (size_t)(padded_n(n) * padded_k(k) / 4);
+}
+
+size_t bitlinear_xq_bytes(int64_t m, int64_t k) {
+  if (m <= 0 || k <= 0) return 0;
+  return (size_t)(m * padded_k(k));
+}
+
+size_t bitlinear_pack_workspace_bytes(int64_t n, int64_t k) {
+  if (n <= 0 || k <= 0) return 0;
+  return pack_workspace_bytes(n, k);
+}
+
+size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || k > BL_MAX_K || n > BL_MAX_MN || m > BL_MAX_MN) return 0;
+  return forward_plan(m, n, k).ws_bytes;
+}
+
+bl_status bitlinear_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (bytes == 0) return BL_OK;
+  if (workspace == nullptr || bytes % 4 != 0) return BL_ERR_INVALID_ARG;
+  if (!aligned(workspace, 4)) return BL_ERR_MISALIGNED;
+  if (launch_fill_zero(reinterpret_cast<uint32_t*>(workspace), bytes / 4,
+                       reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return BL_ERR_HIP;
+  return BL_OK;
+}
+
+bl_status bitlinear_pack_weights(const void* w, int w_dtype, int64_t n, int64_t k, float eps,
+                                 const float* gamma_in, void* packed, float* gamma_out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (w == nullptr || packed == nullptr || gamma_out == nullptr) return BL_ERR_INVALID_ARG;
+  if (!valid_dtype(w_dtype) || !valid_eps(eps)) return BL_ERR_INVALID_ARG;
+  if (n < 1 || k < 1) return BL_ERR_INVALID_ARG;
+  if (n > BL_MAX_MN || k > BL_MAX_K) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned(w, 16) || !aligned(packed, 256) || !aligned(gamma_out, 4) ||
+      (gamma_in != nullptr && !aligned(gamma_in, 4)))
+    return BL_ERR_MISALIGNED;
+  if (gamma_in == nullptr) {
+    if (workspace == nullptr || workspace_bytes < pack_workspace_bytes(n, k))
+      return BL_ERR_WORKSPACE;
+    if (!aligned(workspace, 8)) return BL_ERR_MISALIGNED;
+  }
+  hipError_t e = launch_pack(w, w_dtype == BL_BF16, n, k, eps, gamma_in,
+                             reinterpret_cast<uint32_t*>(packed), gamma_out,
+                             reinterpret_cast<double*>(workspace),
+                             reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? BL_OK : BL_ERR_HIP;
+}
+
+bl_status bitlinear_quant_act(const void* x, int x_dtype, int64_t m, int64_t k, float eps,
+                              int8_t* xq, float* scale, void* stream) {
+  if (!valid_dtype(x_dtype) || !valid_eps(eps)) return BL_ERR_INVALID_ARG;
+  if (m < 0 || k < 1) return BL_ERR_INVALID_ARG;
+  if (m > BL_MAX_MN || k > BL_MAX_K) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (m == 0) return BL_OK;
+  if (x == nullptr || xq == nullptr || scale == nullptr) return BL_ERR_INVALID_ARG;
+  if (!aligned(x, x_dtype == BL_BF16 ? 2 : 4) || !aligned(xq, 16) || !aligned(scale, 4))
+    return BL_ERR_MISALIGNED;
+  hipError_t e = launch_quant_act(x, x_dtype == BL_BF16, m, k, padded_k(k), eps, xq, scale,
+                                  reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? BL_OK : BL_ERR_HIP;
+}
+
+bl_status bitlinear_forward(const int8_t* xq, const float* scale, const void* packed,
+                            const float* gamma, int64_t m, int64_t n, int64_t k, int epilogue,
+                            int y_dtype, void* y, int32_t* acc_out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(y_dtype)) return BL_ERR_INVALID_ARG;
+  if (epilogue != BL_EPI_NONE && epilogue != BL_EPI_RELU2) return BL_ERR_INVALID_ARG;
+  if (m < 0 || n < 1 || k < 1) return BL_ERR_INVALID_ARG;
+  if (m > BL_MAX_MN || n > BL_MAX_MN || k > BL_MAX_K) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (m == 0) return BL_OK;
+  if (xq == nullptr || scale == nullptr || packed == nullptr || gamma == nullptr || y == nullptr)
+    return BL_ERR_INVALID_ARG;
+  if (!aligned(xq, 16) || !aligned(scale, 4) || !aligned(packed, 16) || !aligned(gamma, 4) ||
+      !aligned(y, y_dtype == BL_BF16 ? 2 : 4) || (acc_out != nullptr && !aligned(acc_out, 4)))
+    return BL_ERR_MISALIGNED;
+  const FwdPlan plan = forward_plan(m, n, k);
+  if (plan.ws_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return BL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return BL_ERR_MISALIGNED;
+  }
+  hipError_t e = launch_forward(plan, xq, scale, reinterpret_cast<const uint32_t*>(packed), gamma,
+                                m, n, k, epilogue == BL_EPI_RELU2, y_dtype == BL_BF16, y, acc_out,
+                                workspace, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? BL_OK : BL_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Device helpers shared by the libbitlinear kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int32_t bl_v4i __attribute__((ext_vector_type(4)));
+
+namespace bl {
+
+constexpr int kRowBlock = 64;     // rows per packed block
+constexpr int kSuperK = 256;      // inputs per packed super-chunk
+constexpr int kBlockU4 = 256;     // uint4 per 4 KiB packed block
+
+// Four weights t = 4i..4i+3 of a packed word, as int8 lanes holding 64*W~.
+// Code t sits at bits 8*(t%4) + 2*(t/4); shifting left by 6-2i brings the
+// pair for t = 4i+e to the top two bits of byte e, and the mask drops the
+// rest.  A two's complement 2-bit field at the top of a byte reads as
+// 64 * field when the byte is taken as int8: 01 -> 64, 11 -> -64, 00 -> 0.
+__device__ __forceinline__ uint32_t unpack_x64(uint32_t w, int i) {
+  return (w << (6 - 2 * i)) & 0xC0C0C0C0u;
+}
+
+// Signed int8 dot product of four byte lanes, accumulated into c.
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite input).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Max over each row of 16 lanes with DPP lane permutations; every lane of
+// the row ends with the row's maximum.
+__device__ __forceinline__ uint32_t dpp_row_max_u32(uint32_t v) {
+  uint32_t t;
+  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  v = v > t ? v : t;
+  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  v = v > t ? v : t;
+  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  v = v > t ? v : t;
+  t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);  // row_mirror
+  v = v > t ? v : t;
+  return v;
+}
+
+// Max over the whole wave (result uniform).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_row_max_u32(v);
+  uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  a = a > b ? a : b;
+  c = c > d ? c : d;
+  return a > c ? a : c;
+}
+
+// Rescale factor gamma / s as the correctly rounded fp32 quotient (the fp64
+// quotient of two fp32 values rounds to the same fp32 as the exact one).
+__device__ __forceinline__ float gamma_over_s(float gamma, float s) {
+  return (float)((double)gamma / (double)s);
+}
+
+// y = acc * f, then ReLU^2 if asked; stored as fp32 or bf16.
+__device__ __forceinline__ void store_out(void* y, int64_t idx, int acc, float f,
+                                          bool relu2, bool bf16) {
+  float v = (float)acc * f;
+  if (relu2) v = v > 0.0f ? v * v : 0.0f;
+  if (bf16)
+    reinterpret_cast<uint16_t*>(y)[idx] = f32_to_bf16(v);
+  else
+    reinterpret_cast<float*>(y)[idx] = v;
+}
+
+// Split-K completion.  Call after this workgroup stored its partial results:
+// returns true for exactly one workgroup of the tile -- the last to finish --
+// which then reads every split's partials.  The counter goes back to zero,
+// so the workspace is ready for the next call.  All threads must call it.
+__device__ __forceinline__ bool splitk_last_arrival(uint32_t* counter, int splits,
+                                                    uint32_t* lds_flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    bool last = prev == (uint32_t)(splits - 1);
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = last ? 1u : 0u;
+  }
+  __syncthreads();
+  bool last = *lds_flag != 0u;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
+}  // namespace bl

@@ -1,0 +1,180 @@
+/*
+ * bitlinear.h -- C ABI of libbitlinear, the BitLinear W1.58A8 forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The pass (page "BitNet b1.58 2B4T Guide: Scaling Native 1-Bit LLMs"):
+ *   1. absmean ternary weight quantization -- section "Ternary Weight
+ *      Quantization: absmean Scaling": gamma = mean |W| over the whole tensor,
+ *      W~ = Clip(Round(W / (gamma + eps)), -1, 1);
+ *   2. per-token absmax int8 activation quantization -- section "8-Bit
+ *      Activation Quantization: absmax Scaling": s = 127 / max|x|,
+ *      x~ = Clip(Round(x * s), -128, 127);
+ *   3. the integer product x~ W~^T with an integer accumulator and
+ *   4. the rescale by beta*gamma/127 = gamma/s -- section "Matrix
+ *      Multiplication as Pure Integer Addition".
+ * Weights are stored two bits each (winbuzzer.com, "Microsoft Releases
+ * BitNet b1.58 2B4T", section "The Catch": GPU kernels pack and unpack the
+ * weights); the up projection of the FFN is followed by ReLU^2 (same page,
+ * section "Under the Hood: The BitNet Approach"), offered here as a fused
+ * epilogue.
+ *
+ * Conventions for every entry point
+ *   - All array arguments are DEVICE pointers on the current HIP device, owned
+ *     by the caller; the library allocates nothing and frees nothing.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work and return; results are ready when the stream
+ *     is synchronised.  No entry point synchronises or copies to the host.
+ *   - Arguments are checked on the host before any launch.  On a non-BL_OK
+ *     return nothing has been enqueued, except BL_ERR_HIP, which reports an
+ *     error from the HIP runtime when a kernel was launched.  Faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ *   - Inputs must be finite.  Outputs for NaN/Inf inputs are unspecified.
+ *   - Matrices are row-major and dense.  Shapes follow W in R^{N x K}
+ *     (N = d_out, K = d_in) and x in R^{M x K} (M = tokens).
+ *   - Sizes are int64_t.  1 <= N, K;  K <= BL_MAX_K;  0 <= M.
+ */
+#ifndef BITLINEAR_H_
+#define BITLINEAR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITLINEAR_ABI_VERSION 1
+
+/* Largest K: the kernels accumulate 64 * x~ * W~ in int32, so
+ * 64 * 127 * K must stay below 2^31. */
+#define BL_MAX_K 262144
+/* Largest M and N accepted (grid and index limits). */
+#define BL_MAX_MN 16777216
+
+typedef enum {
+  BL_OK = 0,
+  BL_ERR_INVALID_ARG = 1,       /* null pointer, size < allowed minimum, bad enum, bad eps */
+  BL_ERR_UNSUPPORTED_SHAPE = 2, /* size above BL_MAX_K or BL_MAX_MN */
+  BL_ERR_MISALIGNED = 3,        /* pointer below its documented alignment */
+  BL_ERR_WORKSPACE = 4,         /* workspace pointer NULL or smaller than required */
+  BL_ERR_HIP = 5                /* the HIP runtime reported an error at launch */
+} bl_status;
+
+typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
+typedef enum { BL_EPI_NONE = 0, BL_EPI_RELU2 = 1 } bl_epilogue;
+
+/* ------------------------------------------------------------------------
+ * Packed ternary weight layout (version 1)
+ *
+ *   N_pad = 64 * ceil(N / 64)     (row blocks of 64 output rows)
+ *   K_pad = 256 * ceil(K / 256)   (super-chunks of 256 inputs), NC = K_pad/256
+ *   buffer = N_pad * K_pad / 4 bytes = array of little-endian uint32 words.
+ *
+ *   Weight (n, k): b = n / 64, r = n % 64, c = k / 256, and
+ *   k % 256 = 64*j + 16*q + t  (j, q in 0..3, t in 0..15).  Its code is in
+ *       word  (((b*NC + c)*4 + q)*64 + r)*4 + j
+ *       bits  [8*(t%4) + 2*(t/4), +2)
+ *   as a 2-bit two's complement number: 0 -> 00, +1 -> 01, -1 -> 11 (10 is
+ *   never written).  Rows n >= N and columns k >= K hold code 0.
+ *
+ *   So each 4 KiB block (b, c) holds 64 rows x 256 inputs; inside it, byte
+ *   offset q*1024 + r*16 + 4*j.  Shifting a word left by 6-2i and masking
+ *   with 0xC0C0C0C0 yields four int8 values 64*W~ for t = 4i..4i+3 in byte
+ *   order, i.e. for consecutive inputs k.
+ * ---------------------------------------------------------------------- */
+
+/* Row count rounded up to 64. */
+int64_t bitlinear_padded_n(int64_t n);
+/* Input count rounded up to 256; also the row stride (bytes) of x~. */
+int64_t bitlinear_padded_k(int64_t k);
+/* Bytes of the packed weight buffer for an N x K matrix. */
+size_t bitlinear_packed_bytes(int64_t n, int64_t k);
+/* Bytes of the quantized activation buffer x~: m * padded_k(k). */
+size_t bitlinear_xq_bytes(int64_t m, int64_t k);
+
+/* ------------------------------------------------------------------------
+ * bitlinear_pack_weights -- absmean ternarization and 2-bit packing.
+ * Defines: "Ternary Weight Quantization: absmean Scaling" (both equations).
+ *
+ *   w          [n][k] fp32 (w_dtype = BL_F32) or bf16 (BL_BF16), 16-byte aligned.
+ *   eps        >= 0 and finite; the pages use 1e-5.
+ *   gamma_in   NULL: gamma = mean|w| is computed on the device (fp64
+ *              partial sums in a fixed order, rounded once to fp32; the
+ *              result does not depend on the launch or the run).
+ *              non-NULL: one fp32 on the device, used as gamma as is (for a
+ *              tensor split across devices, or to re-pack with a known
+ *              gamma); the workspace is then not touched.
+ *   packed     out, bitlinear_packed_bytes(n, k) bytes, 256-byte aligned.
+ *   gamma_out  out, one fp32 on the device (may equal gamma_in).
+ *   workspace  bitlinear_pack_workspace_bytes(n, k) bytes, 8-byte aligned,
+ *              contents ignored; may be NULL when gamma_in is given.
+ * Codes: W~ = Clip(rint(fp32(w / fp32(gamma + eps))), -1, 1), ties to even.
+ * ---------------------------------------------------------------------- */
+size_t bitlinear_pack_workspace_bytes(int64_t n, int64_t k);
+bl_status bitlinear_pack_weights(const void* w, int w_dtype, int64_t n, int64_t k,
+                                 float eps, const float* gamma_in, void* packed,
+                                 float* gamma_out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bitlinear_quant_act -- per-token absmax int8 activation quantization.
+ * Defines: "8-Bit Activation Quantization: absmax Scaling".
+ *
+ *   x       [m][k] fp32 or bf16 (x_dtype), 4-byte aligned (16 for speed).
+ *   eps     >= 0 and finite (1e-5 on the pages).
+ *   xq      out, int8 [m][padded_k(k)], 16-byte aligned.  Columns k..K_pad-1
+ *           are written as 0.
+ *   scale   out, fp32 [m]:  s_m = fp32(127 / max(beta_m, eps)),
+ *           beta_m = max_j |x_mj|.
+ * x~ = clamp(rint(fp32(x * s_m)), -128, 127) (ties to even); |x~| <= 127.
+ * m == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+bl_status bitlinear_quant_act(const void* x, int x_dtype, int64_t m, int64_t k,
+                              float eps, int8_t* xq, float* scale, void* stream);
+
+/* ------------------------------------------------------------------------
+ * bitlinear_forward -- y = (x~ W~^T) * gamma / s, with an optional fused
+ * ReLU^2.  Defines: "Matrix Multiplication as Pure Integer Addition"
+ * (integer accumulator; rescale by beta*gamma/127).
+ *
+ *   xq, scale  from bitlinear_quant_act (same m, k).
+ *   packed     from bitlinear_pack_weights (same n, k); 16-byte aligned.
+ *   gamma      one fp32 on the device (gamma_out of the pack call).
+ *   epilogue   BL_EPI_NONE or BL_EPI_RELU2 (y <- y > 0 ? y*y : 0, in fp32).
+ *   y_dtype    BL_F32 or BL_BF16 (round to nearest even); y is [m][n],
+ *              4-byte aligned.
+ *   acc_out    NULL, or int32 [m][n] that receives the exact integer
+ *              accumulator x~ W~^T (for verification).
+ *   workspace  bitlinear_forward_workspace_bytes(m, n, k) bytes, 256-byte
+ *              aligned, zero-filled once before its first use (see
+ *              bitlinear_workspace_init).  It starts with one counter word
+ *              per output tile; every completed call sets those back to zero,
+ *              so the workspace can be reused without clearing (the bytes
+ *              after the counters hold partial sums, whatever their value).
+ *              Calls that share a workspace must be ordered (one stream, or
+ *              events); concurrent calls on one workspace race.  May be NULL
+ *              when the required size is 0.
+ * The accumulator is exact (int32); y is acc * fp32(gamma/s_m) in fp32.
+ * m == 0 is a no-op.  The result is the same for every launch and run.
+ * ---------------------------------------------------------------------- */
+size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k);
+bl_status bitlinear_forward(const int8_t* xq, const float* scale, const void* packed,
+                            const float* gamma, int64_t m, int64_t n, int64_t k,
+                            int epilogue, int y_dtype, void* y, int32_t* acc_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Zero-fill a forward workspace with a device kernel (no hipMemset, so it can
+ * be captured in a HIP graph).  bytes must be a multiple of 4. */
+bl_status bitlinear_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Static description of a status code. */
+const char* bitlinear_status_string(int status);
+
+/* BITLINEAR_ABI_VERSION of the loaded library. */
+int bitlinear_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H_ */

@@ -162,10 +162,12 @@ def pack_ternary(codes: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(words).reshape(-1).view(np.uint8)
 
 
-def unpack_ternary(packed: np.ndarray, n: int, k: int) -> np.ndarray:
-    """Inverse of ``pack_ternary`` by direct lookup of every (n, k)."""
+def unpack_ternary(packed: np.ndarray, n: int, k: int, rows=None) -> np.ndarray:
+    """Inverse of ``pack_ternary`` by direct lookup of every (n, k); with
+    ``rows`` only those rows of the N x K matrix are read."""
     words = np.ascontiguousarray(packed).view(np.uint32)
-    nn, kk = np.meshgrid(np.arange(n), np.arange(k), indexing="ij")
+    row_ids = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    nn, kk = np.meshgrid(row_ids, np.arange(k), indexing="ij")
     nc = padded_k(k) // SUPER_K
     b, r = nn // ROW_BLOCK, nn % ROW_BLOCK
     c, rem256 = kk // SUPER_K, kk % SUPER_K

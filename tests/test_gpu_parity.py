@@ -1,0 +1,269 @@
+"""GPU parity of every step of the pass against the CPU oracle, called
+through the C ABI (via the thin binding).  Integers and bytes are compared bit
+for bit; outputs within 1e-5 (fp32) / 1e-2 (bf16) relative, zeros exact."""
+import numpy as np
+import pytest
+
+import oracle as O
+from datagen import random_case
+from gpu_util import (assert_y_close, dev, gamma_agrees, host, log, x_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_gemm_int8_amd as B
+    return B
+
+
+# ------------------------------------------------------------ activations --
+QA_CASES = [(1, 1, "f32"), (1, 7, "bf16"), (3, 256, "f32"), (4, 272, "bf16"), (5, 1000, "f32"),
+            (9, 2560, "bf16"), (2, 6912, "bf16"), (64, 300, "f32"), (33, 8, "bf16"),
+            (1, 28672, "bf16"), (130, 520, "f32")]
+
+
+@pytest.mark.parametrize("m,k,xdt", QA_CASES)
+def test_quant_act(B, m, k, xdt):
+    log(f"quant_act m={m} k={k} {xdt}")
+    _, x = random_case(1000 + m * 7 + k, m, 1, k, x_kind="t3")
+    if m > 2:
+        x[1] = 0.0                                  # all-zero token
+        x[2] = 0.0
+        x[2, k // 2] = -3.0                         # single nonzero
+    xd, xo = x_device(x, xdt)
+    xq, s = B.quant_act(xd)
+    xq, s = host(xq), host(s)
+    oq, os_ = O.quant_act(xo)
+    np.testing.assert_array_equal(s, os_)
+    np.testing.assert_array_equal(xq[:, :k], oq)
+    assert np.all(xq[:, k:] == 0)
+    assert xq.shape[1] == O.padded_k(k)
+
+
+def test_quant_act_ties(B):
+    # x*s lands exactly on k + 0.5 for many elements (beta = 127 -> s = 1)
+    x = np.array([[127.0, 2.5, -3.5, 0.5, -0.5, 1.5, 126.5, -126.5] * 32], np.float32)
+    xq, s = B.quant_act(dev(x))
+    oq, os_ = O.quant_act(x)
+    np.testing.assert_array_equal(host(xq)[:, :256], oq)
+    np.testing.assert_array_equal(host(s), os_)
+
+
+def test_quant_act_worked_example(B):
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))["activations"]
+    xq, s = B.quant_act(dev(np.array(g["x"], np.float32)))
+    np.testing.assert_array_equal(host(xq)[:, :4], np.array(g["xq"], np.int8))
+    np.testing.assert_array_equal(host(s), np.array(g["s"], np.float32))
+
+
+def test_quant_act_unaligned_pointer(B):
+    import torch
+    _, x = random_case(5, 3, 1, 100)
+    big = dev(np.concatenate([np.zeros(1, np.float32), x.ravel()]))
+    xv = big[1:].view(3, 100)                        # 4-byte aligned, not 16
+    xq, s = B.quant_act(xv)
+    oq, os_ = O.quant_act(x)
+    np.testing.assert_array_equal(host(xq)[:, :100], oq)
+    np.testing.assert_array_equal(host(s), os_)
+
+
+# ---------------------------------------------------------------- packing --
+PACK_CASES = [(1, 1), (3, 5), (64, 256), (65, 257), (130, 520), (256, 256), (640, 2560),
+              (100, 1000), (7, 4097)]
+
+
+@pytest.mark.parametrize("n,k", PACK_CASES)
+def test_pack_gamma_in(B, n, k):
+    log(f"pack gamma_in n={n} k={k}")
+    w, _ = random_case(2000 + n + k, 1, n, k)
+    g = O.absmean_gamma(w)
+    packed, gout = B.pack_weights(dev(w), gamma_in=dev(np.array([g], np.float32)))
+    ref = O.pack_ternary(O.ternary_codes(w, g))
+    np.testing.assert_array_equal(host(packed)[:ref.size], ref)
+    assert host(gout)[0] == g
+
+
+@pytest.mark.parametrize("n,k", PACK_CASES)
+def test_pack_gamma_device(B, n, k):
+    log(f"pack n={n} k={k}")
+    w, _ = random_case(3000 + n + k, 1, n, k)
+    packed, gout = B.pack_weights(dev(w))
+    g = host(gout)[0]
+    assert gamma_agrees(g, w)
+    ref = O.pack_ternary(O.ternary_codes(w, np.float32(g)))
+    np.testing.assert_array_equal(host(packed), ref)
+
+
+def test_pack_bf16_weights(B):
+    from datagen import to_bf16_bits, bf16_bits_to_f32
+    from gpu_util import dev_bf16
+    w, _ = random_case(77, 1, 200, 600)
+    bits = to_bf16_bits(w)
+    wf = bf16_bits_to_f32(bits)
+    packed, gout = B.pack_weights(dev_bf16(bits))
+    assert gamma_agrees(host(gout)[0], wf)
+    np.testing.assert_array_equal(host(packed), O.pack_ternary(O.ternary_codes(wf, host(gout)[0])))
+
+
+def test_pack_threshold_neighbours(B):
+    # weights at and next to every decision point |w|/d = 0.5, 1.5 for a
+    # given gamma; eps as on the pages.
+    gamma = np.float32(0.015625)
+    eps = np.float32(1e-5)
+    d = np.float32(gamma + eps)
+    pts = []
+    for base in (np.float32(d * np.float32(0.5)), np.float32(d * np.float32(1.5)), d / 2, d):
+        v = np.float32(base)
+        for _ in range(6):
+            v = np.nextafter(v, np.float32(-np.inf))
+        for _ in range(13):
+            pts += [v, -v]
+            v = np.nextafter(v, np.float32(np.inf))
+    w = np.array(pts, np.float32)
+    w = np.resize(w, (4, 256)).astype(np.float32)
+    codes = O.ternary_codes(w, gamma, eps)
+    assert (codes == 0).any() and (codes != 0).any()
+    packed, _ = B.pack_weights(dev(w), eps=float(eps), gamma_in=dev(np.array([gamma], np.float32)))
+    np.testing.assert_array_equal(host(packed), O.pack_ternary(codes))
+
+
+def test_pack_degenerate(B):
+    w = np.zeros((70, 300), np.float32)
+    packed, g = B.pack_weights(dev(w))
+    assert host(g)[0] == 0 and not host(packed).any()
+    packed, g = B.pack_weights(dev(w), eps=0.0)
+    assert not host(packed).any()
+    # the two-readings example: divisor gamma + eps
+    w = np.array([[0.4375, -0.4375, 1.0, -1.375]], np.float32)
+    packed, g = B.pack_weights(dev(w), eps=0.1875)
+    assert host(g)[0] == np.float32(0.8125)
+    np.testing.assert_array_equal(O.unpack_ternary(host(packed), 1, 4), [[0, 0, 1, -1]])
+
+
+# ---------------------------------------------------------------- forward --
+FWD_CASES = [
+    # m, n, k, relu2, y dtype, x dtype
+    (1, 1, 1, False, "f32", "f32"),
+    (1, 256, 256, False, "f32", "f32"),
+    (1, 100, 272, True, "bf16", "bf16"),
+    (2, 640, 2560, False, "bf16", "bf16"),
+    (3, 130, 520, True, "f32", "f32"),
+    (4, 300, 1000, False, "f32", "bf16"),
+    (1, 64, 8192, False, "f32", "bf16"),
+    (5, 200, 600, False, "f32", "f32"),
+    (16, 256, 512, True, "bf16", "bf16"),
+    (17, 300, 1000, False, "f32", "bf16"),
+    (32, 640, 2560, False, "bf16", "bf16"),
+    (33, 100, 257, True, "f32", "f32"),
+    (64, 512, 2560, False, "bf16", "bf16"),
+    (65, 129, 300, False, "f32", "f32"),
+    (130, 320, 1024, True, "bf16", "bf16"),
+    (256, 384, 768, False, "f32", "bf16"),
+]
+
+
+def _forward_case(B, m, n, k, relu2, ydt, xdt, seed):
+    import torch
+    w, x = random_case(seed, m, n, k, x_kind="t3")
+    if m > 3:
+        x[3] = 0.0
+    xd, xo = x_device(x, xdt)
+    packed, gamma = B.pack_weights(dev(w))
+    xq, s = B.quant_act(xd)
+    y, acc = B.forward(xq, s, packed, gamma, n, k, relu2=relu2,
+                       out_dtype=torch.bfloat16 if ydt == "bf16" else torch.float32, acc_out=True)
+    g = host(gamma)[0]
+    assert gamma_agrees(g, w)
+    r = O.forward(xo, w, relu2=relu2, y_dtype=ydt, gamma=g)
+    np.testing.assert_array_equal(host(acc), r["acc"])
+    assert_y_close(host(y), r["y"], ydt, f"m={m} n={n} k={k}")
+
+
+@pytest.mark.parametrize("m,n,k,relu2,ydt,xdt", FWD_CASES)
+def test_forward(B, m, n, k, relu2, ydt, xdt):
+    log(f"forward m={m} n={n} k={k} relu2={relu2} y={ydt} x={xdt}")
+    _forward_case(B, m, n, k, relu2, ydt, xdt, seed=m * 1000003 + n * 101 + k)
+
+
+def test_forward_worked_example(B):
+    import json, os
+    import torch
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
+    w = np.array(gold["weights_basic"]["w"], np.float32)
+    x = np.array(gold["activations"]["x"], np.float32)
+    f = gold["forward"]
+    packed, gamma = B.pack_weights(dev(w))
+    xq, s = B.quant_act(dev(x))
+    y, acc = B.forward(xq, s, packed, gamma, 2, 4, acc_out=True)
+    np.testing.assert_array_equal(host(acc), f["acc"])
+    np.testing.assert_array_equal(host(y), np.array(f["y_f32"], np.float32))
+    y2 = B.forward(xq, s, packed, gamma, 2, 4, relu2=True)
+    np.testing.assert_array_equal(host(y2), np.array(f["y_relu2_f32"], np.float32))
+    yb = B.forward(xq, s, packed, gamma, 2, 4, out_dtype=torch.bfloat16)
+    np.testing.assert_array_equal(O.bf16_bits_to_f32(host(yb)), np.array(f["y_bf16"], np.float32))
+
+
+def test_forward_extreme_accumulator(B):
+    # every code +1 or -1 against full-scale activations: |acc| = 127*K
+    import torch
+    k = 8192
+    w = np.ones((64, k), np.float32)
+    w[1::2] *= -1
+    x = np.full((3, k), 5.0, np.float32)
+    x[1] *= -1
+    packed, gamma = B.pack_weights(dev(w))
+    xq, s = B.quant_act(dev(x))
+    _, acc = B.forward(xq, s, packed, gamma, 64, k, acc_out=True)
+    a = host(acc)
+    assert a[0, 0] == 127 * k and a[0, 1] == -127 * k and a[1, 0] == -127 * k
+    xq5, s5 = B.quant_act(dev(np.tile(x, (3, 1))))
+    _, acc5 = B.forward(xq5, s5, packed, gamma, 64, k, acc_out=True)
+    assert host(acc5)[0, 0] == 127 * k and host(acc5)[4, 0] == -127 * k
+
+
+def test_forward_deterministic_and_workspace_clean(B):
+    import torch
+    w, x = random_case(9, 4, 2560, 6912)
+    packed, gamma = B.pack_weights(dev(w))
+    xq, s = B.quant_act(dev(x))
+    ws = B.Workspace()
+    outs = [host(B.forward(xq, s, packed, gamma, 2560, 6912, workspace=ws)) for _ in range(3)]
+    assert B.forward_workspace_bytes(4, 2560, 6912) > 0
+    np.testing.assert_array_equal(outs[0], outs[1])
+    np.testing.assert_array_equal(outs[0], outs[2])
+    torch.cuda.synchronize()
+    # M <= 4 splits K per 64-row block: one counter word per block, all zero again
+    nblocks = (2560 + 63) // 64
+    assert not host(ws.buf)[: 4 * nblocks].any(), "split-K counters not reset"
+    r = O.forward(x, w, gamma=host(gamma)[0])
+    from gpu_util import assert_y_close
+    assert_y_close(outs[2], r["y"], "f32")
+
+
+def test_forward_no_write_past_output(B):
+    import torch
+    for (m, n, k) in [(1, 100, 300), (20, 70, 300), (130, 200, 512)]:
+        w, x = random_case(m + n, m, n, k)
+        packed, gamma = B.pack_weights(dev(w))
+        xq, s = B.quant_act(dev(x))
+        buf = torch.full((m * n + 4096,), -7.0, dtype=torch.float32, device="cuda")
+        y = buf[: m * n].view(m, n)
+        B.forward(xq, s, packed, gamma, n, k, y=y)
+        assert torch.all(buf[m * n:] == -7.0).item()
+        r = O.forward(x, w, gamma=host(gamma)[0])
+        assert_y_close(host(y), r["y"], "f32")
+
+
+def test_forward_empty_batch(B):
+    import torch
+    w, _ = random_case(1, 1, 64, 256)
+    packed, gamma = B.pack_weights(dev(w))
+    xq = torch.empty((0, 256), dtype=torch.int8, device="cuda")
+    s = torch.empty(0, dtype=torch.float32, device="cuda")
+    y = B.forward(xq, s, packed, gamma, 64, 256)
+    assert y.shape == (0, 64)
