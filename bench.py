@@ -1,0 +1,351 @@
+"""Benchmark of the BitLinear W1.58A8 forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+Workload (the batch-1 decode set at 2B-class shapes, seeded synthetic data):
+q, o 2560x2560; k, v 640x2560; up 6912x2560 with ReLU^2; down 2560x6912;
+activations bf16 1 x K ~ N(0,1) with 1% of the channels x100; bf16 outputs.
+One step = the whole per-call hot path for that set: absmax int8 quantization
+of the four distinct inputs (q/k/v share one) and the six ternary x int8
+products with their fused gamma/s (+ReLU^2) epilogues.  Weights are packed
+before timing (as at model load) and the packed set is replicated so that
+consecutive steps read different copies -- more bytes than the 256 MB
+Infinity Cache plus L2 -- so every step streams its weights from HBM.
+
+value = algorithmic bytes of a step / step time (GB/s).  Per step the
+algorithmic bytes are, for each matrix, N*K/4 (packed W) + M*K (x~) + 4M (s)
++ 4 (gamma) + 2*M*N (bf16 y), plus for each input 2*M*K (bf16 x) + M*K (x~)
++ 4M (s).
+
+Also reported on the same line:
+  roofline      the dominant kernel (the batch-1 dot4 GEMV): algorithmic
+                bytes per launch / its mean launch duration, from HIP events
+                around graph replays of back-to-back launches on the stream
+                the kernels run on;
+  prefill       2048-token prefill GEMMs (2048x2560 -> 6912 with ReLU^2, and
+                2048x6912 -> 2560): 2*M*N*K / kernel time, in TOPS;
+  decode_100b   batch-1 GEMV at 100B-class shapes (up 28672x8192, down
+                8192x28672), 5 weight copies each, GB/s;
+  cpu_baseline  the CPU oracle (numpy) on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA, 5.0 POPS
+CACHE_BYTES = (256 + 32) << 20   # Infinity Cache + 8 x 4 MB L2
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+# --------------------------------------------------------------- helpers --
+def gemv_bytes(m, n, k):
+    return n * k / 4 + m * k + 4 * m + 4 + 2 * m * n
+
+
+def quant_bytes(m, k):
+    return 2 * m * k + m * k + 4 * m
+
+
+class DecodeSet:
+    """Packed weights (several copies), inputs and outputs of one matrix set."""
+
+    def __init__(self, B, torch, wl, m, copies, names=None):
+        import datagen
+        self.B, self.torch, self.m = B, torch, m
+        self.names = names or list(wl.matrices.keys())
+        self.mats = {}
+        for name in self.names:
+            n, k, relu2, group = wl.matrices[name]
+            w = torch.from_numpy(datagen.workload_weights(wl, name)).cuda()
+            packed, gamma = B.pack_weights(w)
+            del w
+            cps = [packed] + [packed.clone() for _ in range(copies - 1)]
+            self.mats[name] = dict(n=n, k=k, relu2=relu2, group=group, packed=cps, gamma=gamma)
+        self.groups = []
+        for name in self.names:
+            g = self.mats[name]["group"]
+            if g not in self.groups:
+                self.groups.append(g)
+        self.x, self.xq, self.s = {}, {}, {}
+        for g in self.groups:
+            bits, _ = datagen.activations(wl, g, m)
+            x = torch.from_numpy(bits.view("int16")).view(torch.bfloat16).cuda()
+            self.x[g] = x
+            xq, s = B.quant_act(x)
+            self.xq[g], self.s[g] = xq, s
+        self.y = {nm: torch.empty((m, d["n"]), dtype=torch.bfloat16, device="cuda")
+                  for nm, d in self.mats.items()}
+        self.ws = B.Workspace()
+        need = max(B.forward_workspace_bytes(m, d["n"], d["k"]) for d in self.mats.values())
+        self.ws.get(need)
+        self.copies = copies
+
+    def bytes_step(self):
+        b = sum(gemv_bytes(self.m, d["n"], d["k"]) for d in self.mats.values())
+        b += sum(quant_bytes(self.m, self.x[g].shape[1]) for g in self.groups)
+        return b
+
+    def quant_into(self):
+        B, lib = self.B, self.B.lib
+        st = B._stream()
+        for g in self.groups:
+            x = self.x[g]
+            B._check("quant", lib.bitlinear_quant_act(x.data_ptr(), B.BL_BF16, x.shape[0], x.shape[1],
+                                                      B.EPS_DEFAULT, self.xq[g].data_ptr(),
+                                                      self.s[g].data_ptr(), st))
+
+    def forward_one(self, name, copy):
+        d = self.mats[name]
+        self.B.forward(self.xq[d["group"]], self.s[d["group"]], d["packed"][copy], d["gamma"],
+                       d["n"], d["k"], relu2=d["relu2"], y=self.y[name], workspace=self.ws)
+
+    def step(self, copy):
+        self.quant_into()
+        for name in self.names:
+            self.forward_one(name, copy)
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                       # warm once outside capture on the same stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(torch, graphs, reps, warmup):
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for i in range(reps):
+        graphs[i % len(graphs)].replay()
+    en.record()
+    torch.cuda.synchronize()
+    return st.elapsed_time(en) / reps    # ms per replay
+
+
+# ------------------------------------------------------------- workloads --
+def run_decode(B, torch, args):
+    import datagen
+    wl = datagen.WORKLOADS["c2"]
+    set_bytes = sum(B.packed_bytes(n, k) for (n, k, _, _) in wl.matrices.values())
+    copies = max(2, math.ceil(2 * CACHE_BYTES / set_bytes))
+    log(f"decode set: {set_bytes/1e6:.2f} MB packed, {copies} copies")
+    ds = DecodeSet(B, torch, wl, 1, copies)
+    torch.cuda.synchronize()
+
+    # one graph per weight copy: quant x4 + forward x6
+    graphs = [capture(torch, lambda c=c: ds.step(c)) for c in range(copies)]
+    # check the graph replay against an eager step, bit for bit
+    ds.step(0)
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in ds.y.items()}
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    for k in eager:
+        assert torch.equal(eager[k].view(torch.int16), ds.y[k].view(torch.int16)), k
+
+    # steady state: whole steps
+    ms = time_graphs(torch, graphs, args.steps, args.warmup)
+    step_bytes = ds.bytes_step()
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    # dominant kernel: the GEMVs alone, back to back, rotating copies
+    gemv_graphs = [capture(torch, lambda c=c: [ds.forward_one(nm, c) for nm in ds.names])
+                   for c in range(copies)]
+    reps = max(args.steps, 2 * copies)
+    ms_gemv_set = time_graphs(torch, gemv_graphs, reps, args.warmup)
+    launches = len(ds.names)
+    gemv_b = sum(gemv_bytes(1, d["n"], d["k"]) for d in ds.mats.values())
+    per_launch_us = ms_gemv_set * 1e3 / launches
+    achieved = gemv_b / (ms_gemv_set * 1e-3) / 1e9
+    per_matrix = {}
+    for nm in ds.names:
+        gs = [capture(torch, lambda c=c, nm=nm: ds.forward_one(nm, c)) for c in range(copies)]
+        t = time_graphs(torch, gs, max(args.steps, 2 * copies), args.warmup)
+        d = ds.mats[nm]
+        per_matrix[nm] = {"us": round(t * 1e3, 3),
+                          "GBs": round(gemv_bytes(1, d["n"], d["k"]) / (t * 1e-3) / 1e9, 1)}
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "gemv_kernel<1> (batch-1 dot4 GEMV, fused dequant)",
+            "bytes_per_launch": round(gemv_b / launches), "us_per_launch": round(per_launch_us, 3),
+            "per_matrix": per_matrix}
+    return ds, value, ms, step_bytes, roof, copies
+
+
+def run_prefill(B, torch, args):
+    import datagen
+    wl = datagen.WORKLOADS["c4"]
+    out = {}
+    tot_ops, tot_ms = 0.0, 0.0
+    for name in ("up", "down"):
+        n, k, relu2, group = wl.matrices[name]
+        m = 2048
+        w = torch.from_numpy(datagen.workload_weights(wl, name)).cuda()
+        packed, gamma = B.pack_weights(w)
+        del w
+        bits, _ = datagen.activations(wl, group, m)
+        x = torch.from_numpy(bits.view("int16")).view(torch.bfloat16).cuda()
+        xq, s = B.quant_act(x)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        ws = B.Workspace()
+        ws.get(B.forward_workspace_bytes(m, n, k))
+        g = capture(torch, lambda: B.forward(xq, s, packed, gamma, n, k, relu2=relu2, y=y, workspace=ws))
+        t = time_graphs(torch, [g], max(20, args.steps // 4), 5)
+        ops = 2.0 * m * n * k
+        tops = ops / (t * 1e-3) / 1e12
+        out[name] = {"shape": f"{m}x{k}->{n}", "us": round(t * 1e3, 2), "TOPS": round(tops, 1),
+                     "frac": round(tops / INT8_PEAK_TOPS, 4)}
+        tot_ops += ops
+        tot_ms += t
+        del packed, xq, x, y
+    tops = tot_ops / (tot_ms * 1e-3) / 1e12
+    return {"workload": "c4 prefill, 2048 tokens", "TOPS": round(tops, 1), "unit": "TOPS",
+            "peak": INT8_PEAK_TOPS, "frac": round(tops / INT8_PEAK_TOPS, 4), "per_matrix": out}
+
+
+def run_decode_100b(B, torch, args):
+    import datagen
+    wl = datagen.WORKLOADS["c5"]
+    out = {}
+    tb, tt = 0.0, 0.0
+    for name in ("up", "down"):
+        n, k, relu2, group = wl.matrices[name]
+        copies = max(2, math.ceil(2 * CACHE_BYTES / B.packed_bytes(n, k)))
+        ds = DecodeSet(B, torch, wl, 1, copies, names=[name])
+        gs = [capture(torch, lambda c=c: ds.forward_one(name, c)) for c in range(copies)]
+        t = time_graphs(torch, gs, max(args.steps, 4 * copies), args.warmup)
+        b = gemv_bytes(1, n, k)
+        out[name] = {"shape": f"1x{k}->{n}", "us": round(t * 1e3, 3),
+                     "GBs": round(b / (t * 1e-3) / 1e9, 1),
+                     "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "copies": copies}
+        tb += b
+        tt += t
+        del ds, gs
+        torch.cuda.empty_cache()
+    gbs = tb / (tt * 1e-3) / 1e9
+    return {"workload": "c5 batch-1 GEMV, up 28672x8192 and down 8192x28672", "GBs": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "per_matrix": out}
+
+
+def run_cpu_baseline(budget_s=12.0):
+    """The oracle as it stands, on the same decode step: activation quant, the
+    six integer products and the dequant, codes prepared beforehand."""
+    import numpy as np
+    import datagen
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    wl = datagen.WORKLOADS["c2"]
+    mats = {}
+    for name, (n, k, relu2, group) in wl.matrices.items():
+        w = datagen.workload_weights(wl, name)
+        g = O.absmean_gamma(w)
+        mats[name] = (O.ternary_codes(w, g), g, relu2, group, n, k)
+    xs = {}
+    for grp in ("attn_in", "o_in", "up_in", "down_in"):
+        bits, _ = datagen.activations(wl, grp, 1)
+        xs[grp] = O.bf16_bits_to_f32(bits)
+    step_bytes = sum(gemv_bytes(1, n, k) for (_, _, _, _, n, k) in mats.values())
+    step_bytes += sum(quant_bytes(1, x.shape[1]) for x in xs.values())
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        q = {grp: O.quant_act(x) for grp, x in xs.items()}
+        for name, (codes, g, relu2, grp, n, k) in mats.items():
+            xq, s = q[grp]
+            acc = O.contract(xq, codes)
+            O.round_output(O.dequant(acc, g, s, relu2), "bf16")
+        steps += 1
+        el = time.perf_counter() - t0
+        if el > budget_s:
+            break
+    per = el / steps
+    return {"value": round(step_bytes / per / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "ms_per_step": round(per * 1e3, 2),
+            "sample": f"{steps} full decode steps of the same workload (4 act quants, 6 products, "
+                      f"dequant; codes prepared untimed), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip prefill and 100B-class legs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU split is described in DESIGN.md, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_gemm_int8_amd as B
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    ds, value, ms, step_bytes, roof, copies = run_decode(B, torch, args)
+    log(f"decode: {ms*1e3:.2f} us/step, {value:.1f} GB/s; gemv {roof['achieved']} GB/s")
+    prefill = None if args.no_extra else run_prefill(B, torch, args)
+    if prefill:
+        log(f"prefill: {prefill['TOPS']} TOPS")
+    d100 = None if args.no_extra else run_decode_100b(B, torch, args)
+    if d100:
+        log(f"decode 100B-class: {d100['GBs']} GB/s")
+    cpu = None if args.no_cpu else run_cpu_baseline()
+    line = {
+        "metric": "BitLinear W1.58A8 decode GB/s (% HBM peak) + prefill TOPS (% int8 MFMA)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "batch-1 decode of the 2B-class BitLinear set: q,o 2560x2560; "
+                               "k,v 640x2560; up 6912x2560 (+ReLU^2); down 2560x6912; "
+                               "bf16 in/out, 1% outlier channels x100",
+                   "batch": 1, "weight_copies": copies, "step_bytes": int(step_bytes),
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "prefill": prefill,
+        "decode_100b": d100,
+        "wall_s": round(time.time() - t0, 1),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -8,10 +8,10 @@
 
 namespace bl {
 
-hipError_t launch_gemv(int m, const int8_t* xq, const float* scale, const uint32_t* packed,
-                       const float* gamma, int64_t n, int64_t k, int splits, bool relu2,
-                       bool bf16, void* y, int32_t* acc_out, int32_t* partial,
-                       uint32_t* counters, hipStream_t stream);
+hipError_t launch_gemv(int m, int waves, const int8_t* xq, const float* scale,
+                       const uint32_t* packed, const float* gamma, int64_t n, int64_t k,
+                       int splits, bool relu2, bool bf16, void* y, int32_t* acc_out,
+                       int32_t* ws_acc, uint32_t* counters, hipStream_t stream);
 hipError_t launch_gemm(int variant, const int8_t* xq, const float* scale, const uint32_t* packed,
                        const float* gamma, int64_t m, int64_t n, int64_t k, int splits,
                        bool relu2, bool bf16, void* y, int32_t* acc_out, int32_t* partial,
@@ -27,7 +27,8 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t words) {
 }
 
 constexpr int64_t kGemvMaxM = 4;
-constexpr int64_t kGemvTargetWaves = 2048;
+constexpr int64_t kGemvTargetGroups = 512;
+constexpr int64_t kGemvMaxLds = 48 * 1024;
 constexpr int64_t kGemmTargetGroups = 512;
 
 inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
@@ -48,14 +49,24 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
   const int64_t nc = cdiv(k, kSuperK);
   if (m <= 0) return p;
   if (m <= kGemvMaxM) {
+    // Waves per workgroup and workgroups per 64-row block.  Many row blocks:
+    // 4 waves each stream a quarter of K.  Few row blocks: 8 waves, and the
+    // block is split over up to 4 workgroups (atomic reduction) while every
+    // wave keeps >= 1 super-chunk.  Then each group's x~ slice must fit LDS.
     p.kind = 0;
-    p.variant = 0;
-    int64_t s = cdiv(kGemvTargetWaves, nb);
-    if (s > nc) s = nc;
-    if (s < 1) s = 1;
+    int waves = nb >= 256 ? 4 : 8;
+    int64_t s = 1;
+    if (nb < 256) {
+      s = cdiv(kGemvTargetGroups, nb);
+      const int64_t smax = nc / waves > 1 ? nc / waves : 1;
+      if (s > smax) s = smax;
+      if (s > 4) s = 4;
+    }
+    while (m * cdiv(nc, s) * 256 > kGemvMaxLds) ++s;
+    p.variant = waves;
     p.splits = (int)s;
     p.tiles = (int)nb;
-    p.partial_ints = s > 1 ? (size_t)(nb * s * m * 64) : 0;
+    p.partial_ints = s > 1 ? (size_t)(nb * m * 64) : 0;
   } else {
     p.kind = 1;
     p.variant = m <= 16 ? 0 : m <= 32 ? 1 : m <= 64 ? 2 : 3;
@@ -68,7 +79,7 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     if (s < 1) s = 1;
     p.splits = (int)s;
     p.tiles = (int)tiles;
-    p.partial_ints = s > 1 ? (size_t)(tiles * s * bm * bn) : 0;
+    p.partial_ints = s > 1 ? (size_t)(tiles * bm * bn) : 0;
   }
   p.ws_bytes = p.splits > 1 ? round_up((size_t)p.tiles * 4, 256) + p.partial_ints * 4 : 0;
   return p;
@@ -86,8 +97,8 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
                                          round_up((size_t)plan.tiles * 4, 256));
   }
   if (plan.kind == 0)
-    return launch_gemv((int)m, xq, scale, packed, gamma, n, k, plan.splits, relu2, bf16, y,
-                       acc_out, partial, counters, stream);
+    return launch_gemv((int)m, plan.variant, xq, scale, packed, gamma, n, k, plan.splits, relu2,
+                       bf16, y, acc_out, partial, counters, stream);
   return launch_gemm(plan.variant, xq, scale, packed, gamma, m, n, k, plan.splits, relu2, bf16,
                      y, acc_out, partial, counters, stream);
 }

@@ -81,25 +81,4 @@ __device__ __forceinline__ void store_out(void* y, int64_t idx, int acc, float f
     reinterpret_cast<float*>(y)[idx] = v;
 }
 
-// Split-K completion.  Call after this workgroup stored its partial results:
-// returns true for exactly one workgroup of the tile -- the last to finish --
-// which then reads every split's partials.  The counter goes back to zero,
-// so the workspace is ready for the next call.  All threads must call it.
-__device__ __forceinline__ bool splitk_last_arrival(uint32_t* counter, int splits,
-                                                    uint32_t* lds_flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    bool last = prev == (uint32_t)(splits - 1);
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *lds_flag = last ? 1u : 0u;
-  }
-  __syncthreads();
-  bool last = *lds_flag != 0u;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
-}
-
 }  // namespace bl

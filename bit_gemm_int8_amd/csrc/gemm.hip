@@ -21,8 +21,8 @@
 // The 16x16 int32 result holds row 4 g + i, column r in element i of lane l.
 //
 // Global loads of super-chunk c+1 are issued before the MFMAs of c (register
-// staging, one LDS buffer).  Split-K over super-chunks uses the workspace
-// and a last-arrival reduction, as in the GEMV.
+// staging, one LDS buffer).  Split-K over super-chunks adds tiles into the
+// workspace with device-scope atomics, as in the GEMV.
 #include "bl_device.h"
 #include "bl_internal.h"
 
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ scale,
     const uint4* __restrict__ packed, const float* __restrict__ gamma, int m, int n,
     int nb, int nc, int64_t kpad, int splits, int tiles_n, int relu2, int bf16,
-    void* __restrict__ y, int32_t* __restrict__ acc_out, int32_t* __restrict__ partial,
+    void* __restrict__ y, int32_t* __restrict__ acc_out, int32_t* __restrict__ ws_acc,
     uint32_t* __restrict__ counters) {
   using T = Tile<FM, FN, WM, WN>;
   constexpr int BM = T::BM, BN = T::BN, NT = T::NT, BNB = T::BNB, UA = T::UA, UB = T::UB;
@@ -146,31 +146,43 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
   }
 
   if (splits > 1) {
+    // Split-K: add this group's tile into the workspace accumulator with
+    // device-scope atomics (each returns, so it has been performed before
+    // the tile's counter is bumped); the group that completes the count reads
+    // the totals and leaves the accumulator and the counter at zero.
     constexpr int NE = FM * FN * 4;
-    int32_t* part = partial + ((int64_t)tile * splits + s) * (int64_t)(BM * BN);
+    int32_t* slot = ws_acc + (int64_t)tile * (BM * BN) + tid;
+    int done = 0;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part[((fm * FN + fn) * 4 + i) * NT + tid] = acc[fm][fn][i];
-    if (!splitk_last_arrival(&counters[tile], splits, &flag)) return;
-    const int32_t* all = partial + (int64_t)tile * splits * (int64_t)(BM * BN);
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[fm][fn][i] = 0;
-    for (int t = 0; t < splits; ++t) {
-      const int32_t* pt = all + (int64_t)t * (BM * BN);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[fm][fn][i] += pt[((fm * FN + fn) * 4 + i) * NT + tid];
+        for (int i = 0; i < 4; ++i)
+          done |= __hip_atomic_fetch_add(slot + ((fm * FN + fn) * 4 + i) * NT, acc[fm][fn][i],
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::"v"(done));
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+      const uint32_t prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      flag = prev == (uint32_t)(splits - 1) ? 1u : 0u;
     }
+    __syncthreads();
+    if (flag == 0u) return;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int32_t* p = slot + ((fm * FN + fn) * 4 + i) * NT;
+          acc[fm][fn][i] = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    if (tid == 0)
+      __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     (void)NE;
   }
 

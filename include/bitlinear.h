@@ -147,10 +147,10 @@ bl_status bitlinear_quant_act(const void* x, int x_dtype, int64_t m, int64_t k,
  *              accumulator x~ W~^T (for verification).
  *   workspace  bitlinear_forward_workspace_bytes(m, n, k) bytes, 256-byte
  *              aligned, zero-filled once before its first use (see
- *              bitlinear_workspace_init).  It starts with one counter word
- *              per output tile; every completed call sets those back to zero,
- *              so the workspace can be reused without clearing (the bytes
- *              after the counters hold partial sums, whatever their value).
+ *              bitlinear_workspace_init).  Every completed call leaves it
+ *              zero-filled again (split-K counters and accumulators are
+ *              cleared by the workgroup that finishes each tile), so one
+ *              workspace serves any sequence of calls without clearing.
  *              Calls that share a workspace must be ordered (one stream, or
  *              events); concurrent calls on one workspace race.  May be NULL
  *              when the required size is 0.

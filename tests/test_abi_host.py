@@ -115,11 +115,11 @@ def test_forward_rejects(bl):
     assert call(y=FAKE + 2) == 3
     assert call(y=FAKE + 2, yd=1) != 3 or True   # bf16 output only needs 2-byte alignment
     # a shape that splits K needs a workspace
-    need = bl.forward_workspace_bytes(1, 64, 8192)
+    need = bl.forward_workspace_bytes(1, 64, 65536)
     assert need > 0
-    assert call(m=1, k=8192, ws=None) == 4
-    assert call(m=1, k=8192, wsb=need - 4) == 4
-    assert call(m=1, k=8192, ws=FAKE + 16, wsb=need) == 3
+    assert call(m=1, k=65536, ws=None) == 4
+    assert call(m=1, k=65536, wsb=need - 4) == 4
+    assert call(m=1, k=65536, ws=FAKE + 16, wsb=need) == 3
     assert call(m=0, xq=None, y=None) == 0        # empty batch: no-op
 
 

@@ -155,6 +155,11 @@ FWD_CASES = [
     (3, 130, 520, True, "f32", "f32"),
     (4, 300, 1000, False, "f32", "bf16"),
     (1, 64, 8192, False, "f32", "bf16"),
+    (1, 200, 16384, True, "bf16", "bf16"),
+    (4, 100, 30000, False, "f32", "f32"),
+    (3, 130, 40000, False, "bf16", "bf16"),
+    (4, 70, 65536, False, "f32", "bf16"),
+    (1, 20000, 512, False, "bf16", "bf16"),
     (5, 200, 600, False, "f32", "f32"),
     (16, 256, 512, True, "bf16", "bf16"),
     (17, 300, 1000, False, "f32", "bf16"),
@@ -237,12 +242,29 @@ def test_forward_deterministic_and_workspace_clean(B):
     np.testing.assert_array_equal(outs[0], outs[1])
     np.testing.assert_array_equal(outs[0], outs[2])
     torch.cuda.synchronize()
-    # M <= 4 splits K per 64-row block: one counter word per block, all zero again
-    nblocks = (2560 + 63) // 64
-    assert not host(ws.buf)[: 4 * nblocks].any(), "split-K counters not reset"
+    assert not host(ws.buf).any(), "workspace not left zero-filled"
     r = O.forward(x, w, gamma=host(gamma)[0])
     from gpu_util import assert_y_close
     assert_y_close(outs[2], r["y"], "f32")
+
+
+def test_workspace_shared_across_paths(B):
+    # split-K GEMM and split-K GEMV calls alternate on one workspace; every
+    # call must find it zero-filled and leave it so.
+    import torch
+    ws = B.Workspace()
+    cases = [(16, 256, 8192), (1, 64, 8192), (40, 300, 4096), (3, 64, 8192), (1, 200, 16384),
+             (16, 256, 8192)]
+    for (m, n, k) in cases:
+        assert B.forward_workspace_bytes(m, n, k) > 0, (m, n, k)
+        w, x = random_case(m * 7 + n + k, m, n, k, x_kind="t3")
+        packed, gamma = B.pack_weights(dev(w))
+        xq, s = B.quant_act(dev(x))
+        y, acc = B.forward(xq, s, packed, gamma, n, k, workspace=ws, acc_out=True)
+        r = O.forward(x, w, gamma=host(gamma)[0])
+        np.testing.assert_array_equal(host(acc), r["acc"], err_msg=str((m, n, k)))
+        torch.cuda.synchronize()
+        assert not host(ws.buf).any(), f"workspace not clean after {(m, n, k)}"
 
 
 def test_forward_no_write_past_output(B):
