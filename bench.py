@@ -12,20 +12,21 @@ before timing (as at model load) and the packed set is replicated so that
 consecutive steps read different copies -- more bytes than the 256 MB
 Infinity Cache plus L2 -- so every step streams its weights from HBM.
 
-value = algorithmic bytes of a step / step time (GB/s).  Per step the
-algorithmic bytes are, for each matrix, N*K/4 (packed W) + M*K (x~) + 4M (s)
-+ 4 (gamma) + 2*M*N (bf16 y), plus for each input 2*M*K (bf16 x) + M*K (x~)
-+ 4M (s).
+A step is one launch of the fused decode kernel (bitlinear_forward_fused):
+each workgroup quantizes its slice of the activations into LDS and streams
+its packed weights.  value = algorithmic bytes of a step / step time (GB/s):
+for each matrix N*K/4 (packed W) + 4 (gamma) + 2*M*N (bf16 y), plus each
+distinct bf16 input once, 2*M*K (x~ never leaves the chip).
 
 Also reported on the same line:
-  roofline      the dominant kernel (the batch-1 dot4 GEMV): algorithmic
-                bytes per launch / its mean launch duration, from HIP events
-                around graph replays of back-to-back launches on the stream
-                the kernels run on;
+  roofline      the step's kernel: algorithmic bytes per launch / its mean
+                launch duration, from HIP events around a graph replay of
+                back-to-back launches on the stream the kernels run on; also
+                the same step unfused and each matrix's plain GEMV;
   prefill       2048-token prefill GEMMs (2048x2560 -> 6912 with ReLU^2, and
                 2048x6912 -> 2560): 2*M*N*K / kernel time, in TOPS;
   decode_100b   batch-1 GEMV at 100B-class shapes (up 28672x8192, down
-                8192x28672), 5 weight copies each, GB/s;
+                8192x28672), weights rotated past the caches, GB/s;
   cpu_baseline  the CPU oracle (numpy) on a bounded sample of the same step.
 """
 from __future__ import annotations
@@ -99,6 +100,13 @@ class DecodeSet:
         b += sum(quant_bytes(self.m, self.x[g].shape[1]) for g in self.groups)
         return b
 
+    def bytes_step_fused(self):
+        """Bytes a step must move: packed weights, gamma, bf16 outputs, and
+        each distinct bf16 input once."""
+        b = sum(d["n"] * d["k"] / 4 + 4 + 2 * self.m * d["n"] for d in self.mats.values())
+        b += sum(2 * self.m * self.x[g].shape[1] for g in self.groups)
+        return b
+
     def quant_into(self):
         B, lib = self.B, self.B.lib
         st = B._stream()
@@ -118,6 +126,18 @@ class DecodeSet:
         for name in self.names:
             self.forward_one(name, copy)
 
+    def fused_steps(self):
+        """One prepared fused call (all matrices, one launch) per weight copy."""
+        out = []
+        for c in range(self.copies):
+            ops = []
+            for nm in self.names:
+                d = self.mats[nm]
+                ops.append(dict(x=self.x[d["group"]], packed=d["packed"][c], gamma=d["gamma"],
+                                n=d["n"], k=d["k"], y=self.y[nm], relu2=d["relu2"]))
+            out.append(self.B.FusedStep(ops, workspace=self.ws))
+        return out
+
 
 def capture(torch, fn):
     g = torch.cuda.CUDAGraph()
@@ -133,66 +153,95 @@ def capture(torch, fn):
     return g
 
 
-def time_graphs(torch, graphs, reps, warmup):
-    for i in range(warmup):
-        graphs[i % len(graphs)].replay()
+def time_launches(torch, launch, count, per_graph, reps=3):
+    """Mean GPU time of one launch: `per_graph` launches launch(i) captured in
+    one graph (i cycles through `count` variants, e.g. weight copies), the
+    graph replayed after a warm-up; best of `reps` timed replays."""
+    g = capture(torch, lambda: [launch(i % count) for i in range(per_graph)])
+    g.replay()
     torch.cuda.synchronize()
-    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    st.record()
-    for i in range(reps):
-        graphs[i % len(graphs)].replay()
-    en.record()
-    torch.cuda.synchronize()
-    return st.elapsed_time(en) / reps    # ms per replay
+    best = float("inf")
+    for _ in range(reps):
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        g.replay()
+        en.record()
+        torch.cuda.synchronize()
+        best = min(best, st.elapsed_time(en))
+    return best / per_graph        # ms
 
 
 # ------------------------------------------------------------- workloads --
+GRAPH_STEPS = 10
+
+
 def run_decode(B, torch, args):
     import datagen
     wl = datagen.WORKLOADS["c2"]
     set_bytes = sum(B.packed_bytes(n, k) for (n, k, _, _) in wl.matrices.values())
     copies = max(2, math.ceil(2 * CACHE_BYTES / set_bytes))
+    copies = GRAPH_STEPS * math.ceil(copies / GRAPH_STEPS)
     log(f"decode set: {set_bytes/1e6:.2f} MB packed, {copies} copies")
     ds = DecodeSet(B, torch, wl, 1, copies)
+    fused = ds.fused_steps()
     torch.cuda.synchronize()
 
-    # one graph per weight copy: quant x4 + forward x6
-    graphs = [capture(torch, lambda c=c: ds.step(c)) for c in range(copies)]
-    # check the graph replay against an eager step, bit for bit
+    # the fused step against the unfused one (quant + forward per matrix), bitwise
     ds.step(0)
     torch.cuda.synchronize()
-    eager = {k: v.clone() for k, v in ds.y.items()}
-    graphs[0].replay()
+    ref = {k: v.clone() for k, v in ds.y.items()}
+    for v in ds.y.values():
+        v.zero_()
+    fused[0]()
     torch.cuda.synchronize()
-    for k in eager:
-        assert torch.equal(eager[k].view(torch.int16), ds.y[k].view(torch.int16)), k
+    for k in ref:
+        assert torch.equal(ref[k].view(torch.int16), ds.y[k].view(torch.int16)), k
 
-    # steady state: whole steps
-    ms = time_graphs(torch, graphs, args.steps, args.warmup)
-    step_bytes = ds.bytes_step()
+    # graphs of GRAPH_STEPS consecutive steps (consecutive weight copies), and
+    # one-step graphs for a remainder
+    groups = copies // GRAPH_STEPS
+    big = [capture(torch, lambda g0=g0: [fused[g0 * GRAPH_STEPS + i]() for i in range(GRAPH_STEPS)])
+           for g0 in range(groups)]
+    single = [capture(torch, lambda c=c: fused[c]()) for c in range(GRAPH_STEPS)]
+    # replay check against the eager result
+    big[0].replay()
+    torch.cuda.synchronize()
+    for k in ref:
+        assert torch.equal(ref[k].view(torch.int16), ds.y[k].view(torch.int16)), k
+    for i in range(max(1, args.warmup // GRAPH_STEPS)):
+        big[i % groups].replay()
+    torch.cuda.synchronize()
+    nbig, rest = divmod(args.steps, GRAPH_STEPS)
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for i in range(nbig):
+        big[i % groups].replay()
+    for i in range(rest):
+        single[i].replay()
+    en.record()
+    torch.cuda.synchronize()
+    ms = st.elapsed_time(en) / args.steps
+    step_bytes = ds.bytes_step_fused()
     value = step_bytes / (ms * 1e-3) / 1e9
 
-    # dominant kernel: the GEMVs alone, back to back, rotating copies
-    gemv_graphs = [capture(torch, lambda c=c: [ds.forward_one(nm, c) for nm in ds.names])
-                   for c in range(copies)]
-    reps = max(args.steps, 2 * copies)
-    ms_gemv_set = time_graphs(torch, gemv_graphs, reps, args.warmup)
-    launches = len(ds.names)
-    gemv_b = sum(gemv_bytes(1, d["n"], d["k"]) for d in ds.mats.values())
-    per_launch_us = ms_gemv_set * 1e3 / launches
-    achieved = gemv_b / (ms_gemv_set * 1e-3) / 1e9
+    # dominant (only) kernel of the step: the fused decode kernel, timed alone
+    per = copies
+    ms_k = time_launches(torch, lambda c: fused[c](), copies, per)
+    achieved = step_bytes / (ms_k * 1e-3) / 1e9
+    # the same step unfused (quant per input + one GEMV per matrix), and each
+    # matrix's plain GEMV alone
+    ms_unf = time_launches(torch, lambda c: ds.step(c), copies, copies)
     per_matrix = {}
     for nm in ds.names:
-        gs = [capture(torch, lambda c=c, nm=nm: ds.forward_one(nm, c)) for c in range(copies)]
-        t = time_graphs(torch, gs, max(args.steps, 2 * copies), args.warmup)
         d = ds.mats[nm]
+        t = time_launches(torch, lambda c, nm=nm: ds.forward_one(nm, c), copies, copies)
         per_matrix[nm] = {"us": round(t * 1e3, 3),
                           "GBs": round(gemv_bytes(1, d["n"], d["k"]) / (t * 1e-3) / 1e9, 1)}
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "gemv_kernel<1> (batch-1 dot4 GEMV, fused dequant)",
-            "bytes_per_launch": round(gemv_b / launches), "us_per_launch": round(per_launch_us, 3),
-            "per_matrix": per_matrix}
+            "kernel": "gemv_fused_kernel<1,8,2> (act quant + batch-1 GEMV + dequant, 6 matrices)",
+            "bytes_per_launch": int(step_bytes), "us_per_launch": round(ms_k * 1e3, 3),
+            "unfused_step_us": round(ms_unf * 1e3, 3), "plain_gemv_per_matrix": per_matrix}
     return ds, value, ms, step_bytes, roof, copies
 
 
@@ -213,12 +262,13 @@ def run_prefill(B, torch, args):
         y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
         ws = B.Workspace()
         ws.get(B.forward_workspace_bytes(m, n, k))
-        g = capture(torch, lambda: B.forward(xq, s, packed, gamma, n, k, relu2=relu2, y=y, workspace=ws))
-        t = time_graphs(torch, [g], max(20, args.steps // 4), 5)
+        t = time_launches(torch, lambda c: B.forward(xq, s, packed, gamma, n, k, relu2=relu2, y=y,
+                                                     workspace=ws), 1, 20)
+        tq = time_launches(torch, lambda c: B.quant_act(x), 1, 20)
         ops = 2.0 * m * n * k
         tops = ops / (t * 1e-3) / 1e12
         out[name] = {"shape": f"{m}x{k}->{n}", "us": round(t * 1e3, 2), "TOPS": round(tops, 1),
-                     "frac": round(tops / INT8_PEAK_TOPS, 4)}
+                     "frac": round(tops / INT8_PEAK_TOPS, 4), "act_quant_us": round(tq * 1e3, 2)}
         tot_ops += ops
         tot_ms += t
         del packed, xq, x, y
@@ -236,19 +286,21 @@ def run_decode_100b(B, torch, args):
         n, k, relu2, group = wl.matrices[name]
         copies = max(2, math.ceil(2 * CACHE_BYTES / B.packed_bytes(n, k)))
         ds = DecodeSet(B, torch, wl, 1, copies, names=[name])
-        gs = [capture(torch, lambda c=c: ds.forward_one(name, c)) for c in range(copies)]
-        t = time_graphs(torch, gs, max(args.steps, 4 * copies), args.warmup)
+        fused = ds.fused_steps()
+        t = time_launches(torch, lambda c: fused[c](), copies, 4 * copies)
+        tp = time_launches(torch, lambda c: ds.forward_one(name, c), copies, 4 * copies)
         b = gemv_bytes(1, n, k)
         out[name] = {"shape": f"1x{k}->{n}", "us": round(t * 1e3, 3),
                      "GBs": round(b / (t * 1e-3) / 1e9, 1),
-                     "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "copies": copies}
+                     "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "plain_gemv_us": round(tp * 1e3, 3), "copies": copies}
         tb += b
         tt += t
-        del ds, gs
+        del ds, fused
         torch.cuda.empty_cache()
     gbs = tb / (tt * 1e-3) / 1e9
-    return {"workload": "c5 batch-1 GEMV, up 28672x8192 and down 8192x28672", "GBs": round(gbs, 1),
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "per_matrix": out}
+    return {"workload": "c5 batch-1 fused GEMV, up 28672x8192 and down 8192x28672",
+            "GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "per_matrix": out}
 
 
 def run_cpu_baseline(budget_s=12.0):

@@ -35,7 +35,19 @@ EXPORTS = [
     "bitlinear_pack_workspace_bytes", "bitlinear_pack_weights", "bitlinear_quant_act",
     "bitlinear_forward_workspace_bytes", "bitlinear_forward", "bitlinear_workspace_init",
     "bitlinear_status_string", "bitlinear_abi_version",
+    "bitlinear_forward_fused_workspace_bytes", "bitlinear_forward_fused",
 ]
+BL_MAX_FUSED = 16
+BL_FUSED_MAX_M = 4
+
+
+class BLLinear(ctypes.Structure):
+    """bl_linear of include/bitlinear.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int), ("packed", ctypes.c_void_p),
+                ("gamma", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("epilogue", ctypes.c_int), ("y_dtype", ctypes.c_int), ("y", ctypes.c_void_p),
+                ("acc_out", ctypes.c_void_p), ("xq_out", ctypes.c_void_p),
+                ("scale_out", ctypes.c_void_p)]
 
 
 class BitLinearError(RuntimeError):
@@ -63,6 +75,8 @@ def _load() -> ctypes.CDLL:
         "bitlinear_workspace_init": (i32, [vp, sz, vp]),
         "bitlinear_status_string": (ctypes.c_char_p, [i32]),
         "bitlinear_abi_version": (i32, []),
+        "bitlinear_forward_fused_workspace_bytes": (sz, [vp, i32, i64]),
+        "bitlinear_forward_fused": (i32, [vp, i32, i64, f32, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -194,3 +208,44 @@ def forward(xq, scale, packed, gamma, n: int, k: int, relu2: bool = False,
         BL_EPI_RELU2 if relu2 else BL_EPI_NONE, _dtype_code(y.dtype), _ptr(y), _ptr(acc),
         _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return (y, acc) if acc_out else y
+
+
+class FusedStep:
+    """A prepared bitlinear_forward_fused call: a table of BitLinear products
+    sharing the token count m, each quantizing its own activations.
+
+    ops: list of dicts with keys x, packed, gamma, n, k, y and optional
+    relu2, acc_out, xq_out, scale_out (tensors on the device)."""
+
+    def __init__(self, ops, eps: float = EPS_DEFAULT, workspace: Optional[Workspace] = None):
+        if not 1 <= len(ops) <= BL_MAX_FUSED:
+            raise ValueError(f"1..{BL_MAX_FUSED} entries")
+        self.ops = ops
+        self.m = int(ops[0]["x"].shape[0])
+        self.eps = float(eps)
+        arr = (BLLinear * len(ops))()
+        for i, o in enumerate(ops):
+            x, y = o["x"], o["y"]
+            if x.shape[0] != self.m or y.shape != (self.m, o["n"]):
+                raise ValueError("every entry needs x [m, k] and y [m, n] with the same m")
+            arr[i] = BLLinear(_ptr(x), _dtype_code(x.dtype), _ptr(o["packed"]), _ptr(o["gamma"]),
+                              int(o["n"]), int(o["k"]),
+                              BL_EPI_RELU2 if o.get("relu2") else BL_EPI_NONE,
+                              _dtype_code(y.dtype), _ptr(y), _ptr(o.get("acc_out")),
+                              _ptr(o.get("xq_out")), _ptr(o.get("scale_out")))
+        self.arr = arr
+        self.nbytes = int(lib.bitlinear_forward_fused_workspace_bytes(arr, len(ops), self.m))
+        self.ws = workspace or Workspace(ops[0]["x"].device)
+        self.ws.get(self.nbytes)
+
+    def __call__(self, stream=None):
+        ws = self.ws.get(self.nbytes, stream)
+        _check("bitlinear_forward_fused", lib.bitlinear_forward_fused(
+            self.arr, len(self.ops), self.m, self.eps, _ptr(ws), 0 if ws is None else ws.numel(),
+            _stream(stream)))
+
+
+def forward_fused(ops, eps: float = EPS_DEFAULT, workspace: Optional[Workspace] = None,
+                  stream=None) -> None:
+    """bitlinear_forward_fused over a list of entries (see FusedStep)."""
+    FusedStep(ops, eps, workspace)(stream)

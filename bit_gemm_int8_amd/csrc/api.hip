@@ -103,6 +103,51 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
                      y, acc_out, partial, counters, stream);
 }
 
+struct FusedPlan {
+  int waves = 8;
+  int groups = 0;
+  size_t lds = 0;
+  size_t ws_bytes = 0;
+  int splits[kMaxFused] = {};
+  size_t counter_off[kMaxFused] = {};   // bytes
+  size_t acc_off[kMaxFused] = {};       // bytes
+};
+
+FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
+  FusedPlan p;
+  int64_t total_nb = 0;
+  for (int i = 0; i < nops; ++i) total_nb += cdiv(ops[i].n, kRowBlock);
+  p.waves = total_nb >= 256 ? 4 : 8;
+  size_t counters = 0, accs = 0;
+  for (int i = 0; i < nops; ++i) {
+    const int64_t nb = cdiv(ops[i].n, kRowBlock), nc = cdiv(ops[i].k, kSuperK);
+    int64_t s = 1;
+    if (total_nb < 256) {
+      s = cdiv(kGemvTargetGroups, total_nb);
+      const int64_t smax = nc / p.waves > 1 ? nc / p.waves : 1;
+      if (s > smax) s = smax;
+      if (s > 4) s = 4;
+    }
+    while (m * cdiv(nc, s) * 256 > kGemvMaxLds) ++s;
+    p.splits[i] = (int)s;
+    p.groups += (int)(nb * s);
+    const size_t lds = (size_t)(m * cdiv(nc, s) * 256);
+    if (lds > p.lds) p.lds = lds;
+    if (s > 1) {
+      p.counter_off[i] = counters * 4;
+      counters += (size_t)nb;
+      p.acc_off[i] = accs * 4;
+      accs += (size_t)(nb * m * 64);
+    }
+  }
+  if (counters > 0) {
+    const size_t base = round_up(counters * 4, 256);
+    for (int i = 0; i < nops; ++i) p.acc_off[i] += base;
+    p.ws_bytes = base + accs * 4;
+  }
+  return p;
+}
+
 }  // namespace bl
 
 using namespace bl;
@@ -150,6 +195,79 @@ size_t bitlinear_pack_workspace_bytes(int64_t n, int64_t k) {
 size_t bitlinear_forward_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0 || k > BL_MAX_K || n > BL_MAX_MN || m > BL_MAX_MN) return 0;
   return forward_plan(m, n, k).ws_bytes;
+}
+
+static bl_status check_fused(const bl_linear* ops, int nops, int64_t m) {
+  if (ops == nullptr || nops < 1 || nops > BL_MAX_FUSED) return BL_ERR_INVALID_ARG;
+  if (m < 0) return BL_ERR_INVALID_ARG;
+  if (m > BL_FUSED_MAX_M) return BL_ERR_UNSUPPORTED_SHAPE;
+  for (int i = 0; i < nops; ++i) {
+    const bl_linear& o = ops[i];
+    if (!valid_dtype(o.x_dtype) || !valid_dtype(o.y_dtype)) return BL_ERR_INVALID_ARG;
+    if (o.epilogue != BL_EPI_NONE && o.epilogue != BL_EPI_RELU2) return BL_ERR_INVALID_ARG;
+    if (o.n < 1 || o.k < 1) return BL_ERR_INVALID_ARG;
+    if (o.n > BL_MAX_MN || o.k > BL_MAX_K) return BL_ERR_UNSUPPORTED_SHAPE;
+    if (m == 0) continue;
+    if (o.x == nullptr || o.packed == nullptr || o.gamma == nullptr || o.y == nullptr)
+      return BL_ERR_INVALID_ARG;
+    if (!aligned(o.x, o.x_dtype == BL_BF16 ? 2 : 4) || !aligned(o.packed, 16) ||
+        !aligned(o.gamma, 4) || !aligned(o.y, o.y_dtype == BL_BF16 ? 2 : 4) ||
+        (o.acc_out != nullptr && !aligned(o.acc_out, 4)) ||
+        (o.xq_out != nullptr && !aligned(o.xq_out, 16)) ||
+        (o.scale_out != nullptr && !aligned(o.scale_out, 4)))
+      return BL_ERR_MISALIGNED;
+  }
+  return BL_OK;
+}
+
+size_t bitlinear_forward_fused_workspace_bytes(const bl_linear* ops, int nops, int64_t m) {
+  if (check_fused(ops, nops, m) != BL_OK || m == 0) return 0;
+  return fused_plan(ops, nops, m).ws_bytes;
+}
+
+bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, float eps,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  const bl_status st = check_fused(ops, nops, m);
+  if (st != BL_OK) return st;
+  if (!valid_eps(eps)) return BL_ERR_INVALID_ARG;
+  if (m == 0) return BL_OK;
+  const FusedPlan plan = fused_plan(ops, nops, m);
+  if (plan.ws_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return BL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return BL_ERR_MISALIGNED;
+  }
+  FusedArgs args{};
+  args.nseg = nops;
+  args.eps = eps;
+  int begin = 0;
+  for (int i = 0; i < nops; ++i) {
+    const bl_linear& o = ops[i];
+    FusedSeg& sg = args.seg[i];
+    sg.x = o.x;
+    sg.packed = o.packed;
+    sg.gamma = o.gamma;
+    sg.y = o.y;
+    sg.acc_out = o.acc_out;
+    sg.xq_out = o.xq_out;
+    sg.scale_out = o.scale_out;
+    sg.n = (int)o.n;
+    sg.k = (int)o.k;
+    sg.nc = (int)cdiv(o.k, kSuperK);
+    sg.splits = plan.splits[i];
+    sg.wg_begin = begin;
+    sg.relu2 = o.epilogue == BL_EPI_RELU2;
+    sg.y_bf16 = o.y_dtype == BL_BF16;
+    sg.x_bf16 = o.x_dtype == BL_BF16;
+    if (sg.splits > 1) {
+      sg.counters = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(workspace) +
+                                                plan.counter_off[i]);
+      sg.ws_acc = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + plan.acc_off[i]);
+    }
+    begin += (int)(cdiv(o.n, kRowBlock) * sg.splits);
+  }
+  const hipError_t e = launch_gemv_fused(args, (int)m, plan.waves, plan.groups, plan.lds,
+                                         reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? BL_OK : BL_ERR_HIP;
 }
 
 bl_status bitlinear_workspace_init(void* workspace, size_t bytes, void* stream) {

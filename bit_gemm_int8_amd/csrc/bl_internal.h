@@ -40,6 +40,29 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
 
 hipError_t launch_fill_zero(uint32_t* p, size_t words, hipStream_t stream);
 
+// Fused decode step: a table of BitLinear products that share a token batch
+// (M <= 4), each quantizing its own activations in the kernel prologue.
+constexpr int kMaxFused = 16;
+struct FusedSeg {
+  const void* x;          // [m][k] activations (fp32 or bf16)
+  const void* packed;     // packed weights (n, k)
+  const float* gamma;
+  void* y;                // [m][n]
+  int32_t* acc_out;       // nullable
+  int8_t* xq_out;         // nullable, [m][padded_k(k)]
+  float* scale_out;       // nullable, [m]
+  int32_t* ws_acc;        // split-K accumulator (splits > 1)
+  uint32_t* counters;     // split-K counters (splits > 1)
+  int n, k, nc, splits, wg_begin, relu2, y_bf16, x_bf16;
+};
+struct FusedArgs {
+  FusedSeg seg[kMaxFused];
+  int nseg;
+  float eps;
+};
+hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, int groups, size_t lds,
+                             hipStream_t stream);
+
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t padded_n(int64_t n) { return 64 * cdiv(n, 64); }
 inline int64_t padded_k(int64_t k) { return 256 * cdiv(k, 256); }

@@ -163,6 +163,43 @@ bl_status bitlinear_forward(const int8_t* xq, const float* scale, const void* pa
                             int epilogue, int y_dtype, void* y, int32_t* acc_out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * bitlinear_forward_fused -- the decode step of several BitLinear layers that
+ * read the same token batch size, in one launch: for each entry, per-token
+ * absmax int8 quantization of its activations ("8-Bit Activation
+ * Quantization: absmax Scaling") and y = (x~ W~^T) * gamma / s ("Matrix
+ * Multiplication as Pure Integer Addition"), with the same numbers as
+ * bitlinear_quant_act followed by bitlinear_forward.
+ *
+ *   ops        host array of nops (1..BL_MAX_FUSED) entries; entries may
+ *              share x (e.g. the q, k and v projections).
+ *   m          tokens, 0..BL_FUSED_MAX_M (0 is a no-op).
+ *   eps        as in bitlinear_quant_act.
+ *   workspace  bitlinear_forward_fused_workspace_bytes(ops, nops, m) bytes,
+ *              with the contract of bitlinear_forward's workspace.
+ * Every workgroup recomputes its entry's per-token absmax from the whole row
+ * of x (all workgroups get the same s and x~), so the activations are read
+ * from cache once per workgroup; meant for decode-sized batches.
+ * ---------------------------------------------------------------------- */
+#define BL_MAX_FUSED 16
+#define BL_FUSED_MAX_M 4
+typedef struct {
+  const void* x;        /* [m][k] fp32 or bf16 activations, 4-byte aligned */
+  int x_dtype;          /* BL_F32 or BL_BF16 */
+  const void* packed;   /* packed weights (n, k), 16-byte aligned */
+  const float* gamma;   /* device fp32 */
+  int64_t n, k;
+  int epilogue;         /* BL_EPI_NONE or BL_EPI_RELU2 */
+  int y_dtype;          /* BL_F32 or BL_BF16 */
+  void* y;              /* [m][n] */
+  int32_t* acc_out;     /* nullable: int32 [m][n] accumulator */
+  int8_t* xq_out;       /* nullable: int8 [m][padded_k(k)], 16-byte aligned */
+  float* scale_out;     /* nullable: fp32 [m] */
+} bl_linear;
+size_t bitlinear_forward_fused_workspace_bytes(const bl_linear* ops, int nops, int64_t m);
+bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, float eps,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Zero-fill a forward workspace with a device kernel (no hipMemset, so it can
  * be captured in a HIP graph).  bytes must be a multiple of 4. */
 bl_status bitlinear_workspace_init(void* workspace, size_t bytes, void* stream);
