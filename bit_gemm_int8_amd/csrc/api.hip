@@ -30,6 +30,7 @@ constexpr int64_t kGemvMaxM = 4;
 constexpr int64_t kGemvTargetGroups = 512;
 constexpr int64_t kGemvMaxLds = 48 * 1024;
 constexpr int64_t kGemmTargetGroups = 512;
+constexpr int64_t kGemmFullTiles = 192;   // 3/4 of the 256 CUs
 
 inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
@@ -68,15 +69,33 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     p.tiles = (int)nb;
     p.partial_ints = s > 1 ? (size_t)(nb * m * 64) : 0;
   } else {
+    // MFMA GEMM.  Small batches (M <= 64) take the 16-row-multiple tiles;
+    // larger ones the 128 x 256 DMA-fed tile when it yields enough tiles to
+    // cover the CUs, else 64 x 256 or 64 x 128.  Split-K (atomic reduction
+    // of whole tiles) only when even those leave most CUs idle.
     p.kind = 1;
-    p.variant = m <= 16 ? 0 : m <= 32 ? 1 : m <= 64 ? 2 : 3;
+    auto tiles_of = [&](int variant) {
+      int bm, bn;
+      gemm_tile_shape(variant, &bm, &bn);
+      return cdiv(m, bm) * cdiv(nb * 64, bn);
+    };
+    if (m <= 16) p.variant = 0;
+    else if (m <= 32) p.variant = 1;
+    else if (m <= 64) p.variant = 2;
+    else if (tiles_of(4) >= kGemmFullTiles) p.variant = 4;
+    else if (tiles_of(2) >= kGemmFullTiles) p.variant = 2;
+    else p.variant = 3;
     int bm, bn;
     gemm_tile_shape(p.variant, &bm, &bn);
-    const int64_t tiles = cdiv(m, bm) * cdiv(nb * 64, bn);
-    int64_t s = cdiv(kGemmTargetGroups, tiles);
-    int64_t smax = nc / 2 > 1 ? nc / 2 : 1;
-    if (s > smax) s = smax;
-    if (s < 1) s = 1;
+    const int64_t tiles = tiles_of(p.variant);
+    int64_t s = 1;
+    if (m <= 64 || tiles < kGemmFullTiles / 4) {
+      s = cdiv(kGemmTargetGroups, tiles);
+      int64_t smax = nc / 2 > 1 ? nc / 2 : 1;
+      if (s > smax) s = smax;
+      if (m > 64 && s > 4) s = 4;
+      if (s < 1) s = 1;
+    }
     p.splits = (int)s;
     p.tiles = (int)tiles;
     p.partial_ints = s > 1 ? (size_t)(tiles * bm * bn) : 0;

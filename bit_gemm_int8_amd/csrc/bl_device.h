@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 typedef int32_t bl_v4i __attribute__((ext_vector_type(4)));
+typedef int32_t bl_v16i __attribute__((ext_vector_type(16)));
 
 namespace bl {
 

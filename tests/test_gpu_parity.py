@@ -169,6 +169,9 @@ FWD_CASES = [
     (65, 129, 300, False, "f32", "f32"),
     (130, 320, 1024, True, "bf16", "bf16"),
     (256, 384, 768, False, "f32", "bf16"),
+    (1000, 6100, 300, True, "bf16", "bf16"),     # 128 x 256 DMA tiles, ragged M, N, K
+    (1024, 6144, 512, False, "f32", "bf16"),
+    (256, 8192, 768, False, "bf16", "f32"),      # 64 x 128 tiles
 ]
 
 
