@@ -345,6 +345,118 @@ def run_cpu_baseline(budget_s=12.0):
                       f"dequant; codes prepared untimed), {el:.1f} s"}
 
 
+# ---------------------------------------------------------- profiling aids --
+KERNEL_SOURCES = ["bit_gemm_int8_amd/csrc/gemv.hip", "bit_gemm_int8_amd/csrc/bl_device.h"]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_fused_decode_2b_traffic.md")
+COPY_BYTES = 256 << 20
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the fused decode kernel from the committed
+    counter summary, or None when the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    vals = dict(l.split(":", 1) for l in text.splitlines() if l.startswith("- ") and ":" in l)
+    vals = {k[2:].strip(): v.strip() for k, v in vals.items()}
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def pmc_driver(B, torch, args):
+    """Launches to read counters from: a plain copy of COPY_BYTES (the
+    calibration), then eager fused decode steps over rotating weight copies."""
+    import datagen
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    wl = datagen.WORKLOADS["c2"]
+    set_bytes = sum(B.packed_bytes(n, k) for (n, k, _, _) in wl.matrices.values())
+    copies = max(2, math.ceil(2 * CACHE_BYTES / set_bytes))
+    ds = DecodeSet(B, torch, wl, 1, copies)
+    fused = ds.fused_steps()
+    for i in range(args.steps):
+        fused[i % copies]()
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_driver": "done", "steps": args.steps, "copies": copies,
+                      "step_bytes": int(ds.bytes_step_fused())}))
+
+
+def _kname(s):
+    return s.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+
+
+def summarize(directory, command):
+    """Write profiles/ summaries from rocprofv3 CSV output in `directory`."""
+    import csv
+    import glob
+    import statistics
+    out = []
+    stats = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
+    for f in stats:
+        rows = list(csv.DictReader(open(f)))
+        lines = ["# Kernel time summary (rocprofv3 --kernel-trace --stats)", "",
+                 f"Command: `{command}`", "",
+                 "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+        for r in rows:
+            lines.append(f"| {_kname(r['Name'])} | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
+                         f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | {float(r['Percentage']):.2f} |")
+        out.append(("gemv_fused_decode_2b_kernel_stats.md", "\n".join(lines) + "\n"))
+    pmc = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if pmc:
+        vals = {}
+        for f in pmc:
+            for r in csv.DictReader(open(f)):
+                vals.setdefault((_kname(r["Kernel_Name"]), r["Counter_Name"]), []).append(
+                    float(r["Counter_Value"]))
+        def med(kern_sub, ctr):
+            v = [x for (k, c), xs in vals.items() if kern_sub in k and c == ctr for x in xs]
+            return statistics.median(v) if v else None
+
+        def largest(kern_sub, ctr):
+            # the calibration copy is the largest copy the driver makes
+            v = [x for (k, c), xs in vals.items() if kern_sub in k and c == ctr for x in xs]
+            return max(v) if v else None
+        copy_f, copy_w = largest("copy", "FETCH_SIZE"), largest("copy", "WRITE_SIZE")
+        gv_f, gv_w = med("gemv_fused_kernel", "FETCH_SIZE"), med("gemv_fused_kernel", "WRITE_SIZE")
+        kib = COPY_BYTES / 1024
+        ff = kib / copy_f if copy_f else None
+        fw = kib / copy_w if copy_w else None
+        traffic = int(round((gv_f * ff + gv_w * fw) * 1024)) if None not in (gv_f, gv_w, ff, fw) else None
+        lines = ["# HBM traffic of the fused decode kernel (rocprofv3 --pmc)", "",
+                 f"Commands: `{command}` (one run with FETCH_SIZE, one with WRITE_SIZE)", "",
+                 "Median per dispatch, KiB as the counters report them; the copy kernel moves "
+                 f"{COPY_BYTES >> 20} MiB each way and sets the scale factors.", "",
+                 f"- copy_fetch_kib: {copy_f}", f"- copy_write_kib: {copy_w}",
+                 f"- fetch_scale: {ff}", f"- write_scale: {fw}",
+                 f"- kernel_fetch_kib: {gv_f}", f"- kernel_write_kib: {gv_w}",
+                 f"- traffic_bytes_per_launch: {traffic}",
+                 f"- kernel_source_sha256_16: {kernel_source_hash()}", ""]
+        out.append(("gemv_fused_decode_2b_traffic.md", "\n".join(lines)))
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for name, text in out:
+        with open(os.path.join(ROOT, "profiles", name), "w") as f:
+            f.write(text)
+        print(f"wrote profiles/{name}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -352,7 +464,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip prefill and 100B-class legs")
+    ap.add_argument("--pmc-driver", action="store_true",
+                    help="only launch what the HBM-traffic counters are read from")
+    ap.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSVs")
+    ap.add_argument("--command", default="", help="command line recorded in the summaries")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU split is described in DESIGN.md, not built).", file=sys.stderr)
@@ -362,8 +481,12 @@ def main():
     import bit_gemm_int8_amd as B
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.pmc_driver:
+        pmc_driver(B, torch, args)
+        return
     t0 = time.time()
     ds, value, ms, step_bytes, roof, copies = run_decode(B, torch, args)
+    roof["traffic"] = recorded_traffic()
     log(f"decode: {ms*1e3:.2f} us/step, {value:.1f} GB/s; gemv {roof['achieved']} GB/s")
     prefill = None if args.no_extra else run_prefill(B, torch, args)
     if prefill:
