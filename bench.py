@@ -239,7 +239,7 @@ def run_decode(B, torch, args):
                           "GBs": round(gemv_bytes(1, d["n"], d["k"]) / (t * 1e-3) / 1e9, 1)}
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "gemv_fused_kernel<1,8,2> (act quant + batch-1 GEMV + dequant, 6 matrices)",
+            "kernel": "gemv_fused_kernel (act quant + batch-1 GEMV + dequant, 6 matrices, one launch)",
             "bytes_per_launch": int(step_bytes), "us_per_launch": round(ms_k * 1e3, 3),
             "unfused_step_us": round(ms_unf * 1e3, 3), "plain_gemv_per_matrix": per_matrix}
     return ds, value, ms, step_bytes, roof, copies

@@ -8,14 +8,14 @@
 
 namespace bl {
 
-hipError_t launch_gemv(int m, int waves, const int8_t* xq, const float* scale,
+hipError_t launch_gemv(int m, int waves, int pf, const int8_t* xq, const float* scale,
                        const uint32_t* packed, const float* gamma, int64_t n, int64_t k,
                        int splits, bool relu2, bool bf16, void* y, int32_t* acc_out,
-                       int32_t* ws_acc, uint32_t* counters, hipStream_t stream);
+                       int64_t* ws_slots, hipStream_t stream);
 hipError_t launch_gemm(int variant, const int8_t* xq, const float* scale, const uint32_t* packed,
                        const float* gamma, int64_t m, int64_t n, int64_t k, int splits,
-                       bool relu2, bool bf16, void* y, int32_t* acc_out, int32_t* partial,
-                       uint32_t* counters, hipStream_t stream);
+                       bool relu2, bool bf16, void* y, int32_t* acc_out, int64_t* ws_slots,
+                       hipStream_t stream);
 void gemm_tile_shape(int variant, int* bm, int* bn);
 
 namespace {
@@ -31,8 +31,6 @@ constexpr int64_t kGemvTargetGroups = 512;
 constexpr int64_t kGemvMaxLds = 48 * 1024;
 constexpr int64_t kGemmTargetGroups = 512;
 constexpr int64_t kGemmFullTiles = 192;   // 3/4 of the 256 CUs
-
-inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
 }  // namespace
 
@@ -50,24 +48,26 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
   const int64_t nc = cdiv(k, kSuperK);
   if (m <= 0) return p;
   if (m <= kGemvMaxM) {
-    // Waves per workgroup and workgroups per 64-row block.  Many row blocks:
-    // 4 waves each stream a quarter of K.  Few row blocks: 8 waves, and the
-    // block is split over up to 4 workgroups (atomic reduction) while every
-    // wave keeps >= 1 super-chunk.  Then each group's x~ slice must fit LDS.
+    // Split-K factor: many row blocks keep one workgroup each; few are split
+    // over up to 4 workgroups (one atomic combine per output), each keeping
+    // >= 2 super-chunks, and each group's x~ slice must fit LDS.  Waves per
+    // workgroup: 8 when a group has >= 6 super-chunks, else 4; two
+    // super-chunks in flight per wave once a wave streams >= 4.  (Tuned on
+    // MI355X over the 2B- and 100B-class decode shapes.)
     p.kind = 0;
-    int waves = nb >= 256 ? 4 : 8;
     int64_t s = 1;
     if (nb < 256) {
       s = cdiv(kGemvTargetGroups, nb);
-      const int64_t smax = nc / waves > 1 ? nc / waves : 1;
-      if (s > smax) s = smax;
       if (s > 4) s = 4;
+      const int64_t smax = nc / 2 > 1 ? nc / 2 : 1;
+      if (s > smax) s = smax;
     }
     while (m * cdiv(nc, s) * 256 > kGemvMaxLds) ++s;
-    p.variant = waves;
+    const int64_t per_group = nc / s;
+    p.variant = per_group >= 6 ? 8 : 4;
+    p.pf = per_group / p.variant >= 4 ? 2 : 1;
     p.splits = (int)s;
-    p.tiles = (int)nb;
-    p.partial_ints = s > 1 ? (size_t)(nb * m * 64) : 0;
+    p.slots = s > 1 ? (size_t)(nb * m * 64) : 0;
   } else {
     // MFMA GEMM.  Small batches (M <= 64) take the 16-row-multiple tiles;
     // larger ones the 128 x 256 DMA-fed tile when it yields enough tiles to
@@ -97,10 +97,9 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
       if (s < 1) s = 1;
     }
     p.splits = (int)s;
-    p.tiles = (int)tiles;
-    p.partial_ints = s > 1 ? (size_t)(tiles * bm * bn) : 0;
+    p.slots = s > 1 ? (size_t)(tiles * bm * bn) : 0;
   }
-  p.ws_bytes = p.splits > 1 ? round_up((size_t)p.tiles * 4, 256) + p.partial_ints * 4 : 0;
+  p.ws_bytes = p.slots * 8;
   return p;
 }
 
@@ -108,18 +107,12 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
                           const uint32_t* packed, const float* gamma, int64_t m, int64_t n,
                           int64_t k, bool relu2, bool bf16, void* y, int32_t* acc_out,
                           void* workspace, hipStream_t stream) {
-  uint32_t* counters = nullptr;
-  int32_t* partial = nullptr;
-  if (plan.splits > 1) {
-    counters = reinterpret_cast<uint32_t*>(workspace);
-    partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) +
-                                         round_up((size_t)plan.tiles * 4, 256));
-  }
+  int64_t* slots = plan.splits > 1 ? reinterpret_cast<int64_t*>(workspace) : nullptr;
   if (plan.kind == 0)
-    return launch_gemv((int)m, plan.variant, xq, scale, packed, gamma, n, k, plan.splits, relu2,
-                       bf16, y, acc_out, partial, counters, stream);
+    return launch_gemv((int)m, plan.variant, plan.pf, xq, scale, packed, gamma, n, k, plan.splits,
+                       relu2, bf16, y, acc_out, slots, stream);
   return launch_gemm(plan.variant, xq, scale, packed, gamma, m, n, k, plan.splits, relu2, bf16,
-                     y, acc_out, partial, counters, stream);
+                     y, acc_out, slots, stream);
 }
 
 struct FusedPlan {
@@ -128,42 +121,37 @@ struct FusedPlan {
   size_t lds = 0;
   size_t ws_bytes = 0;
   int splits[kMaxFused] = {};
-  size_t counter_off[kMaxFused] = {};   // bytes
-  size_t acc_off[kMaxFused] = {};       // bytes
+  size_t slot_off[kMaxFused] = {};      // bytes
 };
 
 FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
+  // T = super-chunks a workgroup should stream: the set's total over ~512
+  // groups, kept within [8, 32].  Entries with up to 2T super-chunks keep
+  // one group per row block; longer ones are split (atomic combine) into
+  // ~T-chunk ranges.  4 waves per group for decode-sized sets (T < 16), 8
+  // for large ones.  (Tuned on MI355X over the 2B- and 100B-class shapes.)
   FusedPlan p;
-  int64_t total_nb = 0;
-  for (int i = 0; i < nops; ++i) total_nb += cdiv(ops[i].n, kRowBlock);
-  p.waves = total_nb >= 256 ? 4 : 8;
-  size_t counters = 0, accs = 0;
+  int64_t units = 0;
+  for (int i = 0; i < nops; ++i) units += cdiv(ops[i].n, kRowBlock) * cdiv(ops[i].k, kSuperK);
+  int64_t t = cdiv(units, 512);
+  t = t < 8 ? 8 : t > 32 ? 32 : t;
+  p.waves = t >= 16 ? 8 : 4;
+  size_t slots = 0;
   for (int i = 0; i < nops; ++i) {
     const int64_t nb = cdiv(ops[i].n, kRowBlock), nc = cdiv(ops[i].k, kSuperK);
-    int64_t s = 1;
-    if (total_nb < 256) {
-      s = cdiv(kGemvTargetGroups, total_nb);
-      const int64_t smax = nc / p.waves > 1 ? nc / p.waves : 1;
-      if (s > smax) s = smax;
-      if (s > 4) s = 4;
-    }
+    int64_t s = nc <= 2 * t ? 1 : cdiv(nc, t);
+    if (s > 8) s = 8;
     while (m * cdiv(nc, s) * 256 > kGemvMaxLds) ++s;
     p.splits[i] = (int)s;
     p.groups += (int)(nb * s);
     const size_t lds = (size_t)(m * cdiv(nc, s) * 256);
     if (lds > p.lds) p.lds = lds;
     if (s > 1) {
-      p.counter_off[i] = counters * 4;
-      counters += (size_t)nb;
-      p.acc_off[i] = accs * 4;
-      accs += (size_t)(nb * m * 64);
+      p.slot_off[i] = slots * 8;
+      slots += (size_t)(nb * m * 64);
     }
   }
-  if (counters > 0) {
-    const size_t base = round_up(counters * 4, 256);
-    for (int i = 0; i < nops; ++i) p.acc_off[i] += base;
-    p.ws_bytes = base + accs * 4;
-  }
+  p.ws_bytes = slots * 8;
   return p;
 }
 
@@ -277,14 +265,15 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
     sg.relu2 = o.epilogue == BL_EPI_RELU2;
     sg.y_bf16 = o.y_dtype == BL_BF16;
     sg.x_bf16 = o.x_dtype == BL_BF16;
-    if (sg.splits > 1) {
-      sg.counters = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(workspace) +
-                                                plan.counter_off[i]);
-      sg.ws_acc = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + plan.acc_off[i]);
-    }
+    if (sg.splits > 1)
+      sg.slots = reinterpret_cast<int64_t*>(reinterpret_cast<char*>(workspace) + plan.slot_off[i]);
     begin += (int)(cdiv(o.n, kRowBlock) * sg.splits);
   }
-  const hipError_t e = launch_gemv_fused(args, (int)m, plan.waves, plan.groups, plan.lds,
+  bool long_rows = false;                            // a row of more than 1024 16-byte units
+  for (int i = 0; i < nops; ++i)
+    if (ops[i].k * (ops[i].x_dtype == BL_BF16 ? 2 : 4) > 1024 * 16) long_rows = true;
+  const hipError_t e = launch_gemv_fused(args, (int)m, plan.waves, long_rows && m == 1,
+                                         plan.groups, plan.lds,
                                          reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? BL_OK : BL_ERR_HIP;
 }

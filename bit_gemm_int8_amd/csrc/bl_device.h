@@ -71,6 +71,39 @@ __device__ __forceinline__ float gamma_over_s(float gamma, float s) {
   return (float)((double)gamma / (double)s);
 }
 
+// Split-K combine in one device-scope round trip.  Every contribution to an
+// output adds 2^40 + its partial sum to the output's 64-bit workspace slot;
+// the atomic returns the previous value, so the contribution that raises the
+// count (bits 40 and up) to `splits` already holds the total, and it clears
+// the slot for the next call.  The partial sums of any subset of
+// contributions stay below 2^31 in magnitude (64 * 127 * K < 2^31), so the
+// count never mixes with the sum.
+constexpr int64_t kSplitCount = int64_t(1) << 40;
+
+// Add one contribution; returns the slot's previous value.
+__device__ __forceinline__ int64_t split_add(int64_t* slot, int partial) {
+  return __hip_atomic_fetch_add(slot, kSplitCount + (int64_t)partial, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// From split_add's return value: true for the contribution that completes
+// the slot (which it then clears), with the total in `total`.
+__device__ __forceinline__ bool split_done(int64_t* slot, int64_t old, int partial, int splits,
+                                           int& total) {
+  const int64_t count = (old + (kSplitCount >> 1)) >> 40;
+  if (count != (int64_t)(splits - 1)) return false;
+  total = (int)(old - count * kSplitCount + (int64_t)partial);
+  __hip_atomic_store(slot, int64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// The total for the completing contribution, else 1 (never a total: every
+// accumulator here is a multiple of 64).
+__device__ __forceinline__ int split_finish(int64_t* slot, int64_t old, int partial, int splits) {
+  int total = 1;
+  return split_done(slot, old, partial, splits, total) ? total : 1;
+}
+
 // y = acc * f, then ReLU^2 if asked; stored as fp32 or bf16.
 __device__ __forceinline__ void store_out(void* y, int64_t idx, int acc, float f,
                                           bool relu2, bool bf16) {

@@ -26,10 +26,10 @@ hipError_t launch_pack(const void* w, bool bf16, int64_t n, int64_t k, float eps
 // Forward: dispatch plan shared by the workspace query and the launch.
 struct FwdPlan {
   int kind;            // 0 = dot4 GEMV, 1 = MFMA GEMM
-  int variant;         // tile variant
+  int variant;         // GEMV: waves per workgroup; GEMM: tile variant
+  int pf;              // GEMV: super-chunks in flight per wave
   int splits;          // split-K factor
-  int tiles;           // output tiles that own a counter
-  size_t partial_ints; // int32 partial elements in the workspace
+  size_t slots;        // 64-bit split-K slots in the workspace (splits > 1)
   size_t ws_bytes;     // total workspace bytes
 };
 FwdPlan forward_plan(int64_t m, int64_t n, int64_t k);
@@ -51,8 +51,7 @@ struct FusedSeg {
   int32_t* acc_out;       // nullable
   int8_t* xq_out;         // nullable, [m][padded_k(k)]
   float* scale_out;       // nullable, [m]
-  int32_t* ws_acc;        // split-K accumulator (splits > 1)
-  uint32_t* counters;     // split-K counters (splits > 1)
+  int64_t* slots;         // split-K slots, [row block][m][64] (splits > 1)
   int n, k, nc, splits, wg_begin, relu2, y_bf16, x_bf16;
 };
 struct FusedArgs {
@@ -60,8 +59,8 @@ struct FusedArgs {
   int nseg;
   float eps;
 };
-hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, int groups, size_t lds,
-                             hipStream_t stream);
+hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, bool long_rows, int groups,
+                             size_t lds, hipStream_t stream);
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t padded_n(int64_t n) { return 64 * cdiv(n, 64); }

@@ -21,8 +21,9 @@
 // The 16x16 int32 result holds row 4 g + i, column r in element i of lane l.
 //
 // Two LDS stages: global loads of super-chunk c+1 are issued before the
-// MFMAs of c and stored to the other stage afterwards (one barrier each).  Split-K over super-chunks adds tiles into the
-// workspace with device-scope atomics, as in the GEMV.
+// MFMAs of c and stored to the other stage afterwards (one barrier each).
+// Split-K over super-chunks combines each element through a 64-bit
+// workspace slot with one device-scope atomic, as in the GEMV.
 #include "bl_device.h"
 #include "bl_internal.h"
 
@@ -44,13 +45,12 @@ struct Tile {
   static_assert(BM * 16 % NT == 0 && BNB * kBlockU4 % NT == 0, "staging split");
 };
 
-template <int FM, int FN, int WM, int WN>
+template <int FM, int FN, int WM, int WN, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ scale,
     const uint4* __restrict__ packed, const float* __restrict__ gamma, int m, int n,
     int nb, int nc, int64_t kpad, int splits, int tiles_n, int relu2, int bf16,
-    void* __restrict__ y, int32_t* __restrict__ acc_out, int32_t* __restrict__ ws_acc,
-    uint32_t* __restrict__ counters) {
+    void* __restrict__ y, int32_t* __restrict__ acc_out, int64_t* __restrict__ ws_slots) {
   using T = Tile<FM, FN, WM, WN>;
   constexpr int BM = T::BM, BN = T::BN, NT = T::NT, UA = T::UA, UB = T::UB;
   // two LDS stages of A and B, then the per-row rescale factors
@@ -161,45 +161,33 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     __syncthreads();
   }
 
-  if (splits > 1) {
-    // Split-K: add this group's tile into the workspace accumulator with
-    // device-scope atomics (each returns, so it has been performed before
-    // the tile's counter is bumped); the group that completes the count reads
-    // the totals and leaves the accumulator and the counter at zero.
-    constexpr int NE = FM * FN * 4;
-    int32_t* slot = ws_acc + (int64_t)tile * (BM * BN) + tid;
-    int done = 0;
+  if constexpr (SPLIT) {
+    // Split-K: each element goes through its 64-bit workspace slot
+    // (split_add, split_finish), a batch of fragment rows at a time with all
+    // adds of a batch issued before any result is used.  Elements another
+    // group completes are set to 1, which no total equals (totals are
+    // multiples of 64), and skipped below.
+    constexpr int BF = FN * 4 >= 32 ? 1 : 32 / (FN * 4);   // fragment rows per batch
+    int64_t* slot = ws_slots + (int64_t)tile * (BM * BN) + tid;
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int f0 = 0; f0 < FM; f0 += BF) {
+      int64_t old[BF][FN][4];
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
+      for (int fm = f0; fm < f0 + BF && fm < FM; ++fm)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          done |= __hip_atomic_fetch_add(slot + ((fm * FN + fn) * 4 + i) * NT, acc[fm][fn][i],
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("" ::"v"(done));
-    __syncthreads();
-    if (tid == 0) {
-      __builtin_amdgcn_s_waitcnt(0);
-      const uint32_t prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-      flag = prev == (uint32_t)(splits - 1) ? 1u : 0u;
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            old[fm - f0][fn][i] = split_add(slot + ((fm * FN + fn) * 4 + i) * NT, acc[fm][fn][i]);
+#pragma unroll
+      for (int fm = f0; fm < f0 + BF && fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[fm][fn][i] = split_finish(slot + ((fm * FN + fn) * 4 + i) * NT,
+                                          old[fm - f0][fn][i], acc[fm][fn][i], splits);
     }
-    __syncthreads();
-    if (flag == 0u) return;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          int32_t* p = slot + ((fm * FN + fn) * 4 + i) * NT;
-          acc[fm][fn][i] = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    if (tid == 0)
-      __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    (void)NE;
   }
 
   const float gam = *gamma;
@@ -219,7 +207,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int gn = b0 * 64 + wn * 16 * FN + 16 * fn + r;
-        if (gn >= n) continue;
+        if (gn >= n || (acc[fm][fn][i] & 63) != 0) continue;
         const int a = acc[fm][fn][i] >> 6;
         const int64_t idx = (int64_t)gm * n + gn;
         if (acc_out != nullptr) acc_out[idx] = a;
@@ -232,12 +220,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 template <int FM, int FN, int WM, int WN>
 hipError_t run(const int8_t* xq, const float* scale, const uint32_t* packed, const float* gamma,
                int64_t m, int64_t n, int64_t k, int splits, bool relu2, bool bf16, void* y,
-               int32_t* acc_out, int32_t* partial, uint32_t* counters, hipStream_t stream) {
+               int32_t* acc_out, int64_t* slots, hipStream_t stream) {
   using T = Tile<FM, FN, WM, WN>;
   static bool lds_ready = false;          // allow more than 64 KiB of dynamic LDS once
   if (!lds_ready) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<FM, FN, WM, WN>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_kernel<FM, FN, WM, WN, false>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<FM, FN, WM, WN, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
     if (e != hipSuccess) return e;
     lds_ready = true;
   }
@@ -246,9 +238,10 @@ hipError_t run(const int8_t* xq, const float* scale, const uint32_t* packed, con
   const int tiles_m = (int)cdiv(m, T::BM);
   const int tiles_n = (int)cdiv(padded_n(n), T::BN);
   const int64_t grid = (int64_t)tiles_m * tiles_n * splits;
-  gemm_kernel<FM, FN, WM, WN><<<(unsigned)grid, T::NT, T::LDS, stream>>>(
+  auto kern = splits > 1 ? gemm_kernel<FM, FN, WM, WN, true> : gemm_kernel<FM, FN, WM, WN, false>;
+  kern<<<(unsigned)grid, T::NT, T::LDS, stream>>>(
       xq, scale, reinterpret_cast<const uint4*>(packed), gamma, (int)m, (int)n, nb, nc,
-      padded_k(k), splits, tiles_n, relu2, bf16, y, acc_out, partial, counters);
+      padded_k(k), splits, tiles_n, relu2, bf16, y, acc_out, slots);
   return hipGetLastError();
 }
 
@@ -302,13 +295,12 @@ struct Tile32 {
   static_assert(BM * 16 % NT == 0 && BNB * kBlockU4 % NT == 0, "copy split");
 };
 
-template <int FM, int FN, int WM, int WN>
+template <int FM, int FN, int WM, int WN, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm32_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ scale,
     const uint4* __restrict__ packed, const float* __restrict__ gamma, int m, int n,
     int nb, int nc, int64_t kpad, int splits, int tiles_n, int relu2, int bf16,
-    void* __restrict__ y, int32_t* __restrict__ acc_out, int32_t* __restrict__ ws_acc,
-    uint32_t* __restrict__ counters) {
+    void* __restrict__ y, int32_t* __restrict__ acc_out, int64_t* __restrict__ ws_slots) {
   using T = Tile32<FM, FN, WM, WN>;
   constexpr int BM = T::BM, BN = T::BN, NT = T::NT, UA = T::UA, UB = T::UB;
   __shared__ __attribute__((aligned(16))) uint8_t A0[T::A_BYTES];
@@ -406,39 +398,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_kernel(
     __syncthreads();
   }
 
-  if (splits > 1) {
-    int32_t* slot = ws_acc + (int64_t)tile * (BM * BN) + tid;
-    int done = 0;
+  if constexpr (SPLIT) {
+    // Split-K through 64-bit workspace slots, as in gemm_kernel, one
+    // fragment row (FN * 16 elements) per batch.
+    int64_t* slot = ws_slots + (int64_t)tile * (BM * BN) + tid;
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int fm = 0; fm < FM; ++fm) {
+      int64_t old[FN][16];
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          done |= __hip_atomic_fetch_add(slot + ((fm * FN + fn) * 16 + e) * NT, acc[fm][fn][e],
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("" ::"v"(done));
-    __syncthreads();
-    if (tid == 0) {
-      __builtin_amdgcn_s_waitcnt(0);
-      const uint32_t prev = __hip_atomic_fetch_add(&counters[tile], 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-      flag = prev == (uint32_t)(splits - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (flag == 0u) return;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+          old[fn][e] = split_add(slot + ((fm * FN + fn) * 16 + e) * NT, acc[fm][fn][e]);
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          int32_t* p = slot + ((fm * FN + fn) * 16 + e) * NT;
-          acc[fm][fn][e] = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    if (tid == 0)
-      __hip_atomic_store(&counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int e = 0; e < 16; ++e)
+          acc[fm][fn][e] = split_finish(slot + ((fm * FN + fn) * 16 + e) * NT, old[fn][e],
+                                        acc[fm][fn][e], splits);
+    }
   }
 
   // rescale factors per tile row (in the now idle first A stage)
@@ -460,7 +438,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_kernel(
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int gn = b0 * 64 + wn * 32 * FN + 32 * fn + c;
-        if (gn >= n) continue;
+        if (gn >= n || (acc[fm][fn][e] & 63) != 0) continue;
         const int a = acc[fm][fn][e] >> 6;
         const int64_t idx = (int64_t)gm * n + gn;
         if (acc_out != nullptr) acc_out[idx] = a;
@@ -473,16 +451,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_kernel(
 template <int FM, int FN, int WM, int WN>
 hipError_t run32(const int8_t* xq, const float* scale, const uint32_t* packed, const float* gamma,
                  int64_t m, int64_t n, int64_t k, int splits, bool relu2, bool bf16, void* y,
-                 int32_t* acc_out, int32_t* partial, uint32_t* counters, hipStream_t stream) {
+                 int32_t* acc_out, int64_t* slots, hipStream_t stream) {
   using T = Tile32<FM, FN, WM, WN>;
   const int nb = (int)cdiv(n, kRowBlock);
   const int nc = (int)cdiv(k, kSuperK);
   const int tiles_m = (int)cdiv(m, T::BM);
   const int tiles_n = (int)cdiv(padded_n(n), T::BN);
   const int64_t grid = (int64_t)tiles_m * tiles_n * splits;
-  gemm32_kernel<FM, FN, WM, WN><<<(unsigned)grid, T::NT, 0, stream>>>(
+  auto kern =
+      splits > 1 ? gemm32_kernel<FM, FN, WM, WN, true> : gemm32_kernel<FM, FN, WM, WN, false>;
+  kern<<<(unsigned)grid, T::NT, 0, stream>>>(
       xq, scale, reinterpret_cast<const uint4*>(packed), gamma, (int)m, (int)n, nb, nc,
-      padded_k(k), splits, tiles_n, relu2, bf16, y, acc_out, partial, counters);
+      padded_k(k), splits, tiles_n, relu2, bf16, y, acc_out, slots);
   return hipGetLastError();
 }
 
@@ -503,14 +483,14 @@ void gemm_tile_shape(int variant, int* bm, int* bn) {
 
 hipError_t launch_gemm(int variant, const int8_t* xq, const float* scale, const uint32_t* packed,
                        const float* gamma, int64_t m, int64_t n, int64_t k, int splits,
-                       bool relu2, bool bf16, void* y, int32_t* acc_out, int32_t* partial,
-                       uint32_t* counters, hipStream_t stream) {
+                       bool relu2, bool bf16, void* y, int32_t* acc_out, int64_t* slots,
+                       hipStream_t stream) {
   switch (variant) {
-    case 0: return run<1, 4, 1, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, partial, counters, stream);
-    case 1: return run<2, 4, 1, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, partial, counters, stream);
-    case 2: return run<4, 4, 1, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, partial, counters, stream);
-    case 3: return run<2, 4, 2, 2>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, partial, counters, stream);
-    default: return run32<2, 2, 2, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, partial, counters, stream);
+    case 0: return run<1, 4, 1, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, slots, stream);
+    case 1: return run<2, 4, 1, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, slots, stream);
+    case 2: return run<4, 4, 1, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, slots, stream);
+    case 3: return run<2, 4, 2, 2>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, slots, stream);
+    default: return run32<2, 2, 2, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, slots, stream);
   }
 }
 

@@ -21,8 +21,8 @@
 //   - a word unpacks to four int8 lanes of 64*W~ with one shift and one mask;
 //     acc = sum >> 6 at the end (every term is a multiple of 64);
 //   - the waves' sums meet in LDS; when the row blocks alone cannot fill the
-//     chip, `splits` workgroups share a row block and add into the workspace
-//     with device-scope atomics (no cache-wide fences).
+//     chip, `splits` workgroups share a row block and combine through one
+//     64-bit device-scope atomic per output (no counters, no fences).
 #include "bl_device.h"
 #include "bl_internal.h"
 
@@ -32,56 +32,79 @@ namespace {
 // One super-chunk: w = the lane's four 16-byte loads q = 0..3 (word (q, j) =
 // w[q].{x,y,z,w}[j], inputs 64j + 16q + 4i + (0..3)), xs = this super-chunk's
 // 256 bytes of x~ for each token in LDS (token stride xs_stride dwords).
+// The q loop runs in two halves with a scheduling barrier between them, so
+// at most 8 x~ loads (32 registers) are held at once.
 template <int M>
 __device__ __forceinline__ void accumulate_chunk(const uint4 (&w)[4], const uint32_t* xs,
                                                  int xs_stride, int (&acc)[M]) {
 #pragma unroll
   for (int m = 0; m < M; ++m) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t wq[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 xv = *reinterpret_cast<const uint4*>(xs + m * xs_stride + 16 * j + 4 * q);
-        acc[m] = dot4(unpack_x64(wq[j], 0), xv.x, acc[m]);
-        acc[m] = dot4(unpack_x64(wq[j], 1), xv.y, acc[m]);
-        acc[m] = dot4(unpack_x64(wq[j], 2), xv.z, acc[m]);
-        acc[m] = dot4(unpack_x64(wq[j], 3), xv.w, acc[m]);
+      for (int q = 2 * h; q < 2 * h + 2; ++q) {
+        const uint32_t wq[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 xv = *reinterpret_cast<const uint4*>(xs + m * xs_stride + 16 * j + 4 * q);
+          acc[m] = dot4(unpack_x64(wq[j], 0), xv.x, acc[m]);
+          acc[m] = dot4(unpack_x64(wq[j], 1), xv.y, acc[m]);
+          acc[m] = dot4(unpack_x64(wq[j], 2), xv.z, acc[m]);
+          acc[m] = dot4(unpack_x64(wq[j], 3), xv.w, acc[m]);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
+// The first PF super-chunks of a wave's range.  Slots past the range load
+// a super-chunk this workgroup reads anyway (the wave's last, or the group's
+// first for a wave with none), never used: with no branches around the
+// loads the compiler can count them and wait for older loads without
+// waiting for these.
 template <int PF>
 __device__ __forceinline__ void prefetch_first(uint4 (&buf)[PF][4], const uint4* blk, int c0,
-                                               int c1) {
+                                               int c1, int g0) {
+  const int last = c1 > c0 ? c1 - 1 : g0;
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
-    if (c0 + p < c1) {
+    const int c = c0 + p < c1 ? c0 + p : last;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) buf[p][q] = blk[(int64_t)(c0 + p) * kBlockU4 + q * 64];
-    }
+    for (int q = 0; q < 4; ++q) buf[p][q] = blk[(int64_t)c * kBlockU4 + q * 64];
   }
 }
 
 // Stream super-chunks c0..c1-1 (the first PF already in buf); x~ in LDS
-// starts at super-chunk g0.
+// starts at super-chunk g0.  The steady-state loop loads without conditions
+// (so the compiler need not keep old buffer values alive); the last fewer
+// than 2*PF chunks drain after it.
 template <int M, int PF>
 __device__ __forceinline__ void stream_chunks(uint4 (&buf)[PF][4], const uint4* blk, int c0,
                                               int c1, int g0, const uint32_t* xs, int xs_stride,
                                               int (&acc)[M]) {
-  for (int c = c0; c < c1; c += PF) {
+  int c = c0;
+  for (; c + 2 * PF <= c1; c += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      if (c + p < c1) {
-        accumulate_chunk<M>(buf[p], xs + (c + p - g0) * 64, xs_stride, acc);
-        if (c + p + PF < c1) {
+      accumulate_chunk<M>(buf[p], xs + (c + p - g0) * 64, xs_stride, acc);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) buf[p][q] = blk[(int64_t)(c + p + PF) * kBlockU4 + q * 64];
-        }
+      for (int q = 0; q < 4; ++q) buf[p][q] = blk[(int64_t)(c + p + PF) * kBlockU4 + q * 64];
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    if (c + p < c1) {
+      accumulate_chunk<M>(buf[p], xs + (c + p - g0) * 64, xs_stride, acc);
+      if (c + p + PF < c1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) buf[p][q] = blk[(int64_t)(c + p + PF) * kBlockU4 + q * 64];
       }
     }
   }
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (c + PF + p < c1) accumulate_chunk<M>(buf[p], xs + (c + PF + p - g0) * 64, xs_stride, acc);
 }
 
 // Sum the waves' accumulators into wave 0.  Returns false in other waves.
@@ -102,44 +125,27 @@ __device__ __forceinline__ bool reduce_waves(int (&acc)[M], int (*red)[M][64], i
   return true;
 }
 
-// Workgroups that share a row block add their sums into the workspace
-// accumulator with device-scope atomics; each add returns, so it has been
-// performed before this group bumps the block's counter.  The group that
-// brings the counter to `splits` reads the totals with device-scope atomic
-// loads and clears them and the counter for the next call.  Wave 0 only;
-// returns true in the group that finishes the block.
+// Workgroups that share a row block combine per (token, row) through a
+// 64-bit workspace slot (split_add, split_done); the lane whose contribution
+// completes a slot writes that output.  Wave 0 only.
 template <int M>
-__device__ __forceinline__ bool combine_splits(int (&acc)[M], int32_t* slot, uint32_t* counter,
-                                               int splits, int lane) {
-  int done = 0;
+__device__ __forceinline__ void combine_splits(int (&acc)[M], bool (&own)[M], int64_t* slot,
+                                               int splits) {
+  int64_t old[M];
 #pragma unroll
-  for (int m = 0; m < M; ++m)
-    done |= __hip_atomic_fetch_add(slot + m * 64, acc[m], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-  asm volatile("" ::"v"(done));                    // the returned values are in
-  uint32_t prev = 0;
-  if (lane == 0) {
-    __builtin_amdgcn_s_waitcnt(0);
-    prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
-  if (prev != (uint32_t)(splits - 1)) return false;
+  for (int m = 0; m < M; ++m) old[m] = split_add(slot + m * 64, acc[m]);
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    acc[m] = __hip_atomic_load(slot + m * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(slot + m * 64, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return true;
+  for (int m = 0; m < M; ++m) own[m] = split_done(slot + m * 64, old[m], acc[m], splits, acc[m]);
 }
 
 template <int M>
-__device__ __forceinline__ void write_rows(const int (&acc)[M], const float (&fac)[M], int64_t row,
-                                           int n, void* y, int32_t* acc_out, bool relu2,
-                                           bool bf16) {
+__device__ __forceinline__ void write_rows(const int (&acc)[M], const bool (&own)[M],
+                                           const float (&fac)[M], int64_t row, int n, void* y,
+                                           int32_t* acc_out, bool relu2, bool bf16) {
   if (row >= n) return;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
+    if (!own[m]) continue;
     const int a = acc[m] >> 6;                       // exact: every term is a multiple of 64
     if (acc_out != nullptr) acc_out[(int64_t)m * n + row] = a;
     store_out(y, (int64_t)m * n + row, a, fac[m], relu2, bf16);
@@ -147,18 +153,21 @@ __device__ __forceinline__ void write_rows(const int (&acc)[M], const float (&fa
 }
 
 // ------------------------------------------------------------ plain GEMV --
+// 16-byte x~ units per thread loaded ahead of the weights: 1024 per group.
+template <int WAVES>
+constexpr int kXR = WAVES >= 16 ? 1 : 16 / WAVES;
+
 template <int M, int WAVES, int PF>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ scale,
     const uint4* __restrict__ packed, const float* __restrict__ gamma, int n, int nc,
     int64_t kpad, int splits, int relu2, int bf16, void* __restrict__ y,
-    int32_t* __restrict__ acc_out, int32_t* __restrict__ ws_acc,
-    uint32_t* __restrict__ counters) {
+    int32_t* __restrict__ acc_out, int64_t* __restrict__ ws_slots) {
   __shared__ int red[WAVES > 1 ? WAVES - 1 : 1][M][64];
   extern __shared__ uint4 xs_lds[];                 // x~ of this group's inputs, per token
   const int b = blockIdx.x / splits;
   const int s = blockIdx.x - b * splits;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar control
   const int lane = threadIdx.x & 63;
   // this workgroup's super-chunks, then this wave's contiguous share
   const int g0 = (int)((int64_t)s * nc / splits);
@@ -167,8 +176,31 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   const int c1 = g0 + (int)((int64_t)(wave + 1) * (g1 - g0) / WAVES);
   const uint4* blk = packed + (int64_t)b * nc * kBlockU4 + lane;
 
+  // x~[m][256*g0 .. 256*g1) for every token (16 units of 16 bytes per
+  // super-chunk and token) goes to LDS.  Its first loads are issued before
+  // the weights: loads retire in issue order, so the staging then waits only
+  // for them, not for the weight stream.
+  constexpr int NT = 64 * WAVES;
+  const int span = (g1 - g0) * 16;                  // uint4 per token
+  auto x_unit = [&](int u) {
+    const int m = u / span, v = u - m * span;
+    return reinterpret_cast<const uint4*>(xq + (int64_t)m * kpad + (int64_t)g0 * 256)[v];
+  };
+  // Slots past the range (span * M units) wrap around and rewrite a unit
+  // with its own value: no branch, so the compiler keeps these loads ahead of
+  // the weights, and no two lanes of a wave hit one LDS address.
+  constexpr int XR = kXR<WAVES>;
+  const int units = span * M;
+  uint4 xr[XR];
+  int xu[XR];
+#pragma unroll
+  for (int r = 0; r < XR; ++r) {
+    xu[r] = ((int)threadIdx.x + NT * r) % units;
+    xr[r] = x_unit(xu[r]);
+  }
+
   uint4 buf[PF][4];
-  prefetch_first<PF>(buf, blk, c0, c1);
+  prefetch_first<PF>(buf, blk, c0, c1, g0);
   // epilogue operands, loaded now so their latency hides under the stream
   const float g = *gamma;
   float fac[M];
@@ -178,37 +210,33 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0;
 
-  // stage x~[m][256*g0 .. 256*g1) for every token (16 units of 16 bytes per
-  // super-chunk and token)
-  const int span = (g1 - g0) * 16;                  // uint4 per token
-  for (int u = threadIdx.x; u < span * M; u += 64 * WAVES) {
-    const int m = u / span, v = u - m * span;
-    xs_lds[u] = reinterpret_cast<const uint4*>(xq + (int64_t)m * kpad + (int64_t)g0 * 256)[v];
-  }
+#pragma unroll
+  for (int r = 0; r < XR; ++r) xs_lds[xu[r]] = xr[r];
+  for (int u = threadIdx.x + NT * XR; u < units; u += NT) xs_lds[u] = x_unit(u);
   __syncthreads();
   stream_chunks<M, PF>(buf, blk, c0, c1, g0, reinterpret_cast<const uint32_t*>(xs_lds), span * 4,
                        acc);
   if (!reduce_waves<M, WAVES>(acc, red, wave, lane)) return;
-  if (splits > 1 &&
-      !combine_splits<M>(acc, ws_acc + (int64_t)b * (M * 64) + lane, &counters[b], splits, lane))
-    return;
+  bool own[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) own[m] = true;
+  if (splits > 1) combine_splits<M>(acc, own, ws_slots + (int64_t)b * (M * 64) + lane, splits);
 #pragma unroll
   for (int m = 0; m < M; ++m) fac[m] = gamma_over_s(g, fac[m]);
-  write_rows<M>(acc, fac, (int64_t)b * 64 + lane, n, y, acc_out, relu2 != 0, bf16 != 0);
+  write_rows<M>(acc, own, fac, (int64_t)b * 64 + lane, n, y, acc_out, relu2 != 0, bf16 != 0);
 }
 
 template <int M, int WAVES, int PF>
 hipError_t run_gemv(const int8_t* xq, const float* scale, const uint32_t* packed,
                     const float* gamma, int64_t n, int64_t k, int splits, bool relu2, bool bf16,
-                    void* y, int32_t* acc_out, int32_t* ws_acc, uint32_t* counters,
-                    hipStream_t stream) {
+                    void* y, int32_t* acc_out, int64_t* ws_slots, hipStream_t stream) {
   const int nb = (int)cdiv(n, kRowBlock);
   const int nc = (int)cdiv(k, kSuperK);
   dim3 grid((unsigned)((int64_t)nb * splits)), block(64 * WAVES);
   const size_t lds = (size_t)M * cdiv(nc, splits) * 256;
   gemv_kernel<M, WAVES, PF><<<grid, block, lds, stream>>>(
       xq, scale, reinterpret_cast<const uint4*>(packed), gamma, (int)n, nc, padded_k(k), splits,
-      relu2, bf16, y, acc_out, ws_acc, counters);
+      relu2, bf16, y, acc_out, ws_slots);
   return hipGetLastError();
 }
 
@@ -217,105 +245,192 @@ hipError_t run_gemv(const int8_t* xq, const float* scale, const uint32_t* packed
 // token's absmax over all K with DPP wave reductions and LDS, s = 127/max(beta,
 // eps), and writes x~ = clamp(rint(x*s)) for its own super-chunks straight
 // into LDS: every group of a segment computes the same s and x~ bit for bit.
+//
+// Order matters: vector-memory loads retire in issue order, so a load issued
+// after the weight stream cannot be waited for without waiting for the
+// weights.  The activation loads therefore go out first (x_load_first, raw
+// 16-byte units into registers, nothing computed on them yet), then the
+// weights; the absmax and the quantization run while the weights are in
+// flight.  A unit holds epu = 8 (bf16) or 4 (fp32) activations, i.e. epu/4
+// dwords of x~.  Thread t holds units u = (ubase + t + NT*j) mod nu, j < kXV,
+// where ubase is the first unit of this workgroup's super-chunks and nu the
+// units in a row: together they cover the row when NT*kXV >= nu (else a
+// second pass reads the rest), and unit ubase + t + NT*j of this workgroup's
+// range is slot j of thread t, ready for the quantization.
 
-template <int WAVES>
-__device__ __forceinline__ uint32_t group_max_u32(uint32_t v, uint32_t* red) {
-  v = wave_max_u32(v);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  uint32_t r = red[0];
-#pragma unroll
-  for (int w = 1; w < WAVES; ++w) r = r > red[w] ? r : red[w];
-  __syncthreads();
+// Activation units per thread and token issued first: 1024 per group, or
+// 4096 (rows up to 64 KiB) in the long-row instance (one token only).
+template <int NT, bool LONGX>
+constexpr int kXV = (LONGX ? 4096 : 1024) / NT;
+
+struct XRow {
+  int epu;      // activations per 16-byte unit
+  int nu;       // units per row
+  bool fast;    // whole 16-byte units (row bytes % 16 == 0, x 16-byte aligned)
+};
+
+__device__ __forceinline__ XRow x_row_info(const FusedSeg& sg) {
+  XRow r;
+  const int esize = sg.x_bf16 ? 2 : 4;
+  r.epu = 16 / esize;
+  r.nu = (sg.k + r.epu - 1) / r.epu;
+  r.fast = ((int64_t)sg.k * esize % 16 == 0) && ((uintptr_t)sg.x % 16 == 0);
   return r;
 }
 
-__device__ __forceinline__ uint32_t quant1(float v, float s) {
-  float r = rintf(v * s);                            // one fp32 multiply, half to even
+__device__ __forceinline__ const char* x_row(const FusedSeg& sg, int m) {
+  return reinterpret_cast<const char*>(sg.x) + (int64_t)m * sg.k * (sg.x_bf16 ? 2 : 4);
+}
+
+// Unit u of a row as it lies in memory (elements past K read as 0).
+__device__ __forceinline__ uint4 load_unit(const FusedSeg& sg, const XRow& xr, const char* row,
+                                           int u) {
+  if (xr.fast) return reinterpret_cast<const uint4*>(row)[u];
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < xr.epu; ++i) {
+    const int kk = u * xr.epu + i;
+    if (kk >= sg.k) break;
+    if (sg.x_bf16)
+      w[i >> 1] |= ((uint32_t)reinterpret_cast<const uint16_t*>(row)[kk]) << (16 * (i & 1));
+    else
+      w[i] = reinterpret_cast<const uint32_t*>(row)[kk];
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// The epu activations of a unit as fp32 bit patterns.
+__device__ __forceinline__ void expand_unit(bool bf16, const uint4& r, uint32_t (&e)[8]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  if (bf16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      e[2 * i] = w[i] << 16;
+      e[2 * i + 1] = w[i] & 0xFFFF0000u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { e[i] = w[i]; e[4 + i] = 0u; }
+  }
+}
+
+__device__ __forceinline__ uint32_t absmax_unit(bool bf16, const uint4& r) {
+  uint32_t e[8];
+  expand_unit(bf16, r, e);
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mx = max(mx, e[i] & 0x7FFFFFFFu);
+  return mx;
+}
+
+template <int M, int NT, bool LONGX>
+__device__ __forceinline__ void x_load_first(const FusedSeg& sg, int g0,
+                                             uint4 (&raw)[M][kXV<NT, LONGX>]) {
+  constexpr int XV = kXV<NT, LONGX>;
+  const XRow xr = x_row_info(sg);
+  const int ubase = g0 * 256 / xr.epu;
+  int u = (int)(((int64_t)ubase + threadIdx.x) % xr.nu);
+  const int step = NT % xr.nu;
+#pragma unroll
+  for (int j = 0; j < XV; ++j) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) raw[m][j] = load_unit(sg, xr, x_row(sg, m), u);
+    u += step;
+    if (u >= xr.nu) u -= xr.nu;
+  }
+}
+
+__device__ __forceinline__ uint32_t quant1(uint32_t bits, float s) {
+  float r = rintf(__uint_as_float(bits) * s);        // one fp32 multiply, half to even
   r = fminf(fmaxf(r, -128.0f), 127.0f);
   return (uint32_t)(uint8_t)(int8_t)(int)r;
 }
 
-__device__ __forceinline__ uint32_t quant4(const float (&f)[4], float s) {
-  return quant1(f[0], s) | (quant1(f[1], s) << 8) | (quant1(f[2], s) << 16) |
-         (quant1(f[3], s) << 24);
+__device__ __forceinline__ uint32_t quant4(const uint32_t* e, float s) {
+  return quant1(e[0], s) | (quant1(e[1], s) << 8) | (quant1(e[2], s) << 16) |
+         (quant1(e[3], s) << 24);
 }
 
-template <int M, int WAVES>
+// x~ dwords of one unit (relative unit q of this workgroup's range) into LDS.
+__device__ __forceinline__ void store_unit_q(bool bf16, const uint4& r, float s, bool live,
+                                             uint32_t* xs_token, int q) {
+  uint32_t e[8];
+  expand_unit(bf16, r, e);
+  if (bf16) {
+    xs_token[2 * q] = live ? quant4(e, s) : 0u;
+    xs_token[2 * q + 1] = live ? quant4(e + 4, s) : 0u;
+  } else {
+    xs_token[q] = live ? quant4(e, s) : 0u;
+  }
+}
+
+// Per-token scales s[m] and x~ of super-chunks g0..g1-1 into LDS (token
+// stride span_w dwords, zero past K), from the units x_load_first holds.
+template <int M, int WAVES, bool LONGX>
 __device__ __forceinline__ void quantize_into_lds(const FusedSeg& sg, int g0, int g1, float eps,
+                                                  const uint4 (&raw)[M][kXV<64 * WAVES, LONGX>],
                                                   uint32_t* xs_words, float (&sv)[M],
-                                                  uint32_t* red) {
-  const int k = sg.k;
+                                                  uint32_t (*red)[M]) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int XV = kXV<NT, LONGX>;
+  const XRow xr = x_row_info(sg);
   const bool bf16 = sg.x_bf16 != 0;
-  // vector path: 4 consecutive elements per access, aligned
-  const bool vec = (k % 4 == 0) && (((uintptr_t)sg.x % (bf16 ? 8 : 16)) == 0);
-  const int span_w = (g1 - g0) * 64;                // dwords of x~ per token
+  const int ubase = g0 * 256 / xr.epu;
+  uint32_t mx[M];
+#pragma unroll
   for (int m = 0; m < M; ++m) {
-    const char* row = reinterpret_cast<const char*>(sg.x) + (int64_t)m * k * (bf16 ? 2 : 4);
-    uint32_t mx = 0;
-    if (vec) {
-      for (int v = threadIdx.x; v < k / 4; v += 64 * WAVES) {
-        uint32_t e[4];
-        if (bf16) {
-          const uint2 u = reinterpret_cast<const uint2*>(row)[v];
-          e[0] = u.x << 16; e[1] = u.x & 0xFFFF0000u; e[2] = u.y << 16; e[3] = u.y & 0xFFFF0000u;
-        } else {
-          const uint4 u = reinterpret_cast<const uint4*>(row)[v];
-          e[0] = u.x; e[1] = u.y; e[2] = u.z; e[3] = u.w;
-        }
+    mx[m] = 0;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t a = e[t] & 0x7FFFFFFFu;
-          mx = mx > a ? mx : a;
-        }
-      }
-    } else {
-      for (int i = threadIdx.x; i < k; i += 64 * WAVES) {
-        const float f = bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[i])
-                             : reinterpret_cast<const float*>(row)[i];
-        const uint32_t a = __float_as_uint(f) & 0x7FFFFFFFu;
-        mx = mx > a ? mx : a;
-      }
+    for (int j = 0; j < XV; ++j) mx[m] = max(mx[m], absmax_unit(bf16, raw[m][j]));
+  }
+  if (NT * XV < xr.nu) {                            // long rows: the units not held
+    int u = (int)(((int64_t)ubase + threadIdx.x + (int64_t)NT * XV) % xr.nu);
+    for (int i = NT * XV; i < xr.nu; i += NT) {
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        mx[m] = max(mx[m], absmax_unit(bf16, load_unit(sg, xr, x_row(sg, m), u)));
+      u += NT % xr.nu;
+      if (u >= xr.nu) u -= xr.nu;
     }
-    const float beta = __uint_as_float(group_max_u32<WAVES>(mx, red));
-    const float s = (float)(127.0 / (double)fmaxf(beta, eps));
-    sv[m] = s;
-    // x~ for inputs 256*g0 + 4*d .. +3, d < span_w; zero past K
-    for (int d = threadIdx.x; d < span_w; d += 64 * WAVES) {
-      const int k0 = g0 * 256 + 4 * d;
-      float f[4];
-      if (vec) {
-        if (k0 < k) {
-          if (bf16) {
-            const uint2 u = reinterpret_cast<const uint2*>(row)[k0 / 4];
-            f[0] = __uint_as_float(u.x << 16); f[1] = __uint_as_float(u.x & 0xFFFF0000u);
-            f[2] = __uint_as_float(u.y << 16); f[3] = __uint_as_float(u.y & 0xFFFF0000u);
-          } else {
-            const float4 u = reinterpret_cast<const float4*>(row)[k0 / 4];
-            f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
-          }
-        } else {
-          f[0] = f[1] = f[2] = f[3] = 0.0f;
-        }
-      } else {
+  }
+  const int wave = threadIdx.x >> 6;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int kk = k0 + t;
-          f[t] = kk < k ? (bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[kk])
-                                : reinterpret_cast<const float*>(row)[kk])
-                        : 0.0f;
-        }
-      }
-      xs_words[m * span_w + d] = quant4(f, s);
+  for (int m = 0; m < M; ++m) {
+    const uint32_t w = wave_max_u32(mx[m]);
+    if ((threadIdx.x & 63) == 0) red[wave][m] = w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    uint32_t r = red[0][m];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) r = max(r, red[w][m]);
+    sv[m] = (float)(127.0 / (double)fmaxf(__uint_as_float(r), eps));
+  }
+  const int span_w = (g1 - g0) * 64;                 // dwords of x~ per token
+  const int span_u = (g1 - g0) * 256 / xr.epu;       // units per token
+#pragma unroll
+  for (int j = 0; j < XV; ++j) {
+    const int q = threadIdx.x + NT * j;
+    if (q < span_u) {
+      const bool live = ubase + q < xr.nu;
+#pragma unroll
+      for (int m = 0; m < M; ++m) store_unit_q(bf16, raw[m][j], sv[m], live, xs_words + m * span_w, q);
+    }
+  }
+  for (int q = threadIdx.x + NT * XV; q < span_u; q += NT) {   // ranges beyond the held slots
+    const bool live = ubase + q < xr.nu;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint4 r = live ? load_unit(sg, xr, x_row(sg, m), ubase + q) : make_uint4(0, 0, 0, 0);
+      store_unit_q(bf16, r, sv[m], live, xs_words + m * span_w, q);
     }
   }
 }
 
-template <int M, int WAVES, int PF>
+template <int M, int WAVES, int PF, bool LONGX>
 __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) {
   __shared__ int red[WAVES > 1 ? WAVES - 1 : 1][M][64];
-  __shared__ uint32_t red_max[WAVES];
+  __shared__ uint32_t red_max[WAVES][M];
   extern __shared__ uint4 xs_lds[];
   // segment of this workgroup
   int si = 0;
@@ -327,7 +442,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) 
   const int b = local / splits;
   const int s = local - b * splits;
   const int nc = sg.nc;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar control
   const int lane = threadIdx.x & 63;
   const int g0 = (int)((int64_t)s * nc / splits);
   const int g1 = (int)((int64_t)(s + 1) * nc / splits);
@@ -336,8 +451,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) 
   const uint4* blk =
       reinterpret_cast<const uint4*>(sg.packed) + (int64_t)b * nc * kBlockU4 + lane;
 
+  uint4 xraw[M][kXV<64 * WAVES, LONGX>];
+  x_load_first<M, 64 * WAVES, LONGX>(sg, g0, xraw);        // activations first (see above)
   uint4 buf[PF][4];
-  prefetch_first<PF>(buf, blk, c0, c1);
+  prefetch_first<PF>(buf, blk, c0, c1, g0);
   const float g = *sg.gamma;
   int acc[M];
 #pragma unroll
@@ -345,7 +462,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) 
 
   uint32_t* xs_words = reinterpret_cast<uint32_t*>(xs_lds);
   float sv[M];
-  quantize_into_lds<M, WAVES>(sg, g0, g1, args.eps, xs_words, sv, red_max);
+  quantize_into_lds<M, WAVES, LONGX>(sg, g0, g1, args.eps, xraw, xs_words, sv, red_max);
   __syncthreads();
   const int span_w = (g1 - g0) * 64;
   // optional copies of x~ and s (row block 0's groups cover all of K_pad)
@@ -363,34 +480,32 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) 
 
   stream_chunks<M, PF>(buf, blk, c0, c1, g0, xs_words, span_w, acc);
   if (!reduce_waves<M, WAVES>(acc, red, wave, lane)) return;
-  if (splits > 1 &&
-      !combine_splits<M>(acc, sg.ws_acc + (int64_t)b * (M * 64) + lane, &sg.counters[b], splits,
-                         lane))
-    return;
+  bool own[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) own[m] = true;
+  if (splits > 1) combine_splits<M>(acc, own, sg.slots + (int64_t)b * (M * 64) + lane, splits);
   float fac[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) fac[m] = gamma_over_s(g, sv[m]);
-  write_rows<M>(acc, fac, (int64_t)b * 64 + lane, sg.n, sg.y, sg.acc_out, sg.relu2 != 0,
+  write_rows<M>(acc, own, fac, (int64_t)b * 64 + lane, sg.n, sg.y, sg.acc_out, sg.relu2 != 0,
                 sg.y_bf16 != 0);
 }
 
 }  // namespace
 
 // Plain GEMV: x~ and s given.
-hipError_t launch_gemv(int m, int waves, const int8_t* xq, const float* scale,
+hipError_t launch_gemv(int m, int waves, int pf, const int8_t* xq, const float* scale,
                        const uint32_t* packed, const float* gamma, int64_t n, int64_t k,
                        int splits, bool relu2, bool bf16, void* y, int32_t* acc_out,
-                       int32_t* ws_acc, uint32_t* counters, hipStream_t stream) {
-#define BL_GEMV(MM, WW)                                                                        \
-  return run_gemv<MM, WW, (WW >= 16 ? 1 : 2)>(xq, scale, packed, gamma, n, k, splits, relu2, \
-                                              bf16, y, acc_out, ws_acc, counters, stream)
-#define BL_GEMV_W(MM)            \
-  switch (waves) {               \
-    case 1: BL_GEMV(MM, 1);      \
-    case 2: BL_GEMV(MM, 2);      \
-    case 4: BL_GEMV(MM, 4);      \
-    case 8: BL_GEMV(MM, 8);      \
-    default: BL_GEMV(MM, 16);    \
+                       int64_t* ws_slots, hipStream_t stream) {
+#define BL_GEMV(MM, WW, PP)                                                                   \
+  return run_gemv<MM, WW, PP>(xq, scale, packed, gamma, n, k, splits, relu2, bf16, y, acc_out, \
+                              ws_slots, stream)
+#define BL_GEMV_W(MM)                                  \
+  if (waves == 8) {                                    \
+    if (pf == 2) BL_GEMV(MM, 8, 2); else BL_GEMV(MM, 8, 1); \
+  } else {                                             \
+    if (pf == 2) BL_GEMV(MM, 4, 2); else BL_GEMV(MM, 4, 1); \
   }
   switch (m) {
     case 1: BL_GEMV_W(1);
@@ -404,24 +519,29 @@ hipError_t launch_gemv(int m, int waves, const int8_t* xq, const float* scale,
 }
 
 // Fused decode step over a complete segment table (wg_begin, splits and
-// workspace pointers filled in).
-hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, int groups, size_t lds,
-                             hipStream_t stream) {
-#define BL_FUSED(MM, WW)                                                             \
-  do {                                                                               \
-    gemv_fused_kernel<MM, WW, 2><<<(unsigned)groups, 64 * WW, lds, stream>>>(args); \
-    return hipGetLastError();                                                        \
+// workspace pointers filled in).  long_rows: one token and some row longer
+// than 1024 16-byte units.
+hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, bool long_rows, int groups,
+                             size_t lds, hipStream_t stream) {
+#define BL_FUSED(MM, WW, LL)                                                             \
+  do {                                                                                   \
+    gemv_fused_kernel<MM, WW, 2, LL><<<(unsigned)groups, 64 * WW, lds, stream>>>(args); \
+    return hipGetLastError();                                                            \
   } while (0)
-#define BL_FUSED_W(MM)     \
+#define BL_FUSED_W(MM, LL) \
   if (waves == 4)          \
-    BL_FUSED(MM, 4);       \
+    BL_FUSED(MM, 4, LL);   \
   else                     \
-    BL_FUSED(MM, 8)
+    BL_FUSED(MM, 8, LL)
   switch (m) {
-    case 1: BL_FUSED_W(1);
-    case 2: BL_FUSED_W(2);
-    case 3: BL_FUSED_W(3);
-    case 4: BL_FUSED_W(4);
+    case 1:
+      if (long_rows) {
+        BL_FUSED_W(1, true);
+      }
+      BL_FUSED_W(1, false);
+    case 2: BL_FUSED_W(2, false);
+    case 3: BL_FUSED_W(3, false);
+    case 4: BL_FUSED_W(4, false);
     default: return hipErrorInvalidValue;
   }
 #undef BL_FUSED_W

@@ -148,9 +148,9 @@ bl_status bitlinear_quant_act(const void* x, int x_dtype, int64_t m, int64_t k,
  *   workspace  bitlinear_forward_workspace_bytes(m, n, k) bytes, 256-byte
  *              aligned, zero-filled once before its first use (see
  *              bitlinear_workspace_init).  Every completed call leaves it
- *              zero-filled again (split-K counters and accumulators are
- *              cleared by the workgroup that finishes each tile), so one
- *              workspace serves any sequence of calls without clearing.
+ *              zero-filled again (each 64-bit split-K slot is cleared by
+ *              the contribution that completes it), so one workspace
+ *              serves any sequence of calls without clearing.
  *              Calls that share a workspace must be ordered (one stream, or
  *              events); concurrent calls on one workspace race.  May be NULL
  *              when the required size is 0.
