@@ -31,6 +31,7 @@ constexpr int64_t kGemvTargetGroups = 512;
 constexpr int64_t kGemvMaxLds = 48 * 1024;
 constexpr int64_t kGemmTargetGroups = 512;
 constexpr int64_t kGemmFullTiles = 192;   // 3/4 of the 256 CUs
+constexpr int64_t kGemmWideTiles = 150;
 
 }  // namespace
 
@@ -70,9 +71,10 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     p.slots = s > 1 ? (size_t)(nb * m * 64) : 0;
   } else {
     // MFMA GEMM.  Small batches (M <= 64) take the 16-row-multiple tiles;
-    // larger ones the 128 x 256 DMA-fed tile when it yields enough tiles to
-    // cover the CUs, else 64 x 256 or 64 x 128.  Split-K (atomic reduction
-    // of whole tiles) only when even those leave most CUs idle.
+    // larger ones the wide-wave tiles, the largest of 128 x 512, 64 x 512,
+    // 64 x 256 that still yields >= 150 tiles (~0.6 per CU), else 64 x 256.
+    // Split-K (one atomic combine per output) only when the tiles leave most
+    // CUs idle.  (Tuned on MI355X over the 2048- and 512-token prefills.)
     p.kind = 1;
     auto tiles_of = [&](int variant) {
       int bm, bn;
@@ -82,9 +84,9 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     if (m <= 16) p.variant = 0;
     else if (m <= 32) p.variant = 1;
     else if (m <= 64) p.variant = 2;
-    else if (tiles_of(4) >= kGemmFullTiles) p.variant = 4;
-    else if (tiles_of(2) >= kGemmFullTiles) p.variant = 2;
-    else p.variant = 3;
+    else if (tiles_of(5) >= kGemmWideTiles) p.variant = 5;
+    else if (tiles_of(6) >= kGemmWideTiles) p.variant = 6;
+    else p.variant = 7;
     int bm, bn;
     gemm_tile_shape(p.variant, &bm, &bn);
     const int64_t tiles = tiles_of(p.variant);

@@ -34,6 +34,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 -> two bf16 (round to nearest even) packed low/high, one
+// v_cvt_pk_bf16_f32.
+typedef __bf16 bl_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float bl_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bl_f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bl_bf16x2));
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }

@@ -1,5 +1,7 @@
-// Ternary x int8 GEMM on int8 MFMA (v_mfma_i32_16x16x64_i8) with the fused
-// dequant, for M > 4 tokens (prefill and batched decode).
+// Ternary x int8 GEMM on int8 MFMA with the fused dequant, for M > 4 tokens
+// (prefill and batched decode): gemm_kernel (v_mfma_i32_16x16x64_i8) for
+// batches up to 64 tokens, gemmw_kernel (v_mfma_i32_32x32x32_i8, wide waves)
+// above.
 //
 // "BitNet b1.58 2B4T Guide: Scaling Native 1-Bit LLMs", section "Matrix
 // Multiplication as Pure Integer Addition": acc = x~ W~^T (integer), then
@@ -7,6 +9,7 @@
 // so it runs on the matrix cores: the 2-bit codes are expanded to int8
 // (64 * W~) in registers right before each MFMA.
 //
+// gemm_kernel:
 // Tile: BM x BN outputs per workgroup, waves in a WM x WN grid, each wave
 // FM x FN fragments of 16x16.  Per 256-input super-chunk the workgroup stages
 //   A: x~ rows m0..m0+BM-1, 256 bytes each, into LDS; the 16-byte unit u of
@@ -245,176 +248,257 @@ hipError_t run(const int8_t* xq, const float* scale, const uint32_t* packed, con
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------------------
-// 32x32x32 variant (v_mfma_i32_32x32x32_i8) for larger M.  Lane l = c + 32 p
-// (c = l % 32, p = l / 32).  A super-chunk is 8 MFMA k-steps (j, h), j = 0..3,
-// h = 0..1; in step (j, h) lane half p covers the 16 inputs 64 j + 16 (2h+p)
-// + (0..15): A from 16-byte unit 4 j + 2 h + p of x~ row c of the fragment, B
-// from packed word (q = 2h + p, j) of output row c.  Result element e of lane
-// l is D[8 (e/4) + 4 p + e % 4][c].  A wave covers 32*FM rows, so each
-// unpacked weight word feeds FM MFMAs.
-//
-// Tiles travel from global memory straight into LDS (global_load_lds_dwordx4:
-// lane i of a wave instruction lands at the wave's LDS base + 16 i), so no
-// registers hold data in flight.  Two LDS stages are separate arrays and the
-// loop is unrolled by two, so the compiler sees that the copies into one stage
-// do not touch the stage being read and only waits for them at the barrier.
-// A unit u of tile row r sits at unit u ^ (r % 16): each lane fetches the
-// global unit that belongs in its slot.
 // 16 bytes per lane from global memory straight into LDS: lane i of the wave
-// writes lds_wave_base + 16 i (global_load_lds_dwordx4).
+// writes lds_wave_base + 16 i (global_load_lds_dwordx4).  A non-template
+// wrapper: the builtin is not accepted inside templates by the host pass.
 __device__ __forceinline__ void lds_copy16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
 }
 
-// One super-chunk of A and B copied global -> LDS (wave instruction u of a
-// tile fills 1 KiB at slot u * NT + 64 * wave).
-template <int UA, int UB, int NT>
-__device__ __forceinline__ void copy_tiles(const int8_t* const (&a_src)[UA],
-                                           const uint4* const (&b_src)[UB], uint8_t* As,
-                                           uint8_t* Bs, int cc, int wave) {
-#pragma unroll
-  for (int u = 0; u < UA; ++u)
-    lds_copy16(a_src[u] + (int64_t)cc * 256, As + (u * NT + wave * 64) * 16);
-#pragma unroll
-  for (int u = 0; u < UB; ++u)
-    lds_copy16(b_src[u] + (int64_t)cc * kBlockU4, Bs + (u * NT + wave * 64) * 16);
-}
-
-template <int FM, int FN, int WM, int WN>
-struct Tile32 {
-  static constexpr int BM = 32 * FM * WM;
-  static constexpr int BN = 32 * FN * WN;
-  static constexpr int NT = 64 * WM * WN;
-  static constexpr int BNB = BN / 64;
-  static constexpr int UA = BM * 16 / NT;          // A copy instructions per thread
-  static constexpr int UB = BNB * kBlockU4 / NT;   // B copy instructions per thread
-  static constexpr int A_BYTES = BM * 256;
-  static constexpr int B_BYTES = BNB * 4096;
-  static_assert(BN % 64 == 0, "tile width must hold whole packed blocks");
-  static_assert(BM * 16 % NT == 0 && BNB * kBlockU4 % NT == 0, "copy split");
+// ------------------------------------------------------------------------
+// Wide-wave 32x32x32 variant for large M.  Waves sit side by side along N
+// (one row of WN waves); each wave owns one 64-row packed block (two 32-column
+// fragments) and 32*FM tile rows, so every unpacked weight word feeds FM
+// MFMAs and no block is unpacked by two waves.  x~ and the packed blocks go
+// global -> LDS by DMA (each wave copies and reads only its own block), two
+// stages of KS super-chunks each: the copies of the next stage are in flight
+// while the current one is computed, so larger KS covers a longer load
+// latency.
+//
+// v_mfma_i32_32x32x32_i8 lanes: lane l = c + 32 ph (c = l % 32, ph = l / 32)
+// supplies row/column c of its operand for 16 inputs; a super-chunk is 8
+// k-steps (j, h), j = 0..3, h = 0..1, and in step (j, h) lane half ph covers
+// inputs 64 j + 16 (2h+ph) + (0..15): the weights from packed word (q = 2h +
+// ph, j) of output row c of the fragment, x~ from 16-byte unit 4 j + 2 h + ph
+// of tile row c (an x~ unit u of tile row r sits at unit u ^ (r % 16) in LDS,
+// so the lanes of one read hit different banks).  Byte e of operand dword i
+// is input 4 i + e on both sides.  The weights are the MFMA's first operand,
+// so the result is the transposed tile: element e of lane l holds tile row
+// 32fm + c and column 32fn + 8(e/4) + 4ph + e%4, four consecutive columns
+// per group of four elements, stored as one vector.
+//
+// Tile order: with `band` > 0, tiles are numbered band by band (band tile
+// rows each, column-major inside a band) and consecutive numbers go to the
+// same XCD (workgroups are dispatched to the 8 XCDs round-robin), so the
+// workgroups that share an XCD's L2 cover a compact block of the output and
+// share its x~ rows and packed columns.
+template <int FM, int WN, int KS>
+struct TileW {
+  static constexpr int BM = 32 * FM;
+  static constexpr int BN = 64 * WN;
+  static constexpr int NT = 64 * WN;
+  static constexpr int UA = BM * 16 / NT;          // A copy instructions per thread and chunk
+  static constexpr int A_CHUNK = BM * 256;         // x~ bytes per super-chunk
+  static constexpr int B_CHUNK = WN * 4096;        // packed bytes per super-chunk
+  static constexpr int A_BYTES = KS * A_CHUNK;     // one stage
+  static constexpr int B_BYTES = KS * B_CHUNK;
+  static_assert(BM * 16 % NT == 0, "copy split");
+  static_assert(2 * (A_BYTES + B_BYTES) <= 160 * 1024, "LDS");
 };
 
-template <int FM, int FN, int WM, int WN, bool SPLIT>
-__global__ __launch_bounds__(64 * WM * WN) void gemm32_kernel(
+__device__ __forceinline__ int tile_of_block(int bid, int tiles, int tiles_m, int tiles_n,
+                                             int band) {
+  if (band <= 0) return bid;
+  // round-robin XCD x = bid % 8 receives the contiguous range of the
+  // banded order starting at x * (tiles / 8) + min(x, tiles % 8)
+  const int x = bid & 7, li = bid >> 3;
+  const int q = tiles >> 3, r = tiles & 7;
+  const int lin = x * q + min(x, r) + li;
+  const int per_band = band * tiles_n;
+  const int b = lin / per_band, w = lin - b * per_band;
+  const int rows = min(band, tiles_m - b * band);  // tile rows in this band
+  const int tn = w / rows, tm = b * band + (w - tn * rows);
+  return tm * tiles_n + tn;
+}
+
+template <int FM, int WN, int KS, bool SPLIT>
+__global__ __launch_bounds__(64 * WN) void gemmw_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ scale,
     const uint4* __restrict__ packed, const float* __restrict__ gamma, int m, int n,
-    int nb, int nc, int64_t kpad, int splits, int tiles_n, int relu2, int bf16,
-    void* __restrict__ y, int32_t* __restrict__ acc_out, int64_t* __restrict__ ws_slots) {
-  using T = Tile32<FM, FN, WM, WN>;
-  constexpr int BM = T::BM, BN = T::BN, NT = T::NT, UA = T::UA, UB = T::UB;
+    int nb, int nc, int64_t kpad, int splits, int tiles_m, int tiles_n, int band, int relu2,
+    int bf16, int vec_out, void* __restrict__ y, int32_t* __restrict__ acc_out,
+    int64_t* __restrict__ ws_slots) {
+  using T = TileW<FM, WN, KS>;
+  constexpr int BM = T::BM, BN = T::BN, NT = T::NT, UA = T::UA;
+  // two stages as separate arrays: the compiler then sees that the copies
+  // into one stage do not touch the other and does not wait for them before
+  // the LDS reads of the stage being computed
   __shared__ __attribute__((aligned(16))) uint8_t A0[T::A_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t A1[T::A_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t B0[T::B_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t B1[T::B_BYTES];
-  __shared__ uint32_t flag;
 
-  const int tile = blockIdx.x / splits;
-  const int s = blockIdx.x - tile * splits;
+  const int tiles = tiles_m * tiles_n;
+  const int bid = (int)blockIdx.x / splits;
+  const int s = (int)blockIdx.x - bid * splits;
+  const int tile = tile_of_block(bid, tiles, tiles_m, tiles_n, band);
   const int tm = tile / tiles_n;
   const int tn = tile - tm * tiles_n;
   const int m0 = tm * BM;
-  const int b0 = tn * T::BNB;
   const int c0 = (int)((int64_t)s * nc / splits);
   const int c1 = (int)((int64_t)(s + 1) * nc / splits);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int wm = wave / WN;
-  const int wn = wave - wm * WN;
   const int c = lane & 31;
   const int ph = lane >> 5;
+  const int blk = min(tn * WN + wave, nb - 1);      // this wave's packed block (clamped)
 
-  // Per-thread source addresses of the copies (super-chunk 0); rows past m
-  // and blocks past nb read clamped, valid memory whose results are dropped.
+  // x~ copy sources (super-chunk 0); rows past m read row m-1 (dropped)
   const int8_t* a_src[UA];
 #pragma unroll
   for (int u = 0; u < UA; ++u) {
-    const int p = u * NT + tid;                  // LDS slot (16 bytes) this lane fills
+    const int p = u * NT + tid;
     const int row = p >> 4, slot = p & 15;
     const int gm = min(m0 + row, m - 1);
     a_src[u] = xq + (int64_t)gm * kpad + ((slot ^ (row & 15)) << 4);
   }
-  const uint4* b_src[UB];
+  const uint4* b_src = packed + (int64_t)blk * nc * kBlockU4 + lane;
+  // one stage: super-chunks cc .. cc+KS-1 (those < c1)
+  auto copy_stage = [&](uint8_t* As, uint8_t* Bs, int cc) {
 #pragma unroll
-  for (int u = 0; u < UB; ++u) {
-    const int p = u * NT + tid;
-    const int blk = min(b0 + (p >> 8), nb - 1);
-    b_src[u] = packed + (int64_t)blk * nc * kBlockU4 + (p & 255);
-  }
-
-  bl_v16i acc[FM][FN];
+    for (int k = 0; k < KS; ++k) {
+      if (cc + k < c1) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+        for (int u = 0; u < UA; ++u)
+          lds_copy16(a_src[u] + (int64_t)(cc + k) * 256,
+                     As + k * T::A_CHUNK + (u * NT + wave * 64) * 16);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = bl_v16i{};
-
-  // per-lane LDS offsets: A fragment rows and the swizzled unit of each k-step
-  const int a_row = (wm * 32 * FM + c) * 256;
-  int a_unit[8];
-#pragma unroll
-  for (int st = 0; st < 8; ++st) a_unit[st] = ((4 * (st >> 1) + 2 * (st & 1) + ph) ^ (c & 15)) << 4;
-  const int bcol = wn * 32 * FN + c;
-  const int b_off = (bcol >> 6) * 4096 + ph * 1024 + (bcol & 63) * 16;
-
-  auto compute = [&](const uint8_t* As, const uint8_t* Bs) {
-    uint4 bw[FN][2];
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int d = ((32 * fn) >> 6) * 4096 + ((32 * fn) & 63) * 16;
-      bw[fn][0] = *reinterpret_cast<const uint4*>(Bs + b_off + d);
-      bw[fn][1] = *reinterpret_cast<const uint4*>(Bs + b_off + d + 2048);
-    }
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {              // k-step (j, h) = (st / 2, st % 2)
-      const int j = st >> 1, h = st & 1;
-      bl_v4i a[FM];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        a[fm] = *reinterpret_cast<const bl_v4i*>(As + a_row + fm * 32 * 256 + a_unit[st]);
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const uint4 wv = bw[fn][h];
-        const uint32_t wj = j == 0 ? wv.x : j == 1 ? wv.y : j == 2 ? wv.z : wv.w;
-        const bl_v4i bop = {(int)unpack_x64(wj, 0), (int)unpack_x64(wj, 1),
-                            (int)unpack_x64(wj, 2), (int)unpack_x64(wj, 3)};
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-          acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[fm], bop, acc[fm][fn], 0, 0, 0);
+        for (int u = 0; u < 4; ++u)
+          lds_copy16(b_src + (int64_t)(cc + k) * kBlockU4 + u * 64,
+                     Bs + k * T::B_CHUNK + wave * 4096 + u * 1024);
       }
     }
   };
 
-  if (c0 < c1) copy_tiles<UA, UB, NT>(a_src, b_src, A0, B0, c0, wave);
+  bl_v16i acc[FM][2];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = bl_v16i{};
+
+  int a_unit[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) a_unit[st] = ((4 * (st >> 1) + 2 * (st & 1) + ph) ^ (c & 15)) << 4;
+  const int a_row = c * 256;
+
+  // One super-chunk: 8 k-steps (j, h) = (st / 2, st % 2), software
+  // pipelined: during step st the A operands of step st+RING-1 are read
+  // from LDS and the B operands of step st+1 unpacked, while step st's
+  // MFMAs run; the group barriers interleave the unpack VALU between the
+  // MFMAs and a scheduling barrier closes each step.
+  auto unpack_b = [&](const uint4 (&bw)[2][2], int st, bl_v4i (&bop)[2]) {
+    const int j = st >> 1, h = st & 1;
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) {
+      const uint4 wv = bw[fn][h];
+      const uint32_t wj = j == 0 ? wv.x : j == 1 ? wv.y : j == 2 ? wv.z : wv.w;
+      bop[fn] = bl_v4i{(int)unpack_x64(wj, 0), (int)unpack_x64(wj, 1), (int)unpack_x64(wj, 2),
+                       (int)unpack_x64(wj, 3)};
+    }
+  };
+  auto read_a = [&](const uint8_t* As, int st, bl_v4i (&a)[FM]) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+      a[fm] = *reinterpret_cast<const bl_v4i*>(As + a_row + fm * 32 * 256 + a_unit[st]);
+  };
+  // this lane's packed words: fragment fn, half h -> uint4 (q = 2h + ph, row 32fn + c)
+  auto read_b = [&](const uint8_t* Bs, uint4 (&bw)[2][2]) {
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        bw[fn][h] = *reinterpret_cast<const uint4*>(Bs + wave * 4096 + (2 * h + ph) * 1024 +
+                                                    (32 * fn + c) * 16);
+  };
+  constexpr int RING = FM >= 4 ? 2 : 3;             // A reads run RING-1 steps ahead
+  auto compute = [&](const uint8_t* As, const uint4 (&bw)[2][2]) {
+    bl_v4i a[RING][FM];
+    bl_v4i bop[2][2];
+#pragma unroll
+    for (int r = 0; r + 1 < RING; ++r) read_a(As, r, a[r]);
+    unpack_b(bw, 0, bop[0]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st + RING - 1 < 8) read_a(As, st + RING - 1, a[(st + RING - 1) % RING]);
+      if (st + 1 < 8) unpack_b(bw, st + 1, bop[(st + 1) & 1]);
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bop[st & 1][fn], a[st % RING][fm],
+                                                             acc[fm][fn], 0, 0, 0);
+      if (st + 1 < 8) {
+        // interleave: the first MFMA (after the wait for this step's
+        // operands), then the LDS reads for a later step, then one MFMA per
+        // two unpack VALU ops
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, FM, 0);     // DS read
+#pragma unroll
+        for (int i = 1; i < 2 * FM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);    // VALU
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // A stage's packed words are read into registers before the copies of
+  // the next stage are issued: LDS reads issued after a copy may be made to
+  // wait for it.
+  auto read_b_stage = [&](const uint8_t* Bs, uint4 (&bw)[KS][2][2]) {
+#pragma unroll
+    for (int k = 0; k < KS; ++k) read_b(Bs + k * T::B_CHUNK, bw[k]);
+  };
+  auto compute_stage = [&](const uint8_t* As, const uint4 (&bw)[KS][2][2], int cc) {
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      if (cc + k < c1) compute(As + k * T::A_CHUNK, bw[k]);
+  };
+
+  // Pairs of stages, then an odd last one (a loop without early exits keeps
+  // the accumulators in place).
+  uint4 bw[KS][2][2];
+  if (c0 < c1) copy_stage(A0, B0, c0);
   __syncthreads();
-  for (int cc = c0; cc < c1; cc += 2) {
-    if (cc + 1 < c1) copy_tiles<UA, UB, NT>(a_src, b_src, A1, B1, cc + 1, wave);
-    compute(A0, B0);
+  int cc = c0;
+  for (; cc + 2 * KS <= c1; cc += 2 * KS) {
+    read_b_stage(B0, bw);
+    copy_stage(A1, B1, cc + KS);
+    compute_stage(A0, bw, cc);
     __syncthreads();
-    if (cc + 1 >= c1) break;
-    if (cc + 2 < c1) copy_tiles<UA, UB, NT>(a_src, b_src, A0, B0, cc + 2, wave);
-    compute(A1, B1);
+    read_b_stage(B1, bw);
+    if (cc + 2 * KS < c1) copy_stage(A0, B0, cc + 2 * KS);
+    compute_stage(A1, bw, cc + KS);
     __syncthreads();
+  }
+  if (cc < c1) {
+    read_b_stage(B0, bw);
+    if (cc + KS < c1) copy_stage(A1, B1, cc + KS);
+    compute_stage(A0, bw, cc);
+    __syncthreads();
+    if (cc + KS < c1) {
+      read_b_stage(B1, bw);
+      compute_stage(A1, bw, cc + KS);
+    }
   }
 
   if constexpr (SPLIT) {
-    // Split-K through 64-bit workspace slots, as in gemm_kernel, one
-    // fragment row (FN * 16 elements) per batch.
     int64_t* slot = ws_slots + (int64_t)tile * (BM * BN) + tid;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
-      int64_t old[FN][16];
+      int64_t old[2][16];
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          old[fn][e] = split_add(slot + ((fm * FN + fn) * 16 + e) * NT, acc[fm][fn][e]);
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
+      for (int fn = 0; fn < 2; ++fn)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          acc[fm][fn][e] = split_finish(slot + ((fm * FN + fn) * 16 + e) * NT, old[fn][e],
+          old[fn][e] = split_add(slot + ((fm * 2 + fn) * 16 + e) * NT, acc[fm][fn][e]);
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          acc[fm][fn][e] = split_finish(slot + ((fm * 2 + fn) * 16 + e) * NT, old[fn][e],
                                         acc[fm][fn][e], splits);
     }
   }
@@ -427,59 +511,91 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm32_kernel(
     fac[t] = gm < m ? gamma_over_s(gam, scale[gm]) : 0.0f;
   }
   __syncthreads();
+  // Each group of four accumulator elements is four consecutive columns of
+  // one row: whole groups go out as one 16-byte (fp32, int32) or 8-byte
+  // (bf16) store when vec_out (n % 4 == 0 and aligned outputs); split
+  // groups, the column tail and unaligned outputs go element by element.
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
+    const int gm = m0 + 32 * fm + c;
+    if (gm >= m) continue;
+    const float f = fac[32 * fm + c];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = wm * 32 * FM + 32 * fm + 8 * (e >> 2) + 4 * ph + (e & 3);
-      const int gm = m0 + row;
-      if (gm >= m) continue;
-      const float f = fac[row];
+    for (int fn = 0; fn < 2; ++fn) {
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int gn = b0 * 64 + wn * 32 * FN + 32 * fn + c;
-        if (gn >= n || (acc[fm][fn][e] & 63) != 0) continue;
-        const int a = acc[fm][fn][e] >> 6;
+      for (int g = 0; g < 4; ++g) {
+        const int gn = (tn * WN + wave) * 64 + 32 * fn + 8 * g + 4 * ph;
         const int64_t idx = (int64_t)gm * n + gn;
-        if (acc_out != nullptr) acc_out[idx] = a;
-        store_out(y, idx, a, f, relu2 != 0, bf16 != 0);
+        int v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = acc[fm][fn][4 * g + t];
+        if (!SPLIT && vec_out && gn + 3 < n) {
+          float o[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            o[t] = (float)(v[t] >> 6) * f;
+            if (relu2) o[t] = o[t] > 0.0f ? o[t] * o[t] : 0.0f;
+          }
+          if (acc_out != nullptr)
+            *reinterpret_cast<int4*>(acc_out + idx) =
+                make_int4(v[0] >> 6, v[1] >> 6, v[2] >> 6, v[3] >> 6);
+          if (bf16)
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + idx) =
+                make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+          else
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + idx) =
+                make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if (gn + t >= n || (v[t] & 63) != 0) continue;
+            const int a = v[t] >> 6;
+            if (acc_out != nullptr) acc_out[idx + t] = a;
+            store_out(y, idx + t, a, f, relu2 != 0, bf16 != 0);
+          }
+        }
       }
     }
   }
 }
 
-template <int FM, int FN, int WM, int WN>
-hipError_t run32(const int8_t* xq, const float* scale, const uint32_t* packed, const float* gamma,
-                 int64_t m, int64_t n, int64_t k, int splits, bool relu2, bool bf16, void* y,
-                 int32_t* acc_out, int64_t* slots, hipStream_t stream) {
-  using T = Tile32<FM, FN, WM, WN>;
+template <int FM, int WN, int KS>
+hipError_t runw(const int8_t* xq, const float* scale, const uint32_t* packed, const float* gamma,
+                int64_t m, int64_t n, int64_t k, int splits, int band, bool relu2, bool bf16,
+                void* y, int32_t* acc_out, int64_t* slots, hipStream_t stream) {
+  using T = TileW<FM, WN, KS>;
   const int nb = (int)cdiv(n, kRowBlock);
   const int nc = (int)cdiv(k, kSuperK);
   const int tiles_m = (int)cdiv(m, T::BM);
   const int tiles_n = (int)cdiv(padded_n(n), T::BN);
   const int64_t grid = (int64_t)tiles_m * tiles_n * splits;
-  auto kern =
-      splits > 1 ? gemm32_kernel<FM, FN, WM, WN, true> : gemm32_kernel<FM, FN, WM, WN, false>;
+  const int vec_out = n % 4 == 0 && (uintptr_t)y % (bf16 ? 8 : 16) == 0 &&
+                      (acc_out == nullptr || (uintptr_t)acc_out % 16 == 0);
+  auto kern = splits > 1 ? gemmw_kernel<FM, WN, KS, true> : gemmw_kernel<FM, WN, KS, false>;
   kern<<<(unsigned)grid, T::NT, 0, stream>>>(
       xq, scale, reinterpret_cast<const uint4*>(packed), gamma, (int)m, (int)n, nb, nc,
-      padded_k(k), splits, tiles_n, relu2, bf16, y, acc_out, slots);
+      padded_k(k), splits, tiles_m, tiles_n, band, relu2, bf16, vec_out, y, acc_out, slots);
   return hipGetLastError();
 }
 
 }  // namespace
 
 // Tile variants: rows per tile x columns per tile.
-//   0: 16 x 256   1: 32 x 256   2: 64 x 256   3: 64 x 128   (16x16x64 MFMA)
-//   4: 128 x 256  (32x32x32 MFMA, tiles copied to LDS by DMA)
+//   0: 16 x 256   1: 32 x 256   2: 64 x 256           (16x16x64 MFMA, M <= 64)
+//   5: 128 x 512  6: 64 x 512   7: 64 x 256           (32x32x32 MFMA, wide waves)
 void gemm_tile_shape(int variant, int* bm, int* bn) {
   switch (variant) {
     case 0: *bm = Tile<1, 4, 1, 4>::BM; *bn = Tile<1, 4, 1, 4>::BN; break;
     case 1: *bm = Tile<2, 4, 1, 4>::BM; *bn = Tile<2, 4, 1, 4>::BN; break;
     case 2: *bm = Tile<4, 4, 1, 4>::BM; *bn = Tile<4, 4, 1, 4>::BN; break;
-    case 3: *bm = Tile<2, 4, 2, 2>::BM; *bn = Tile<2, 4, 2, 2>::BN; break;
-    default: *bm = Tile32<2, 2, 2, 4>::BM; *bn = Tile32<2, 2, 2, 4>::BN; break;
+    case 5: *bm = TileW<4, 8, 1>::BM; *bn = TileW<4, 8, 1>::BN; break;
+    case 6: *bm = TileW<2, 8, 1>::BM; *bn = TileW<2, 8, 1>::BN; break;
+    default: *bm = TileW<2, 4, 1>::BM; *bn = TileW<2, 4, 1>::BN; break;
   }
 }
+
+// band: tile rows per band of the XCD-grouped order for the wide variants.
+constexpr int kBand = 4;
 
 hipError_t launch_gemm(int variant, const int8_t* xq, const float* scale, const uint32_t* packed,
                        const float* gamma, int64_t m, int64_t n, int64_t k, int splits,
@@ -489,8 +605,9 @@ hipError_t launch_gemm(int variant, const int8_t* xq, const float* scale, const 
     case 0: return run<1, 4, 1, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, slots, stream);
     case 1: return run<2, 4, 1, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, slots, stream);
     case 2: return run<4, 4, 1, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, slots, stream);
-    case 3: return run<2, 4, 2, 2>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, slots, stream);
-    default: return run32<2, 2, 2, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y, acc_out, slots, stream);
+    case 5: return runw<4, 8, 1>(xq, scale, packed, gamma, m, n, k, splits, kBand, relu2, bf16, y, acc_out, slots, stream);
+    case 6: return runw<2, 8, 1>(xq, scale, packed, gamma, m, n, k, splits, kBand, relu2, bf16, y, acc_out, slots, stream);
+    default: return runw<2, 4, 1>(xq, scale, packed, gamma, m, n, k, splits, kBand, relu2, bf16, y, acc_out, slots, stream);
   }
 }
 

@@ -167,11 +167,15 @@ FWD_CASES = [
     (33, 100, 257, True, "f32", "f32"),
     (64, 512, 2560, False, "bf16", "bf16"),
     (65, 129, 300, False, "f32", "f32"),
-    (130, 320, 1024, True, "bf16", "bf16"),
+    (130, 320, 1024, True, "bf16", "bf16"),      # 64 x 256 wide tiles, split-K
+    (129, 260, 5000, True, "f32", "bf16"),       # 64 x 256, split-K over 4, ragged M
     (256, 384, 768, False, "f32", "bf16"),
-    (1000, 6100, 300, True, "bf16", "bf16"),     # 128 x 256 DMA tiles, ragged M, N, K
-    (1024, 6144, 512, False, "f32", "bf16"),
-    (256, 8192, 768, False, "bf16", "f32"),      # 64 x 128 tiles
+    (200, 1001, 700, False, "bf16", "f32"),      # 64 x 256, odd N: element stores
+    (1000, 6100, 300, True, "bf16", "bf16"),     # 64 x 512 tiles, ragged M, N, K
+    (1024, 6144, 512, False, "f32", "bf16"),     # 64 x 512, vector stores
+    (256, 8192, 768, False, "bf16", "f32"),      # 64 x 256
+    (1100, 9001, 300, True, "bf16", "bf16"),     # 128 x 512 tiles, ragged M, odd N
+    (1030, 9216, 256, False, "f32", "f32"),      # 128 x 512, vector stores
 ]
 
 
