@@ -27,6 +27,8 @@ Also reported on the same line:
                 2048x6912 -> 2560): 2*M*N*K / kernel time, in TOPS;
   decode_100b   batch-1 GEMV at 100B-class shapes (up 28672x8192, down
                 8192x28672), weights rotated past the caches, GB/s;
+  stack_c3      the 2B-class set as a 30-layer stack (388 MB packed), one
+                pass in layer order at 1/8/32/64 tokens: us per pass;
   cpu_baseline  the CPU oracle (numpy) on a bounded sample of the same step.
 """
 from __future__ import annotations
@@ -303,6 +305,91 @@ def run_decode_100b(B, torch, args):
             "GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "per_matrix": out}
 
 
+def run_stack_c3(B, torch, args):
+    """The c3 stack: the 2B-class set as 30 layers, each with its own copy of
+    the packed weights (388 MB in all, past the caches).  One pass = every
+    layer in order: q/k/v (one shared input), o, up (ReLU^2), down, at 1, 8,
+    32 and 64 tokens with Student-t activations.  Up to 4 tokens each group
+    is one fused decode launch (activation quant in its prologue); above,
+    one activation quant per distinct input and one GEMM per matrix.  A pass
+    is captured as one graph; the best of a few replays is reported."""
+    import datagen
+    wl = datagen.WORKLOADS["c3"]
+    layers = wl.layers
+    mats = {}
+    for name, (n, k, relu2, group) in wl.matrices.items():
+        w = torch.from_numpy(datagen.workload_weights(wl, name)).cuda()
+        packed, gamma = B.pack_weights(w)
+        del w
+        mats[name] = dict(n=n, k=k, relu2=relu2, group=group, gamma=gamma,
+                          packed=[packed] + [packed.clone() for _ in range(layers - 1)])
+    order = [("q", "k", "v"), ("o",), ("up",), ("down",)]
+    lib = B.lib
+    out = {}
+    for m in wl.batches:
+        xs = {}
+        for g in wl.groups():
+            bits, _ = datagen.activations(wl, g, m)
+            xs[g] = torch.from_numpy(bits.view("int16")).view(torch.bfloat16).cuda()
+        ys = {nm: torch.empty((m, d["n"]), dtype=torch.bfloat16, device="cuda")
+              for nm, d in mats.items()}
+        ws = B.Workspace()
+        calls = []
+        if m <= 4:
+            for l in range(layers):
+                for grp in order:
+                    ops = [dict(x=xs[mats[nm]["group"]], packed=mats[nm]["packed"][l],
+                                gamma=mats[nm]["gamma"], n=mats[nm]["n"], k=mats[nm]["k"],
+                                y=ys[nm], relu2=mats[nm]["relu2"]) for nm in grp]
+                    calls.append(B.FusedStep(ops, workspace=ws))
+        else:
+            xq = {g: torch.empty((m, B.padded_k(x.shape[1])), dtype=torch.int8, device="cuda")
+                  for g, x in xs.items()}
+            sc = {g: torch.empty(m, dtype=torch.float32, device="cuda") for g in xs}
+            ws.get(max(B.forward_workspace_bytes(m, d["n"], d["k"]) for d in mats.values()))
+
+            def quant(g):
+                x = xs[g]
+                B._check("quant", lib.bitlinear_quant_act(
+                    x.data_ptr(), B.BL_BF16, m, x.shape[1], B.EPS_DEFAULT, xq[g].data_ptr(),
+                    sc[g].data_ptr(), B._stream()))
+
+            def gemm(nm, l):
+                d = mats[nm]
+                B.forward(xq[d["group"]], sc[d["group"]], d["packed"][l], d["gamma"], d["n"],
+                          d["k"], relu2=d["relu2"], y=ys[nm], workspace=ws)
+
+            for l in range(layers):
+                for grp in order:
+                    calls.append(lambda g=mats[grp[0]]["group"]: quant(g))
+                    for nm in grp:
+                        calls.append(lambda nm=nm, l=l: gemm(nm, l))
+        torch.cuda.synchronize()
+        g = capture(torch, lambda: [c() for c in calls])
+        g.replay()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(5):
+            st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            st.record()
+            g.replay()
+            en.record()
+            torch.cuda.synchronize()
+            best = min(best, st.elapsed_time(en))
+        by = layers * (sum(d["n"] * d["k"] / 4 + 4 + 2 * m * d["n"] for d in mats.values()) +
+                       sum(2 * m * x.shape[1] for x in xs.values()))
+        ops = 2.0 * m * layers * sum(d["n"] * d["k"] for d in mats.values())
+        out[str(m)] = {"us_per_pass": round(best * 1e3, 1), "launches": len(calls),
+                       "GBs": round(by / (best * 1e-3) / 1e9, 1),
+                       "TOPS": round(ops / (best * 1e-3) / 1e12, 2)}
+        log(f"c3 stack m={m}: {best*1e3:.1f} us/pass")
+        del g, calls, xs, ys, ws
+        torch.cuda.empty_cache()
+    return {"workload": "c3: 30 layers x {q,k,v,o,up,down} at 2B-class shapes, one pass in "
+                        "layer order, packed weights 388 MB",
+            "per_batch": out}
+
+
 def run_cpu_baseline(budget_s=12.0):
     """The oracle as it stands, on the same decode step: activation quant, the
     six integer products and the dequant, codes prepared beforehand."""
@@ -494,6 +581,7 @@ def main():
     d100 = None if args.no_extra else run_decode_100b(B, torch, args)
     if d100:
         log(f"decode 100B-class: {d100['GBs']} GB/s")
+    stack = None if args.no_extra else run_stack_c3(B, torch, args)
     cpu = None if args.no_cpu else run_cpu_baseline()
     line = {
         "metric": "BitLinear W1.58A8 decode GB/s (% HBM peak) + prefill TOPS (% int8 MFMA)",
@@ -517,6 +605,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": prefill,
         "decode_100b": d100,
+        "stack_c3": stack,
         "wall_s": round(time.time() - t0, 1),
     }
     print(json.dumps(line))

@@ -8,7 +8,7 @@
 
 namespace bl {
 
-hipError_t launch_gemv(int m, int waves, int pf, const int8_t* xq, const float* scale,
+hipError_t launch_gemv(int m, int waves, int pf, int qpl, const int8_t* xq, const float* scale,
                        const uint32_t* packed, const float* gamma, int64_t n, int64_t k,
                        int splits, bool relu2, bool bf16, void* y, int32_t* acc_out,
                        int64_t* ws_slots, hipStream_t stream);
@@ -49,24 +49,33 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
   const int64_t nc = cdiv(k, kSuperK);
   if (m <= 0) return p;
   if (m <= kGemvMaxM) {
-    // Split-K factor: many row blocks keep one workgroup each; few are split
-    // over up to 4 workgroups (one atomic combine per output), each keeping
-    // >= 2 super-chunks, and each group's x~ slice must fit LDS.  Waves per
-    // workgroup: 8 when a group has >= 6 super-chunks, else 4; two
-    // super-chunks in flight per wave once a wave streams >= 4.  (Tuned on
+    // Rows up to 40 super-chunks (K <= 10240): 16-row groups (a quarter of
+    // a packed block each, four lanes per row), no K split, 8 waves when a
+    // group has >= 16 super-chunks.  Longer rows: 64-row groups, split over
+    // up to 4 workgroups when the row blocks alone cannot fill the chip
+    // (one atomic combine per output), each keeping >= 2 super-chunks; 8
+    // waves when a group has >= 6 super-chunks, two in flight per wave once
+    // a wave streams >= 4.  Each group's x~ slice must fit LDS.  (Tuned on
     // MI355X over the 2B- and 100B-class decode shapes.)
     p.kind = 0;
     int64_t s = 1;
-    if (nb < 256) {
-      s = cdiv(kGemvTargetGroups, nb);
-      if (s > 4) s = 4;
-      const int64_t smax = nc / 2 > 1 ? nc / 2 : 1;
-      if (s > smax) s = smax;
+    if (nc <= 40 && m * nc * 256 <= kGemvMaxLds) {
+      p.qpl = 1;
+      p.variant = nc >= 16 ? 8 : 4;
+      p.pf = 4;
+    } else {
+      if (nb < 256) {
+        s = cdiv(kGemvTargetGroups, nb);
+        if (s > 4) s = 4;
+        const int64_t smax = nc / 2 > 1 ? nc / 2 : 1;
+        if (s > smax) s = smax;
+      }
+      while (m * cdiv(nc, s) * 256 > kGemvMaxLds) ++s;
+      const int64_t per_group = nc / s;
+      p.qpl = 4;
+      p.variant = per_group >= 6 ? 8 : 4;
+      p.pf = per_group / p.variant >= 4 ? 2 : 1;
     }
-    while (m * cdiv(nc, s) * 256 > kGemvMaxLds) ++s;
-    const int64_t per_group = nc / s;
-    p.variant = per_group >= 6 ? 8 : 4;
-    p.pf = per_group / p.variant >= 4 ? 2 : 1;
     p.splits = (int)s;
     p.slots = s > 1 ? (size_t)(nb * m * 64) : 0;
   } else {
@@ -111,14 +120,15 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
                           void* workspace, hipStream_t stream) {
   int64_t* slots = plan.splits > 1 ? reinterpret_cast<int64_t*>(workspace) : nullptr;
   if (plan.kind == 0)
-    return launch_gemv((int)m, plan.variant, plan.pf, xq, scale, packed, gamma, n, k, plan.splits,
-                       relu2, bf16, y, acc_out, slots, stream);
+    return launch_gemv((int)m, plan.variant, plan.pf, plan.qpl, xq, scale, packed, gamma, n, k,
+                       plan.splits, relu2, bf16, y, acc_out, slots, stream);
   return launch_gemm(plan.variant, xq, scale, packed, gamma, m, n, k, plan.splits, relu2, bf16,
                      y, acc_out, slots, stream);
 }
 
 struct FusedPlan {
   int waves = 8;
+  int qpl = 4;                          // 16-byte q-parts per lane (rows per group / 16)
   int groups = 0;
   size_t lds = 0;
   size_t ws_bytes = 0;
@@ -145,7 +155,7 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
     if (s > 8) s = 8;
     while (m * cdiv(nc, s) * 256 > kGemvMaxLds) ++s;
     p.splits[i] = (int)s;
-    p.groups += (int)(nb * s);
+    p.groups += (int)(nb * (4 / p.qpl) * s);
     const size_t lds = (size_t)(m * cdiv(nc, s) * 256);
     if (lds > p.lds) p.lds = lds;
     if (s > 1) {
@@ -269,12 +279,12 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
     sg.x_bf16 = o.x_dtype == BL_BF16;
     if (sg.splits > 1)
       sg.slots = reinterpret_cast<int64_t*>(reinterpret_cast<char*>(workspace) + plan.slot_off[i]);
-    begin += (int)(cdiv(o.n, kRowBlock) * sg.splits);
+    begin += (int)(cdiv(o.n, kRowBlock) * (4 / plan.qpl) * sg.splits);
   }
   bool long_rows = false;                            // a row of more than 1024 16-byte units
   for (int i = 0; i < nops; ++i)
     if (ops[i].k * (ops[i].x_dtype == BL_BF16 ? 2 : 4) > 1024 * 16) long_rows = true;
-  const hipError_t e = launch_gemv_fused(args, (int)m, plan.waves, long_rows && m == 1,
+  const hipError_t e = launch_gemv_fused(args, (int)m, plan.waves, plan.qpl, long_rows && m == 1,
                                          plan.groups, plan.lds,
                                          reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? BL_OK : BL_ERR_HIP;

@@ -28,6 +28,7 @@ struct FwdPlan {
   int kind;            // 0 = dot4 GEMV, 1 = MFMA GEMM
   int variant;         // GEMV: waves per workgroup; GEMM: tile variant
   int pf;              // GEMV: super-chunks in flight per wave
+  int qpl;             // GEMV: 16-byte q-parts per lane (4: 64 rows per group, 1: 16 rows)
   int splits;          // split-K factor
   size_t slots;        // 64-bit split-K slots in the workspace (splits > 1)
   size_t ws_bytes;     // total workspace bytes
@@ -59,8 +60,8 @@ struct FusedArgs {
   int nseg;
   float eps;
 };
-hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, bool long_rows, int groups,
-                             size_t lds, hipStream_t stream);
+hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, int qpl, bool long_rows,
+                             int groups, size_t lds, hipStream_t stream);
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t padded_n(int64_t n) { return 64 * cdiv(n, 64); }

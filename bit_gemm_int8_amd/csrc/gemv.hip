@@ -29,24 +29,27 @@
 namespace bl {
 namespace {
 
-// One super-chunk: w = the lane's four 16-byte loads q = 0..3 (word (q, j) =
-// w[q].{x,y,z,w}[j], inputs 64j + 16q + 4i + (0..3)), xs = this super-chunk's
-// 256 bytes of x~ for each token in LDS (token stride xs_stride dwords).
-// The q loop runs in two halves with a scheduling barrier between them, so
-// at most 8 x~ loads (32 registers) are held at once.
-template <int M>
-__device__ __forceinline__ void accumulate_chunk(const uint4 (&w)[4], const uint32_t* xs,
-                                                 int xs_stride, int (&acc)[M]) {
+// One super-chunk: w = the lane's QPL 16-byte loads, q = q0 .. q0+QPL-1
+// (word (q, j) = w[q - q0].{x,y,z,w}[j], inputs 64j + 16q + 4i + (0..3)),
+// xs = this super-chunk's 256 bytes of x~ for each token in LDS (token
+// stride xs_stride dwords).  With all four q in a lane the loop runs in two
+// halves with a scheduling barrier between them, so at most 8 x~ loads (32
+// registers) are held at once.
+template <int M, int QPL>
+__device__ __forceinline__ void accumulate_chunk(const uint4 (&w)[QPL], const uint32_t* xs,
+                                                 int xs_stride, int q0, int (&acc)[M]) {
+  constexpr int HALVES = QPL >= 2 ? 2 : 1;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < HALVES; ++h) {
 #pragma unroll
-      for (int q = 2 * h; q < 2 * h + 2; ++q) {
-        const uint32_t wq[4] = {w[q].x, w[q].y, w[q].z, w[q].w};
+      for (int qi = h * QPL / HALVES; qi < (h + 1) * QPL / HALVES; ++qi) {
+        const uint32_t wq[4] = {w[qi].x, w[qi].y, w[qi].z, w[qi].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint4 xv = *reinterpret_cast<const uint4*>(xs + m * xs_stride + 16 * j + 4 * q);
+          const uint4 xv =
+              *reinterpret_cast<const uint4*>(xs + m * xs_stride + 16 * j + 4 * (q0 + qi));
           acc[m] = dot4(unpack_x64(wq[j], 0), xv.x, acc[m]);
           acc[m] = dot4(unpack_x64(wq[j], 1), xv.y, acc[m]);
           acc[m] = dot4(unpack_x64(wq[j], 2), xv.z, acc[m]);
@@ -63,15 +66,15 @@ __device__ __forceinline__ void accumulate_chunk(const uint4 (&w)[4], const uint
 // first for a wave with none), never used: with no branches around the
 // loads the compiler can count them and wait for older loads without
 // waiting for these.
-template <int PF>
-__device__ __forceinline__ void prefetch_first(uint4 (&buf)[PF][4], const uint4* blk, int c0,
+template <int PF, int QPL>
+__device__ __forceinline__ void prefetch_first(uint4 (&buf)[PF][QPL], const uint4* blk, int c0,
                                                int c1, int g0) {
   const int last = c1 > c0 ? c1 - 1 : g0;
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
     const int c = c0 + p < c1 ? c0 + p : last;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) buf[p][q] = blk[(int64_t)c * kBlockU4 + q * 64];
+    for (int q = 0; q < QPL; ++q) buf[p][q] = blk[(int64_t)c * kBlockU4 + q * 64];
   }
 }
 
@@ -79,32 +82,45 @@ __device__ __forceinline__ void prefetch_first(uint4 (&buf)[PF][4], const uint4*
 // starts at super-chunk g0.  The steady-state loop loads without conditions
 // (so the compiler need not keep old buffer values alive); the last fewer
 // than 2*PF chunks drain after it.
-template <int M, int PF>
-__device__ __forceinline__ void stream_chunks(uint4 (&buf)[PF][4], const uint4* blk, int c0,
+template <int M, int PF, int QPL>
+__device__ __forceinline__ void stream_chunks(uint4 (&buf)[PF][QPL], const uint4* blk, int c0,
                                               int c1, int g0, const uint32_t* xs, int xs_stride,
-                                              int (&acc)[M]) {
+                                              int q0, int (&acc)[M]) {
   int c = c0;
   for (; c + 2 * PF <= c1; c += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      accumulate_chunk<M>(buf[p], xs + (c + p - g0) * 64, xs_stride, acc);
+      accumulate_chunk<M, QPL>(buf[p], xs + (c + p - g0) * 64, xs_stride, q0, acc);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) buf[p][q] = blk[(int64_t)(c + p + PF) * kBlockU4 + q * 64];
+      for (int q = 0; q < QPL; ++q) buf[p][q] = blk[(int64_t)(c + p + PF) * kBlockU4 + q * 64];
     }
   }
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
     if (c + p < c1) {
-      accumulate_chunk<M>(buf[p], xs + (c + p - g0) * 64, xs_stride, acc);
+      accumulate_chunk<M, QPL>(buf[p], xs + (c + p - g0) * 64, xs_stride, q0, acc);
       if (c + p + PF < c1) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) buf[p][q] = blk[(int64_t)(c + p + PF) * kBlockU4 + q * 64];
+        for (int q = 0; q < QPL; ++q)
+          buf[p][q] = blk[(int64_t)(c + p + PF) * kBlockU4 + q * 64];
       }
     }
   }
 #pragma unroll
   for (int p = 0; p < PF; ++p)
-    if (c + PF + p < c1) accumulate_chunk<M>(buf[p], xs + (c + PF + p - g0) * 64, xs_stride, acc);
+    if (c + PF + p < c1)
+      accumulate_chunk<M, QPL>(buf[p], xs + (c + PF + p - g0) * 64, xs_stride, q0, acc);
+}
+
+// Lanes that share a row (lane = r + RPW g, RPW = 16 QPL) add up their
+// q-parts; afterwards every lane of the row holds the row's sum.
+template <int M, int QPL>
+__device__ __forceinline__ void reduce_lane_groups(int (&acc)[M]) {
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    if (QPL <= 2) acc[m] += __shfl_xor(acc[m], 32);
+    if (QPL == 1) acc[m] += __shfl_xor(acc[m], 16);
+  }
 }
 
 // Sum the waves' accumulators into wave 0.  Returns false in other waves.
@@ -157,24 +173,32 @@ __device__ __forceinline__ void write_rows(const int (&acc)[M], const bool (&own
 template <int WAVES>
 constexpr int kXR = WAVES >= 16 ? 1 : 16 / WAVES;
 
-template <int M, int WAVES, int PF>
+// A workgroup owns RPW = 16*QPL rows of a 64-row packed block (sub-block
+// `sub`) and a range of super-chunks; lane l = r + RPW g reads row r's
+// q-parts QPL*g .. QPL*g+QPL-1, so one wave instruction still reads whole
+// 256-byte runs, and the lanes of a row add up their parts at the end.
+// Fewer rows per group give more groups without splitting K.
+template <int M, int WAVES, int PF, int QPL>
 __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ scale,
     const uint4* __restrict__ packed, const float* __restrict__ gamma, int n, int nc,
     int64_t kpad, int splits, int relu2, int bf16, void* __restrict__ y,
     int32_t* __restrict__ acc_out, int64_t* __restrict__ ws_slots) {
+  constexpr int RPW = 16 * QPL, SUBS = 4 / QPL;
   __shared__ int red[WAVES > 1 ? WAVES - 1 : 1][M][64];
   extern __shared__ uint4 xs_lds[];                 // x~ of this group's inputs, per token
-  const int b = blockIdx.x / splits;
-  const int s = blockIdx.x - b * splits;
+  const int bs = blockIdx.x / splits;
+  const int s = blockIdx.x - bs * splits;
+  const int b = bs / SUBS, sub = bs - b * SUBS;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar control
   const int lane = threadIdx.x & 63;
+  const int r = lane % RPW, q0 = QPL * (lane / RPW);
   // this workgroup's super-chunks, then this wave's contiguous share
   const int g0 = (int)((int64_t)s * nc / splits);
   const int g1 = (int)((int64_t)(s + 1) * nc / splits);
   const int c0 = g0 + (int)((int64_t)wave * (g1 - g0) / WAVES);
   const int c1 = g0 + (int)((int64_t)(wave + 1) * (g1 - g0) / WAVES);
-  const uint4* blk = packed + (int64_t)b * nc * kBlockU4 + lane;
+  const uint4* blk = packed + (int64_t)b * nc * kBlockU4 + q0 * 64 + sub * RPW + r;
 
   // x~[m][256*g0 .. 256*g1) for every token (16 units of 16 bytes per
   // super-chunk and token) goes to LDS.  Its first loads are issued before
@@ -199,8 +223,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     xr[r] = x_unit(xu[r]);
   }
 
-  uint4 buf[PF][4];
-  prefetch_first<PF>(buf, blk, c0, c1, g0);
+  uint4 buf[PF][QPL];
+  prefetch_first<PF, QPL>(buf, blk, c0, c1, g0);
   // epilogue operands, loaded now so their latency hides under the stream
   const float g = *gamma;
   float fac[M];
@@ -214,27 +238,30 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
   for (int r = 0; r < XR; ++r) xs_lds[xu[r]] = xr[r];
   for (int u = threadIdx.x + NT * XR; u < units; u += NT) xs_lds[u] = x_unit(u);
   __syncthreads();
-  stream_chunks<M, PF>(buf, blk, c0, c1, g0, reinterpret_cast<const uint32_t*>(xs_lds), span * 4,
-                       acc);
+  stream_chunks<M, PF, QPL>(buf, blk, c0, c1, g0, reinterpret_cast<const uint32_t*>(xs_lds),
+                            span * 4, q0, acc);
+  reduce_lane_groups<M, QPL>(acc);
   if (!reduce_waves<M, WAVES>(acc, red, wave, lane)) return;
+  if (lane >= RPW) return;
+  const int rb = sub * RPW + r;                     // row within the 64-row block
   bool own[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) own[m] = true;
-  if (splits > 1) combine_splits<M>(acc, own, ws_slots + (int64_t)b * (M * 64) + lane, splits);
+  if (splits > 1) combine_splits<M>(acc, own, ws_slots + (int64_t)b * (M * 64) + rb, splits);
 #pragma unroll
   for (int m = 0; m < M; ++m) fac[m] = gamma_over_s(g, fac[m]);
-  write_rows<M>(acc, own, fac, (int64_t)b * 64 + lane, n, y, acc_out, relu2 != 0, bf16 != 0);
+  write_rows<M>(acc, own, fac, (int64_t)b * 64 + rb, n, y, acc_out, relu2 != 0, bf16 != 0);
 }
 
-template <int M, int WAVES, int PF>
+template <int M, int WAVES, int PF, int QPL>
 hipError_t run_gemv(const int8_t* xq, const float* scale, const uint32_t* packed,
                     const float* gamma, int64_t n, int64_t k, int splits, bool relu2, bool bf16,
                     void* y, int32_t* acc_out, int64_t* ws_slots, hipStream_t stream) {
   const int nb = (int)cdiv(n, kRowBlock);
   const int nc = (int)cdiv(k, kSuperK);
-  dim3 grid((unsigned)((int64_t)nb * splits)), block(64 * WAVES);
+  dim3 grid((unsigned)((int64_t)nb * (4 / QPL) * splits)), block(64 * WAVES);
   const size_t lds = (size_t)M * cdiv(nc, splits) * 256;
-  gemv_kernel<M, WAVES, PF><<<grid, block, lds, stream>>>(
+  gemv_kernel<M, WAVES, PF, QPL><<<grid, block, lds, stream>>>(
       xq, scale, reinterpret_cast<const uint4*>(packed), gamma, (int)n, nc, padded_k(k), splits,
       relu2, bf16, y, acc_out, ws_slots);
   return hipGetLastError();
@@ -427,8 +454,9 @@ __device__ __forceinline__ void quantize_into_lds(const FusedSeg& sg, int g0, in
   }
 }
 
-template <int M, int WAVES, int PF, bool LONGX>
+template <int M, int WAVES, int PF, int QPL, bool LONGX>
 __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) {
+  constexpr int RPW = 16 * QPL, SUBS = 4 / QPL;     // rows per group, groups per row block
   __shared__ int red[WAVES > 1 ? WAVES - 1 : 1][M][64];
   __shared__ uint32_t red_max[WAVES][M];
   extern __shared__ uint4 xs_lds[];
@@ -439,22 +467,24 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) 
   const FusedSeg& sg = args.seg[si];
   const int local = (int)blockIdx.x - sg.wg_begin;
   const int splits = sg.splits;
-  const int b = local / splits;
-  const int s = local - b * splits;
+  const int bs = local / splits;
+  const int s = local - bs * splits;
+  const int b = bs / SUBS, sub = bs - b * SUBS;
   const int nc = sg.nc;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar control
   const int lane = threadIdx.x & 63;
+  const int r = lane % RPW, q0 = QPL * (lane / RPW);
   const int g0 = (int)((int64_t)s * nc / splits);
   const int g1 = (int)((int64_t)(s + 1) * nc / splits);
   const int c0 = g0 + (int)((int64_t)wave * (g1 - g0) / WAVES);
   const int c1 = g0 + (int)((int64_t)(wave + 1) * (g1 - g0) / WAVES);
-  const uint4* blk =
-      reinterpret_cast<const uint4*>(sg.packed) + (int64_t)b * nc * kBlockU4 + lane;
+  const uint4* blk = reinterpret_cast<const uint4*>(sg.packed) + (int64_t)b * nc * kBlockU4 +
+                     q0 * 64 + sub * RPW + r;
 
   uint4 xraw[M][kXV<64 * WAVES, LONGX>];
   x_load_first<M, 64 * WAVES, LONGX>(sg, g0, xraw);        // activations first (see above)
-  uint4 buf[PF][4];
-  prefetch_first<PF>(buf, blk, c0, c1, g0);
+  uint4 buf[PF][QPL];
+  prefetch_first<PF, QPL>(buf, blk, c0, c1, g0);
   const float g = *sg.gamma;
   int acc[M];
 #pragma unroll
@@ -465,47 +495,59 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) 
   quantize_into_lds<M, WAVES, LONGX>(sg, g0, g1, args.eps, xraw, xs_words, sv, red_max);
   __syncthreads();
   const int span_w = (g1 - g0) * 64;
-  // optional copies of x~ and s (row block 0's groups cover all of K_pad)
-  if (b == 0 && sg.xq_out != nullptr) {
+  // optional copies of x~ and s (the groups of row block 0, sub-block 0
+  // cover all of K_pad)
+  if (b == 0 && sub == 0 && sg.xq_out != nullptr) {
     const int64_t kpad = (int64_t)nc * 256;
     for (int m = 0; m < M; ++m)
       for (int d = threadIdx.x; d < span_w; d += 64 * WAVES)
         reinterpret_cast<uint32_t*>(sg.xq_out + (int64_t)m * kpad + (int64_t)g0 * 256)[d] =
             xs_words[m * span_w + d];
   }
-  if (b == 0 && s == 0 && sg.scale_out != nullptr && threadIdx.x == 0) {
+  if (b == 0 && sub == 0 && s == 0 && sg.scale_out != nullptr && threadIdx.x == 0) {
 #pragma unroll
     for (int m = 0; m < M; ++m) sg.scale_out[m] = sv[m];
   }
 
-  stream_chunks<M, PF>(buf, blk, c0, c1, g0, xs_words, span_w, acc);
+  stream_chunks<M, PF, QPL>(buf, blk, c0, c1, g0, xs_words, span_w, q0, acc);
+  reduce_lane_groups<M, QPL>(acc);
   if (!reduce_waves<M, WAVES>(acc, red, wave, lane)) return;
+  if (lane >= RPW) return;
+  const int rb = sub * RPW + r;                     // row within the 64-row block
   bool own[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) own[m] = true;
-  if (splits > 1) combine_splits<M>(acc, own, sg.slots + (int64_t)b * (M * 64) + lane, splits);
+  if (splits > 1) combine_splits<M>(acc, own, sg.slots + (int64_t)b * (M * 64) + rb, splits);
   float fac[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) fac[m] = gamma_over_s(g, sv[m]);
-  write_rows<M>(acc, own, fac, (int64_t)b * 64 + lane, sg.n, sg.y, sg.acc_out, sg.relu2 != 0,
+  write_rows<M>(acc, own, fac, (int64_t)b * 64 + rb, sg.n, sg.y, sg.acc_out, sg.relu2 != 0,
                 sg.y_bf16 != 0);
 }
 
 }  // namespace
 
 // Plain GEMV: x~ and s given.
-hipError_t launch_gemv(int m, int waves, int pf, const int8_t* xq, const float* scale,
+hipError_t launch_gemv(int m, int waves, int pf, int qpl, const int8_t* xq, const float* scale,
                        const uint32_t* packed, const float* gamma, int64_t n, int64_t k,
                        int splits, bool relu2, bool bf16, void* y, int32_t* acc_out,
                        int64_t* ws_slots, hipStream_t stream) {
-#define BL_GEMV(MM, WW, PP)                                                                   \
-  return run_gemv<MM, WW, PP>(xq, scale, packed, gamma, n, k, splits, relu2, bf16, y, acc_out, \
-                              ws_slots, stream)
-#define BL_GEMV_W(MM)                                  \
-  if (waves == 8) {                                    \
-    if (pf == 2) BL_GEMV(MM, 8, 2); else BL_GEMV(MM, 8, 1); \
-  } else {                                             \
-    if (pf == 2) BL_GEMV(MM, 4, 2); else BL_GEMV(MM, 4, 1); \
+#define BL_GEMV(MM, WW, PP, QQ)                                                                 \
+  return run_gemv<MM, WW, PP, QQ>(xq, scale, packed, gamma, n, k, splits, relu2, bf16, y,       \
+                                  acc_out, ws_slots, stream)
+  // 64 rows per group (qpl 4): 1 or 2 super-chunks in flight per wave;
+  // 16 rows (qpl 1, a quarter of the bytes per super-chunk): 4 or 8
+#define BL_GEMV_W(MM)                                                   \
+  if (qpl == 1) {                                                       \
+    if (waves == 8) {                                                   \
+      if (pf >= 8) { BL_GEMV(MM, 8, 8, 1); } else { BL_GEMV(MM, 8, 4, 1); } \
+    } else {                                                            \
+      if (pf >= 8) { BL_GEMV(MM, 4, 8, 1); } else { BL_GEMV(MM, 4, 4, 1); } \
+    }                                                                   \
+  } else if (waves == 8) {                                              \
+    if (pf == 2) { BL_GEMV(MM, 8, 2, 4); } else { BL_GEMV(MM, 8, 1, 4); } \
+  } else {                                                              \
+    if (pf == 2) { BL_GEMV(MM, 4, 2, 4); } else { BL_GEMV(MM, 4, 1, 4); } \
   }
   switch (m) {
     case 1: BL_GEMV_W(1);
@@ -521,18 +563,25 @@ hipError_t launch_gemv(int m, int waves, int pf, const int8_t* xq, const float* 
 // Fused decode step over a complete segment table (wg_begin, splits and
 // workspace pointers filled in).  long_rows: one token and some row longer
 // than 1024 16-byte units.
-hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, bool long_rows, int groups,
-                             size_t lds, hipStream_t stream) {
-#define BL_FUSED(MM, WW, LL)                                                             \
-  do {                                                                                   \
-    gemv_fused_kernel<MM, WW, 2, LL><<<(unsigned)groups, 64 * WW, lds, stream>>>(args); \
-    return hipGetLastError();                                                            \
+hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, int qpl, bool long_rows,
+                             int groups, size_t lds, hipStream_t stream) {
+#define BL_FUSED(MM, WW, QQ, LL)                                                       \
+  do {                                                                                 \
+    gemv_fused_kernel<MM, WW, (QQ == 1 ? 4 : 2), QQ, LL>                               \
+        <<<(unsigned)groups, 64 * WW, lds, stream>>>(args);                            \
+    return hipGetLastError();                                                          \
   } while (0)
-#define BL_FUSED_W(MM, LL) \
-  if (waves == 4)          \
-    BL_FUSED(MM, 4, LL);   \
-  else                     \
-    BL_FUSED(MM, 8, LL)
+#define BL_FUSED_Q(MM, WW, LL) \
+  if (qpl == 1)                \
+    BL_FUSED(MM, WW, 1, LL);   \
+  else                         \
+    BL_FUSED(MM, WW, 4, LL)
+#define BL_FUSED_W(MM, LL)   \
+  if (waves == 4) {          \
+    BL_FUSED_Q(MM, 4, LL);   \
+  } else {                   \
+    BL_FUSED_Q(MM, 8, LL);   \
+  }
   switch (m) {
     case 1:
       if (long_rows) {
@@ -545,6 +594,7 @@ hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, bool long_
     default: return hipErrorInvalidValue;
   }
 #undef BL_FUSED_W
+#undef BL_FUSED_Q
 #undef BL_FUSED
 }
 
