@@ -26,7 +26,9 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t words) {
   for (; i < words; i += stride) p[i] = 0u;
 }
 
-constexpr int64_t kGemvMaxM = 4;
+constexpr int64_t kGemvMaxM = 2;           // dot4 GEMV up to here
+constexpr int64_t kMfmaGemvMaxM = 16;      // MFMA GEMV up to here (one 16-column tile)
+constexpr int64_t kMfmaGemvMaxLds = 64 * 1024;
 constexpr int64_t kGemvTargetGroups = 512;
 constexpr int64_t kGemvMaxLds = 48 * 1024;
 constexpr int64_t kGemmTargetGroups = 512;
@@ -78,6 +80,22 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     }
     p.splits = (int)s;
     p.slots = s > 1 ? (size_t)(nb * m * 64) : 0;
+  } else if (m <= kMfmaGemvMaxM && (m <= 8 || nb < 256)) {
+    // MFMA GEMV: the tokens are the columns of one 16 x 16 x 64 product,
+    // the unpacked weights its rows; x~ of the workgroup's range of
+    // super-chunks is staged once in LDS (split K over the fewest
+    // workgroups that keep it within 64 KiB).  Up to 8 tokens at every
+    // size; 9 to 16 only while the row blocks are too few for the GEMM's
+    // 256-row tiles to fill the chip.  Two 64-row groups per workgroup once
+    // there are >= 256 row blocks and >= 8 tokens, else one 32-row group
+    // of 8 waves splitting the range.  (Tuned on MI355X over the 2B- and
+    // 100B-class decode shapes.)
+    p.kind = 2;
+    int64_t s = 1;
+    while (m * cdiv(nc, s) * 256 > kMfmaGemvMaxLds) ++s;
+    p.variant = m >= 8 && nb >= 256 ? 1 : 0;
+    p.splits = (int)s;
+    p.slots = s > 1 ? (size_t)(nb * m * 64) : 0;
   } else {
     // MFMA GEMM.  Small batches (M <= 64) take the 16-row-multiple tiles;
     // larger ones the wide-wave tiles, the largest of 128 x 512, 64 x 512,
@@ -122,6 +140,9 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
   if (plan.kind == 0)
     return launch_gemv((int)m, plan.variant, plan.pf, plan.qpl, xq, scale, packed, gamma, n, k,
                        plan.splits, relu2, bf16, y, acc_out, slots, stream);
+  if (plan.kind == 2)
+    return launch_gemv_mfma(plan.variant, xq, scale, packed, gamma, m, n, k, plan.splits, relu2,
+                            bf16, y, acc_out, slots, stream);
   return launch_gemm(plan.variant, xq, scale, packed, gamma, m, n, k, plan.splits, relu2, bf16,
                      y, acc_out, slots, stream);
 }

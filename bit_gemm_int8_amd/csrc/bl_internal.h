@@ -25,8 +25,8 @@ hipError_t launch_pack(const void* w, bool bf16, int64_t n, int64_t k, float eps
 
 // Forward: dispatch plan shared by the workspace query and the launch.
 struct FwdPlan {
-  int kind;            // 0 = dot4 GEMV, 1 = MFMA GEMM
-  int variant;         // GEMV: waves per workgroup; GEMM: tile variant
+  int kind;            // 0 = dot4 GEMV, 1 = MFMA GEMM, 2 = MFMA GEMV
+  int variant;         // dot4 GEMV: waves per workgroup; otherwise the kernel variant
   int pf;              // GEMV: super-chunks in flight per wave
   int qpl;             // GEMV: 16-byte q-parts per lane (4: 64 rows per group, 1: 16 rows)
   int splits;          // split-K factor
@@ -60,6 +60,10 @@ struct FusedArgs {
   int nseg;
   float eps;
 };
+hipError_t launch_gemv_mfma(int variant, const int8_t* xq, const float* scale,
+                            const uint32_t* packed, const float* gamma, int64_t m, int64_t n,
+                            int64_t k, int splits, bool relu2, bool bf16, void* y,
+                            int32_t* acc_out, int64_t* ws_slots, hipStream_t stream);
 hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, int qpl, bool long_rows,
                              int groups, size_t lds, hipStream_t stream);
 

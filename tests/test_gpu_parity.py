@@ -162,6 +162,15 @@ FWD_CASES = [
     (1, 20000, 512, False, "bf16", "bf16"),
     (5, 200, 600, False, "f32", "f32"),
     (16, 256, 512, True, "bf16", "bf16"),
+    # MFMA GEMV (3 to 16 tokens): one 32-row group per workgroup ...
+    (8, 2560, 16384, False, "bf16", "bf16"),     # K split over 3 (uneven ranges)
+    (12, 1000, 3000, True, "f32", "bf16"),       # ragged row block, vector stores
+    (7, 1001, 2560, False, "bf16", "f32"),       # odd N: element stores
+    (16, 2048, 8192, True, "bf16", "bf16"),      # 16 tokens, K split over 2
+    # ... two 64-row groups per workgroup (>= 256 row blocks, >= 8 tokens)
+    (10, 16448, 768, False, "f32", "bf16"),      # 257 blocks: an idle last group
+    (9, 16450, 1024, True, "bf16", "bf16"),      # odd N, element stores
+    (8, 16384, 9000, False, "bf16", "bf16"),     # K split over 2, ragged K
     (17, 300, 1000, False, "f32", "bf16"),
     (32, 640, 2560, False, "bf16", "bf16"),
     (33, 100, 257, True, "f32", "f32"),
@@ -240,13 +249,13 @@ def test_forward_extreme_accumulator(B):
 
 def test_forward_deterministic_and_workspace_clean(B):
     import torch
-    # long rows (64 super-chunks): the GEMV splits K over workgroups
-    w, x = random_case(9, 4, 2560, 16384)
+    # long rows (64 super-chunks): the MFMA GEMV splits K over workgroups
+    w, x = random_case(9, 8, 2560, 16384)
     packed, gamma = B.pack_weights(dev(w))
     xq, s = B.quant_act(dev(x))
     ws = B.Workspace()
     outs = [host(B.forward(xq, s, packed, gamma, 2560, 16384, workspace=ws)) for _ in range(3)]
-    assert B.forward_workspace_bytes(4, 2560, 16384) > 0
+    assert B.forward_workspace_bytes(8, 2560, 16384) > 0
     np.testing.assert_array_equal(outs[0], outs[1])
     np.testing.assert_array_equal(outs[0], outs[2])
     torch.cuda.synchronize()
@@ -257,12 +266,12 @@ def test_forward_deterministic_and_workspace_clean(B):
 
 
 def test_workspace_shared_across_paths(B):
-    # split-K GEMM and split-K GEMV calls alternate on one workspace; every
-    # call must find it zero-filled and leave it so.
+    # split-K GEMM, MFMA GEMV and dot4 GEMV calls alternate on one
+    # workspace; every call must find it zero-filled and leave it so.
     import torch
     ws = B.Workspace()
-    cases = [(16, 256, 8192), (1, 64, 16384), (40, 300, 4096), (3, 64, 12288), (1, 200, 16384),
-             (16, 256, 8192)]
+    cases = [(16, 256, 8192), (1, 64, 16384), (40, 300, 4096), (3, 64, 30000), (2, 64, 16384),
+             (1, 200, 16384), (20, 256, 8192), (16, 256, 8192)]
     for (m, n, k) in cases:
         assert B.forward_workspace_bytes(m, n, k) > 0, (m, n, k)
         w, x = random_case(m * 7 + n + k, m, n, k, x_kind="t3")
