@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "libbitlinear.so")
-SOURCES = ["api.hip", "quant_act.hip", "pack.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quant_act.hip", "pack.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

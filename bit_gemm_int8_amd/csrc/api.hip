@@ -27,13 +27,12 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t words) {
 }
 
 constexpr int64_t kGemvMaxM = 2;           // dot4 GEMV up to here
-constexpr int64_t kMfmaGemvMaxM = 16;      // MFMA GEMV up to here (one 16-column tile)
-constexpr int64_t kMfmaGemvMaxLds = 64 * 1024;
+constexpr int64_t kMfmaGemvMaxM = 64;      // windowed MFMA GEMV up to here (4 token groups)
 constexpr int64_t kGemvTargetGroups = 512;
 constexpr int64_t kGemvMaxLds = 48 * 1024;
 constexpr int64_t kGemmTargetGroups = 512;
 constexpr int64_t kGemmFullTiles = 192;   // 3/4 of the 256 CUs
-constexpr int64_t kGemmWideTiles = 150;
+constexpr int64_t kCUs = 256;
 
 }  // namespace
 
@@ -80,49 +79,48 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     }
     p.splits = (int)s;
     p.slots = s > 1 ? (size_t)(nb * m * 64) : 0;
-  } else if (m <= kMfmaGemvMaxM && (m <= 8 || nb < 256)) {
-    // MFMA GEMV: the tokens are the columns of one 16 x 16 x 64 product,
-    // the unpacked weights its rows; x~ of the workgroup's range of
-    // super-chunks is staged once in LDS (split K over the fewest
-    // workgroups that keep it within 64 KiB).  Up to 8 tokens at every
-    // size; 9 to 16 only while the row blocks are too few for the GEMM's
-    // 256-row tiles to fill the chip.  Two 64-row groups per workgroup once
-    // there are >= 256 row blocks and >= 8 tokens, else one 32-row group
-    // of 8 waves splitting the range.  (Tuned on MI355X over the 2B- and
+  } else if (m <= kMfmaGemvMaxM) {
+    // Windowed MFMA GEMV: 16, 32 or 64 token columns.  Many row blocks
+    // (>= 256): wide row groups, the whole K per wave; fewer: slices of K
+    // over the waves of a workgroup, 8 slices for few (<= 64) long (>= 24
+    // super-chunks) rows at 16 tokens.  (Tuned on MI355X over the 2B- and
     // 100B-class decode shapes.)
     p.kind = 2;
-    int64_t s = 1;
-    while (m * cdiv(nc, s) * 256 > kMfmaGemvMaxLds) ++s;
-    p.variant = m >= 8 && nb >= 256 ? 1 : 0;
-    p.splits = (int)s;
-    p.slots = s > 1 ? (size_t)(nb * m * 64) : 0;
+    const bool wide = nb >= 256;
+    if (m <= 16) p.variant = wide ? 2 : (nb <= 64 && nc >= 24) ? 1 : 0;
+    else if (m <= 32) p.variant = wide ? 4 : 3;
+    else p.variant = wide ? 6 : 5;
+    p.splits = 1;
+    p.slots = 0;
   } else {
-    // MFMA GEMM.  Small batches (M <= 64) take the 16-row-multiple tiles;
-    // larger ones the wide-wave tiles, the largest of 128 x 512, 64 x 512,
-    // 64 x 256 that still yields >= 150 tiles (~0.6 per CU), else 64 x 256.
+    // MFMA GEMM, wide waves.  The tile shape maximises the work the first
+    // rounds of tiles over the 256 CUs keep busy, weighted by how well each
+    // shape runs (128 x 512 best, 64 x 512 then 64 x 256 and 96 x 256).
     // Split-K (one atomic combine per output) only when the tiles leave most
     // CUs idle.  (Tuned on MI355X over the 2048- and 512-token prefills.)
     p.kind = 1;
-    auto tiles_of = [&](int variant) {
+    static const double kRate[4] = {1.0, 0.9, 0.85, 0.85};
+    double best = -1.0;
+    for (int v = 0; v < 4; ++v) {
       int bm, bn;
-      gemm_tile_shape(variant, &bm, &bn);
-      return cdiv(m, bm) * cdiv(nb * 64, bn);
-    };
-    if (m <= 16) p.variant = 0;
-    else if (m <= 32) p.variant = 1;
-    else if (m <= 64) p.variant = 2;
-    else if (tiles_of(5) >= kGemmWideTiles) p.variant = 5;
-    else if (tiles_of(6) >= kGemmWideTiles) p.variant = 6;
-    else p.variant = 7;
+      gemm_tile_shape(v, &bm, &bn);
+      const int64_t tiles = cdiv(m, bm) * cdiv(nb * 64, bn);
+      const double useful = (double)m * (double)(nb * 64) / ((double)bm * bn);
+      const double score = kRate[v] * useful / (double)(cdiv(tiles, kCUs) * kCUs);
+      if (score > best) {
+        best = score;
+        p.variant = v;
+      }
+    }
     int bm, bn;
     gemm_tile_shape(p.variant, &bm, &bn);
-    const int64_t tiles = tiles_of(p.variant);
+    const int64_t tiles = cdiv(m, bm) * cdiv(nb * 64, bn);
     int64_t s = 1;
-    if (m <= 64 || tiles < kGemmFullTiles / 4) {
+    if (tiles < kGemmFullTiles / 4) {
       s = cdiv(kGemmTargetGroups, tiles);
       int64_t smax = nc / 2 > 1 ? nc / 2 : 1;
       if (s > smax) s = smax;
-      if (m > 64 && s > 4) s = 4;
+      if (s > 4) s = 4;
       if (s < 1) s = 1;
     }
     p.splits = (int)s;
@@ -141,8 +139,8 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
     return launch_gemv((int)m, plan.variant, plan.pf, plan.qpl, xq, scale, packed, gamma, n, k,
                        plan.splits, relu2, bf16, y, acc_out, slots, stream);
   if (plan.kind == 2)
-    return launch_gemv_mfma(plan.variant, xq, scale, packed, gamma, m, n, k, plan.splits, relu2,
-                            bf16, y, acc_out, slots, stream);
+    return launch_gemv_mfma(plan.variant, xq, scale, packed, gamma, m, n, k, relu2, bf16, y,
+                            acc_out, stream);
   return launch_gemm(plan.variant, xq, scale, packed, gamma, m, n, k, plan.splits, relu2, bf16,
                      y, acc_out, slots, stream);
 }

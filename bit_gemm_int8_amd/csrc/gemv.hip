@@ -525,214 +525,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) 
                 sg.y_bf16 != 0);
 }
 
-// ------------------------------------------------------------ MFMA GEMV --
-// Decode products for up to 16 tokens on v_mfma_i32_16x16x64_i8: the
-// unpacked weights of 16 rows are the first operand (lane l = r + 16 g
-// supplies row r, inputs 16 g .. 16 g + 15 of a 64-input step: packed word
-// (q = g, j) of row r, i.e. the lane's one 16-byte load per super-chunk
-// holds its four steps j), and x~ of the tokens the second (lane l supplies
-// token n = l % 16, the same 16 inputs; lanes of tokens >= m read a zero
-// slot).  The 16 x 16 result holds row 4 g + i, token n in element i of lane
-// l.  The unpack is the only VALU work per weight; the matrix core does the
-// multiply-adds for all tokens at once.
-// A workgroup stages x~ of every token for its range of super-chunks once
-// in LDS (behind a 16-byte zero slot at offset 0) and has WR x WK waves: WR
-// groups of WK waves, each group owning SB 16-row sub-blocks (one 64-row
-// packed block at SB = 4), the WK waves of a group splitting the range and
-// adding up in LDS.  Several row groups per workgroup share one staging of
-// x~, which would otherwise be read once per 16 to 64 rows.
-template <int WR, int WK, int PF, int SB>
-__global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_kernel(
-    const int8_t* __restrict__ xq, const float* __restrict__ scale,
-    const uint4* __restrict__ packed, const float* __restrict__ gamma, int m, int n, int nb,
-    int nc, int64_t kpad, int splits, int relu2, int bf16, int vec_out, void* __restrict__ y,
-    int32_t* __restrict__ acc_out, int64_t* __restrict__ ws_slots) {
-  static_assert(SB == 1 || SB == 2 || SB == 4, "a wave's sub-blocks lie in one packed block");
-  constexpr int WAVES = WR * WK;
-  __shared__ int red[WK > 1 ? (WK - 1) * WR : 1][SB][4][64];
-  __shared__ float fac_lds[16];
-  extern __shared__ uint4 xs_lds[];                 // [0]: zero slot, then x~ per token
-  const int bs = blockIdx.x / splits;
-  const int s = blockIdx.x - bs * splits;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wr = wave / WK, wk = wave - wr * WK;
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15, g = lane >> 4;
-  // the group's first sub-block; groups past the last row compute a copy of
-  // the last sub-blocks (loads stay in bounds) and store nothing
-  int u0 = (bs * WR + wr) * SB;
-  const bool live = u0 < nb * 4;
-  if (!live) u0 = nb * 4 - SB;
-  const int b = u0 >> 2, sub0 = u0 & 3;
-  const int g0 = (int)((int64_t)s * nc / splits);
-  const int g1 = (int)((int64_t)(s + 1) * nc / splits);
-  const int c0 = g0 + (int)((int64_t)wk * (g1 - g0) / WK);
-  const int c1 = g0 + (int)((int64_t)(wk + 1) * (g1 - g0) / WK);
-  const uint4* blk = packed + (int64_t)b * nc * kBlockU4 + g * 64 + sub0 * 16 + r;
-
-  // x~[t][256*g0 .. 256*g1) for the m tokens into LDS after the zero slot;
-  // the first units are loaded ahead of the weights (see gemv_kernel)
-  constexpr int NT = 64 * WAVES;
-  const int span = (g1 - g0) * 16;                  // uint4 per token
-  const int units = span * m;
-  auto x_unit = [&](int u) {
-    const int t = u / span, v = u - t * span;
-    return reinterpret_cast<const uint4*>(xq + (int64_t)t * kpad + (int64_t)g0 * 256)[v];
-  };
-  constexpr int XR = kXR<WAVES>;
-  uint4 xr[XR];
-  int xu[XR];
-#pragma unroll
-  for (int q = 0; q < XR; ++q) {
-    xu[q] = ((int)threadIdx.x + NT * q) % units;
-    xr[q] = x_unit(xu[q]);
-  }
-  uint4 buf[PF][SB];
-  {
-    const int last = c1 > c0 ? c1 - 1 : g0;
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int c = c0 + p < c1 ? c0 + p : last;
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) buf[p][sb] = blk[(int64_t)c * kBlockU4 + sb * 16];
-    }
-  }
-  const float gam = *gamma;
-  if (threadIdx.x < 16)
-    fac_lds[threadIdx.x] = (int)threadIdx.x < m ? gamma_over_s(gam, scale[threadIdx.x]) : 0.0f;
-#pragma unroll
-  for (int q = 0; q < XR; ++q) xs_lds[1 + xu[q]] = xr[q];
-  for (int u = threadIdx.x + NT * XR; u < units; u += NT) xs_lds[1 + u] = x_unit(u);
-  if (threadIdx.x == 0) xs_lds[0] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
-
-  // this lane's x~ column: token r (or the zero slot), k-group g
-  const uint32_t xmask = r < m ? 0xFFFFFFFFu : 0u;
-  const uint32_t xbase = 16u + (uint32_t)(r * span) * 16u + (uint32_t)g * 16u;
-  const uint8_t* xl = reinterpret_cast<const uint8_t*>(xs_lds);
-  bl_v4i acc[SB];
-#pragma unroll
-  for (int sb = 0; sb < SB; ++sb) acc[sb] = bl_v4i{0, 0, 0, 0};
-  auto chunk = [&](const uint4 (&w)[SB], int c) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t off = (xbase + (uint32_t)(c - g0) * 256u + (uint32_t)j * 64u) & xmask;
-      const bl_v4i xv = *reinterpret_cast<const bl_v4i*>(xl + off);
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb) {
-        const uint32_t wj = j == 0 ? w[sb].x : j == 1 ? w[sb].y : j == 2 ? w[sb].z : w[sb].w;
-        const bl_v4i a = {(int)unpack_x64(wj, 0), (int)unpack_x64(wj, 1), (int)unpack_x64(wj, 2),
-                          (int)unpack_x64(wj, 3)};
-        acc[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xv, acc[sb], 0, 0, 0);
-      }
-    }
-  };
-  // stream: steady state without conditional loads, then the drain
-  int c = c0;
-  for (; c + 2 * PF <= c1; c += PF) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      chunk(buf[p], c + p);
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb)
-        buf[p][sb] = blk[(int64_t)(c + p + PF) * kBlockU4 + sb * 16];
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < PF; ++p) {
-    if (c + p < c1) {
-      chunk(buf[p], c + p);
-      if (c + p + PF < c1) {
-#pragma unroll
-        for (int sb = 0; sb < SB; ++sb)
-          buf[p][sb] = blk[(int64_t)(c + p + PF) * kBlockU4 + sb * 16];
-      }
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (c + PF + p < c1) chunk(buf[p], c + PF + p);
-
-  // the group's sums into its first wave
-  if (WK > 1) {
-    if (wk > 0) {
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wr * (WK - 1) + wk - 1][sb][i][lane] = acc[sb][i];
-    }
-    __syncthreads();
-    if (wk > 0) return;
-#pragma unroll
-    for (int w = 0; w < WK - 1; ++w)
-#pragma unroll
-      for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[sb][i] += red[wr * (WK - 1) + w][sb][i][lane];
-  }
-  // lane (token r, group g) holds rows 4g..4g+3 of each sub-block for token r
-  if (!live || r >= m) return;
-  const float f = fac_lds[r];
-#pragma unroll
-  for (int sb = 0; sb < SB; ++sb) {
-    const int rb = (sub0 + sb) * 16 + 4 * g;        // first of 4 rows within the block
-    int v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = acc[sb][i];
-    if (splits > 1) {
-      int64_t* slot = ws_slots + (int64_t)b * (m * 64) + r * 64 + rb;
-      int64_t old[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) old[i] = split_add(slot + i, v[i]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = split_finish(slot + i, old[i], v[i], splits);
-    }
-    const int row0 = b * 64 + rb;
-    const int64_t idx = (int64_t)r * n + row0;
-    if (splits == 1 && vec_out && row0 + 3 < n) {
-      float o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[i] = (float)(v[i] >> 6) * f;
-        if (relu2) o[i] = o[i] > 0.0f ? o[i] * o[i] : 0.0f;
-      }
-      if (acc_out != nullptr)
-        *reinterpret_cast<int4*>(acc_out + idx) = make_int4(v[0] >> 6, v[1] >> 6, v[2] >> 6, v[3] >> 6);
-      if (bf16)
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + idx) =
-            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-      else
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + idx) =
-            make_float4(o[0], o[1], o[2], o[3]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (row0 + i >= n || (v[i] & 63) != 0) continue;
-        const int a = v[i] >> 6;
-        if (acc_out != nullptr) acc_out[idx + i] = a;
-        store_out(y, idx + i, a, f, relu2 != 0, bf16 != 0);
-      }
-    }
-  }
-}
-
-template <int WR, int WK, int PF, int SB>
-hipError_t run_gemv_mfma(const int8_t* xq, const float* scale, const uint32_t* packed,
-                         const float* gamma, int64_t m, int64_t n, int64_t k, int splits,
-                         bool relu2, bool bf16, void* y, int32_t* acc_out, int64_t* ws_slots,
-                         hipStream_t stream) {
-  const int nb = (int)cdiv(n, kRowBlock);
-  const int nc = (int)cdiv(k, kSuperK);
-  dim3 grid((unsigned)(cdiv((int64_t)nb * 4, WR * SB) * splits)), block(64 * WR * WK);
-  const size_t lds = 16 + (size_t)m * cdiv(nc, splits) * 256;
-  const int vec_out = n % 4 == 0 && (uintptr_t)y % (bf16 ? 8 : 16) == 0 &&
-                      (acc_out == nullptr || (uintptr_t)acc_out % 16 == 0);
-  gemv_mfma_kernel<WR, WK, PF, SB><<<grid, block, lds, stream>>>(
-      xq, scale, reinterpret_cast<const uint4*>(packed), gamma, (int)m, (int)n, nb, nc,
-      padded_k(k), splits, relu2, bf16, vec_out, y, acc_out, ws_slots);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 // Plain GEMV: x~ and s given.
@@ -764,22 +556,6 @@ hipError_t launch_gemv(int m, int waves, int pf, int qpl, const int8_t* xq, cons
   }
 #undef BL_GEMV_W
 #undef BL_GEMV
-}
-
-// MFMA GEMV, 1 to 16 tokens: variant 0 = one 32-row group of 8 waves
-// splitting the range, variant 1 = two 64-row groups of 4 waves each.
-hipError_t launch_gemv_mfma(int variant, const int8_t* xq, const float* scale,
-                            const uint32_t* packed, const float* gamma, int64_t m, int64_t n,
-                            int64_t k, int splits, bool relu2, bool bf16, void* y,
-                            int32_t* acc_out, int64_t* ws_slots, hipStream_t stream) {
-  if (m < 1 || m > 16) return hipErrorInvalidValue;
-  if (variant == 0)
-    return run_gemv_mfma<1, 8, 2, 2>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y,
-                                     acc_out, ws_slots, stream);
-  if (variant == 1)
-    return run_gemv_mfma<2, 4, 2, 4>(xq, scale, packed, gamma, m, n, k, splits, relu2, bf16, y,
-                                     acc_out, ws_slots, stream);
-  return hipErrorInvalidValue;
 }
 
 // Fused decode step over a complete segment table (wg_begin, splits and

@@ -148,43 +148,53 @@ def test_pack_degenerate(B):
 # ---------------------------------------------------------------- forward --
 FWD_CASES = [
     # m, n, k, relu2, y dtype, x dtype
+    # dot4 GEMV (1 and 2 tokens)
     (1, 1, 1, False, "f32", "f32"),
     (1, 256, 256, False, "f32", "f32"),
     (1, 100, 272, True, "bf16", "bf16"),
     (2, 640, 2560, False, "bf16", "bf16"),
-    (3, 130, 520, True, "f32", "f32"),
-    (4, 300, 1000, False, "f32", "bf16"),
     (1, 64, 8192, False, "f32", "bf16"),
     (1, 200, 16384, True, "bf16", "bf16"),
+    (1, 20000, 512, False, "bf16", "bf16"),
+    (2, 300, 40000, True, "f32", "bf16"),        # split K
+    # windowed MFMA GEMV, 3 to 16 tokens: 2 row groups x 4 slices
+    (3, 130, 520, True, "f32", "f32"),           # 3 super-chunks: an empty slice
+    (4, 300, 1000, False, "f32", "bf16"),
+    (5, 200, 600, False, "f32", "f32"),
+    (16, 256, 512, True, "bf16", "bf16"),
+    (12, 1000, 3000, True, "f32", "bf16"),       # ragged row block, vector stores
+    (7, 1001, 2560, False, "bf16", "f32"),       # odd N: element stores
+    # ... 8 slices (few long rows)
     (4, 100, 30000, False, "f32", "f32"),
     (3, 130, 40000, False, "bf16", "bf16"),
     (4, 70, 65536, False, "f32", "bf16"),
-    (1, 20000, 512, False, "bf16", "bf16"),
-    (5, 200, 600, False, "f32", "f32"),
-    (16, 256, 512, True, "bf16", "bf16"),
-    # MFMA GEMV (3 to 16 tokens): one 32-row group per workgroup ...
-    (8, 2560, 16384, False, "bf16", "bf16"),     # K split over 3 (uneven ranges)
-    (12, 1000, 3000, True, "f32", "bf16"),       # ragged row block, vector stores
-    (7, 1001, 2560, False, "bf16", "f32"),       # odd N: element stores
-    (16, 2048, 8192, True, "bf16", "bf16"),      # 16 tokens, K split over 2
-    # ... two 64-row groups per workgroup (>= 256 row blocks, >= 8 tokens)
-    (10, 16448, 768, False, "f32", "bf16"),      # 257 blocks: an idle last group
-    (9, 16450, 1024, True, "bf16", "bf16"),      # odd N, element stores
-    (8, 16384, 9000, False, "bf16", "bf16"),     # K split over 2, ragged K
+    (8, 2560, 16384, False, "bf16", "bf16"),
+    (16, 2048, 8192, True, "bf16", "bf16"),
+    # ... wide row groups (>= 256 row blocks), whole K per wave
+    (10, 16448, 768, False, "f32", "bf16"),      # 257 blocks: idle groups
+    (9, 16450, 1024, True, "bf16", "bf16"),      # odd N: element stores
+    (8, 16384, 9000, False, "bf16", "bf16"),     # ragged K
+    # ... 17 to 32 tokens (2 token groups)
     (17, 300, 1000, False, "f32", "bf16"),
     (32, 640, 2560, False, "bf16", "bf16"),
+    (24, 16448, 1000, True, "bf16", "bf16"),     # wide row groups
+    # ... 33 to 64 tokens (4 token groups)
     (33, 100, 257, True, "f32", "f32"),
     (64, 512, 2560, False, "bf16", "bf16"),
-    (65, 129, 300, False, "f32", "f32"),
-    (130, 320, 1024, True, "bf16", "bf16"),      # 64 x 256 wide tiles, split-K
+    (50, 16400, 700, False, "f32", "bf16"),      # wide row groups
+    (64, 16385, 512, True, "bf16", "f32"),       # wide, odd N
+    # wide-wave MFMA GEMM (more than 64 tokens)
+    (65, 129, 300, False, "f32", "f32"),         # 64 x 256 tiles
+    (130, 320, 1024, True, "bf16", "bf16"),      # 64 x 256, split-K over 2
     (129, 260, 5000, True, "f32", "bf16"),       # 64 x 256, split-K over 4, ragged M
     (256, 384, 768, False, "f32", "bf16"),
     (200, 1001, 700, False, "bf16", "f32"),      # 64 x 256, odd N: element stores
     (1000, 6100, 300, True, "bf16", "bf16"),     # 64 x 512 tiles, ragged M, N, K
     (1024, 6144, 512, False, "f32", "bf16"),     # 64 x 512, vector stores
     (256, 8192, 768, False, "bf16", "f32"),      # 64 x 256
-    (1100, 9001, 300, True, "bf16", "bf16"),     # 128 x 512 tiles, ragged M, odd N
-    (1030, 9216, 256, False, "f32", "f32"),      # 128 x 512, vector stores
+    (1100, 9001, 300, True, "bf16", "bf16"),     # 64 x 256, ragged M, odd N
+    (1536, 10240, 300, True, "bf16", "bf16"),    # 128 x 512 tiles
+    (2000, 2560, 320, False, "bf16", "bf16"),    # 96 x 256 tiles, ragged M
 ]
 
 
@@ -249,13 +259,13 @@ def test_forward_extreme_accumulator(B):
 
 def test_forward_deterministic_and_workspace_clean(B):
     import torch
-    # long rows (64 super-chunks): the MFMA GEMV splits K over workgroups
-    w, x = random_case(9, 8, 2560, 16384)
+    # long rows (64 super-chunks): the dot4 GEMV splits K over workgroups
+    w, x = random_case(9, 2, 2560, 16384)
     packed, gamma = B.pack_weights(dev(w))
     xq, s = B.quant_act(dev(x))
     ws = B.Workspace()
     outs = [host(B.forward(xq, s, packed, gamma, 2560, 16384, workspace=ws)) for _ in range(3)]
-    assert B.forward_workspace_bytes(8, 2560, 16384) > 0
+    assert B.forward_workspace_bytes(2, 2560, 16384) > 0
     np.testing.assert_array_equal(outs[0], outs[1])
     np.testing.assert_array_equal(outs[0], outs[2])
     torch.cuda.synchronize()
@@ -266,12 +276,12 @@ def test_forward_deterministic_and_workspace_clean(B):
 
 
 def test_workspace_shared_across_paths(B):
-    # split-K GEMM, MFMA GEMV and dot4 GEMV calls alternate on one
-    # workspace; every call must find it zero-filled and leave it so.
+    # split-K GEMM and split-K GEMV calls alternate on one workspace; every
+    # call must find it zero-filled and leave it so.
     import torch
     ws = B.Workspace()
-    cases = [(16, 256, 8192), (1, 64, 16384), (40, 300, 4096), (3, 64, 30000), (2, 64, 16384),
-             (1, 200, 16384), (20, 256, 8192), (16, 256, 8192)]
+    cases = [(100, 256, 8192), (1, 64, 16384), (130, 300, 4096), (2, 64, 16384),
+             (1, 200, 16384), (70, 129, 5000), (100, 256, 8192)]
     for (m, n, k) in cases:
         assert B.forward_workspace_bytes(m, n, k) > 0, (m, n, k)
         w, x = random_case(m * 7 + n + k, m, n, k, x_kind="t3")
