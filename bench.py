@@ -25,8 +25,10 @@ Also reported on the same line:
                 the same step unfused and each matrix's plain GEMV;
   prefill       2048-token prefill GEMMs (2048x2560 -> 6912 with ReLU^2, and
                 2048x6912 -> 2560): 2*M*N*K / kernel time, in TOPS;
-  decode_100b   batch-1 GEMV at 100B-class shapes (up 28672x8192, down
-                8192x28672), weights rotated past the caches, GB/s;
+  c5            one 100B-class layer (q,o 8192x8192; k,v 1024x8192; up
+                28672x8192; down 8192x28672) at 1, 16 and 512 tokens,
+                weights rotated past the caches: each matrix alone (GB/s,
+                TOPS) and the whole layer with its activation quants;
   stack_c3      the 2B-class set as a 30-layer stack (388 MB packed), one
                 pass in layer order at 1/8/32/64 tokens: us per pass;
   cpu_baseline  the CPU oracle (numpy) on a bounded sample of the same step.
@@ -66,18 +68,22 @@ def quant_bytes(m, k):
 class DecodeSet:
     """Packed weights (several copies), inputs and outputs of one matrix set."""
 
-    def __init__(self, B, torch, wl, m, copies, names=None):
+    def __init__(self, B, torch, wl, m, copies, names=None, mats=None):
         import datagen
         self.B, self.torch, self.m = B, torch, m
         self.names = names or list(wl.matrices.keys())
-        self.mats = {}
-        for name in self.names:
-            n, k, relu2, group = wl.matrices[name]
-            w = torch.from_numpy(datagen.workload_weights(wl, name)).cuda()
-            packed, gamma = B.pack_weights(w)
-            del w
-            cps = [packed] + [packed.clone() for _ in range(copies - 1)]
-            self.mats[name] = dict(n=n, k=k, relu2=relu2, group=group, packed=cps, gamma=gamma)
+        if mats is not None:               # the packed copies of another set
+            self.mats = mats
+        else:
+            self.mats = {}
+            for name in self.names:
+                n, k, relu2, group = wl.matrices[name]
+                w = torch.from_numpy(datagen.workload_weights(wl, name)).cuda()
+                packed, gamma = B.pack_weights(w)
+                del w
+                cps = [packed] + [packed.clone() for _ in range(copies - 1)]
+                self.mats[name] = dict(n=n, k=k, relu2=relu2, group=group, packed=cps,
+                                       gamma=gamma)
         self.groups = []
         for name in self.names:
             g = self.mats[name]["group"]
@@ -279,30 +285,56 @@ def run_prefill(B, torch, args):
             "peak": INT8_PEAK_TOPS, "frac": round(tops / INT8_PEAK_TOPS, 4), "per_matrix": out}
 
 
-def run_decode_100b(B, torch, args):
+def run_c5(B, torch, args):
+    """The 100B-class layer (q, o 8192x8192; k, v 1024x8192; up 28672x8192
+    with ReLU^2; down 8192x28672) at 1, 16 and 512 tokens, weights rotated
+    past the caches: each matrix's forward alone (x~ given) and the whole
+    layer (one activation quant per distinct input + the six forwards);
+    at 1 token also the fused step of up and of down alone."""
     import datagen
     wl = datagen.WORKLOADS["c5"]
+    set_bytes = sum(B.packed_bytes(n, k) for (n, k, _, _) in wl.matrices.values())
+    copies = max(2, math.ceil(2 * CACHE_BYTES / set_bytes))
+    base = DecodeSet(B, torch, wl, 1, copies)
     out = {}
-    tb, tt = 0.0, 0.0
-    for name in ("up", "down"):
-        n, k, relu2, group = wl.matrices[name]
-        copies = max(2, math.ceil(2 * CACHE_BYTES / B.packed_bytes(n, k)))
-        ds = DecodeSet(B, torch, wl, 1, copies, names=[name])
-        fused = ds.fused_steps()
-        t = time_launches(torch, lambda c: fused[c](), copies, 4 * copies)
-        tp = time_launches(torch, lambda c: ds.forward_one(name, c), copies, 4 * copies)
-        b = gemv_bytes(1, n, k)
-        out[name] = {"shape": f"1x{k}->{n}", "us": round(t * 1e3, 3),
-                     "GBs": round(b / (t * 1e-3) / 1e9, 1),
-                     "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "plain_gemv_us": round(tp * 1e3, 3), "copies": copies}
-        tb += b
-        tt += t
-        del ds, fused
+    for m in wl.batches:
+        ds = base if m == 1 else DecodeSet(B, torch, wl, m, copies, mats=base.mats)
+        per = {}
+        for nm in ds.names:
+            d = ds.mats[nm]
+            t = time_launches(torch, lambda c, nm=nm: ds.forward_one(nm, c), copies, 4 * copies)
+            b = gemv_bytes(m, d["n"], d["k"])
+            ops = 2.0 * m * d["n"] * d["k"]
+            per[nm] = {"shape": f"{m}x{d['k']}->{d['n']}", "us": round(t * 1e3, 3),
+                       "GBs": round(b / (t * 1e-3) / 1e9, 1),
+                       "TOPS": round(ops / (t * 1e-3) / 1e12, 2)}
+        tl = time_launches(torch, lambda c: ds.step(c), copies, 2 * copies)
+        ops = 2.0 * m * sum(d["n"] * d["k"] for d in ds.mats.values())
+        res = {"layer_us": round(tl * 1e3, 2),
+               "layer_GBs": round(ds.bytes_step() / (tl * 1e-3) / 1e9, 1),
+               "layer_TOPS": round(ops / (tl * 1e-3) / 1e12, 2), "per_matrix": per}
+        if m == 1:
+            fused = {}
+            for nm in ("up", "down"):
+                one = DecodeSet(B, torch, wl, 1, copies, names=[nm], mats={nm: base.mats[nm]})
+                steps = one.fused_steps()
+                t = time_launches(torch, lambda c: steps[c](), copies, 4 * copies)
+                b = one.bytes_step_fused()
+                fused[nm] = {"us": round(t * 1e3, 3), "GBs": round(b / (t * 1e-3) / 1e9, 1),
+                             "frac": round(b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                del one, steps
+            res["fused_act_quant"] = fused
+        out[str(m)] = res
+        log(f"c5 m={m}: layer {tl*1e3:.1f} us")
+        if ds is not base:
+            del ds
         torch.cuda.empty_cache()
-    gbs = tb / (tt * 1e-3) / 1e9
-    return {"workload": "c5 batch-1 fused GEMV, up 28672x8192 and down 8192x28672",
-            "GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "per_matrix": out}
+    del base
+    torch.cuda.empty_cache()
+    return {"workload": "c5: one 100B-class layer (q,o 8192x8192; k,v 1024x8192; up "
+                        "28672x8192 +ReLU^2; down 8192x28672), packed 155 MB, "
+                        f"{copies} copies rotated",
+            "per_batch": out}
 
 
 def run_stack_c3(B, torch, args):
@@ -578,9 +610,7 @@ def main():
     prefill = None if args.no_extra else run_prefill(B, torch, args)
     if prefill:
         log(f"prefill: {prefill['TOPS']} TOPS")
-    d100 = None if args.no_extra else run_decode_100b(B, torch, args)
-    if d100:
-        log(f"decode 100B-class: {d100['GBs']} GB/s")
+    c5 = None if args.no_extra else run_c5(B, torch, args)
     stack = None if args.no_extra else run_stack_c3(B, torch, args)
     cpu = None if args.no_cpu else run_cpu_baseline()
     line = {
@@ -604,7 +634,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "prefill": prefill,
-        "decode_100b": d100,
+        "c5": c5,
         "stack_c3": stack,
         "wall_s": round(time.time() - t0, 1),
     }

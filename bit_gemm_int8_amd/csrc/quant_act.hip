@@ -5,11 +5,14 @@
 // x~ = Clip(Round(x * 127 / beta)); the page's listing clamps beta below at
 // 1e-5, multiplies by 127/beta, rounds half to even and clamps to [-128, 127].
 //
-// One workgroup (4 waves) per token.  Pass 1 reduces max|x| with DPP inside
-// each wave and LDS across waves; pass 2 re-reads the token (L2-resident: at
-// most 2*K bytes) and writes x~ and the zero tail up to the padded row stride.
-// The max is taken on the fp32 bit patterns with the sign cleared, which
-// order like the magnitudes for finite values.
+// One workgroup (4 waves) per token.  max|x| is reduced with DPP inside each
+// wave and LDS across waves, then x~ and the zero tail up to the padded row
+// stride are written.  Rows of up to 16 16-byte vectors per thread (K <=
+// 32768 bf16 or 16384 fp32, 16-byte aligned) are loaded into registers all at
+// once and quantized from there (quant_act_reg_kernel); longer or unaligned
+// rows are read twice, the second time from L2 (quant_act_kernel).  The max
+// is taken on the fp32 bit patterns with the sign cleared, which order like
+// the magnitudes for finite values.
 #include "bl_device.h"
 #include "bl_internal.h"
 
@@ -35,6 +38,100 @@ __device__ __forceinline__ int8_t quantize(float v, float s) {
   return (int8_t)(int)r;
 }
 
+// max of the sign-cleared fp32 bit patterns of one 16-byte vector
+template <bool BF16>
+__device__ __forceinline__ uint32_t vec_absmax_bits(const uint4& u, uint32_t mx) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (BF16) {
+      const uint32_t lo = (w[e] << 16) & 0x7FFFFFFFu;
+      const uint32_t hi = w[e] & 0x7FFF0000u;
+      mx = mx > lo ? mx : lo;
+      mx = mx > hi ? mx : hi;
+    } else {
+      const uint32_t b = w[e] & 0x7FFFFFFFu;
+      mx = mx > b ? mx : b;
+    }
+  }
+  return mx;
+}
+
+// x~ of one 16-byte input vector (vector index v of the row) into qrow
+template <bool BF16>
+__device__ __forceinline__ void vec_quant_store(const uint4& u, float s, int8_t* qrow,
+                                                int64_t v) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  if (BF16) {
+    uint32_t out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t o = 0;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t ww = w[2 * h + e];
+        const int8_t q0 = quantize(__uint_as_float(ww << 16), s);
+        const int8_t q1 = quantize(__uint_as_float(ww & 0xFFFF0000u), s);
+        o |= ((uint32_t)(uint8_t)q0) << (16 * e);
+        o |= ((uint32_t)(uint8_t)q1) << (16 * e + 8);
+      }
+      out[h] = o;
+    }
+    reinterpret_cast<uint2*>(qrow)[v] = make_uint2(out[0], out[1]);
+  } else {
+    uint32_t o = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o |= ((uint32_t)(uint8_t)quantize(__uint_as_float(w[e]), s)) << (8 * e);
+    reinterpret_cast<uint32_t*>(qrow)[v] = o;
+  }
+}
+
+// beta over the workgroup from each thread's partial max; s = 127 /
+// max(beta, eps), correctly rounded to fp32
+__device__ __forceinline__ float row_scale(uint32_t mx, float eps, uint32_t* red) {
+  const int tid = threadIdx.x;
+  mx = wave_max_u32(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  const uint32_t m01 = red[0] > red[1] ? red[0] : red[1];
+  const uint32_t m23 = red[2] > red[3] ? red[2] : red[3];
+  const float beta = __uint_as_float(m01 > m23 ? m01 : m23);
+  return (float)(127.0 / (double)fmaxf(beta, eps));
+}
+
+// Rows of at most R vectors per thread, 16-byte aligned.
+template <bool BF16, int R>
+__global__ __launch_bounds__(kThreads) void quant_act_reg_kernel(
+    const void* __restrict__ x, int64_t k, int64_t kpad, float eps,
+    int8_t* __restrict__ xq, float* __restrict__ scale) {
+  constexpr int V = BF16 ? 8 : 4;                   // elements per vector
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint4* xrow = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(x) +
+                                                     row * k * (BF16 ? 2 : 4));
+  int8_t* qrow = xq + row * kpad;
+  __shared__ uint32_t red[kThreads / 64];
+  const int nvec = (int)(k / V);
+  uint4 u[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int v = tid + kThreads * i;
+    u[i] = v < nvec ? xrow[v] : make_uint4(0, 0, 0, 0);
+  }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) mx = vec_absmax_bits<BF16>(u[i], mx);
+  const float s = row_scale(mx, eps, red);
+  if (tid == 0) scale[row] = s;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int v = tid + kThreads * i;
+    if (v < nvec) vec_quant_store<BF16>(u[i], s, qrow, v);
+  }
+  for (int64_t i = k + tid; i < kpad; i += kThreads) qrow[i] = 0;
+}
+
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     const void* __restrict__ x, int64_t k, int64_t kpad, float eps,
@@ -50,71 +147,22 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
   uint32_t mx = 0;
   if (VEC) {
     const int64_t nvec = k / V;
-    for (int64_t v = tid; v < nvec; v += kThreads) {
-      uint4 u = reinterpret_cast<const uint4*>(xrow)[v];
-      if (BF16) {
-        uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint32_t lo = (w[e] << 16) & 0x7FFFFFFFu;
-          uint32_t hi = w[e] & 0x7FFF0000u;
-          mx = mx > lo ? mx : lo;
-          mx = mx > hi ? mx : hi;
-        }
-      } else {
-        uint32_t w[4] = {u.x & 0x7FFFFFFFu, u.y & 0x7FFFFFFFu, u.z & 0x7FFFFFFFu,
-                         u.w & 0x7FFFFFFFu};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = mx > w[e] ? mx : w[e];
-      }
-    }
+    for (int64_t v = tid; v < nvec; v += kThreads)
+      mx = vec_absmax_bits<BF16>(reinterpret_cast<const uint4*>(xrow)[v], mx);
   } else {
     for (int64_t i = tid; i < k; i += kThreads) {
       uint32_t b = __float_as_uint(load_elem(xrow, i, BF16)) & 0x7FFFFFFFu;
       mx = mx > b ? mx : b;
     }
   }
-  mx = wave_max_u32(mx);
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  uint32_t m01 = red[0] > red[1] ? red[0] : red[1];
-  uint32_t m23 = red[2] > red[3] ? red[2] : red[3];
-  const float beta = __uint_as_float(m01 > m23 ? m01 : m23);
-  // s = 127 / max(beta, eps), correctly rounded to fp32.
-  const float s = (float)(127.0 / (double)fmaxf(beta, eps));
+  const float s = row_scale(mx, eps, red);
   if (tid == 0) scale[row] = s;
 
   // ---- pass 2: quantize ----
   if (VEC) {
     const int64_t nvec = k / V;
-    for (int64_t v = tid; v < nvec; v += kThreads) {
-      uint4 u = reinterpret_cast<const uint4*>(xrow)[v];
-      if (BF16) {
-        uint32_t w[4] = {u.x, u.y, u.z, u.w};
-        uint32_t out[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint32_t o = 0;
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            uint32_t ww = w[2 * h + e];
-            int8_t q0 = quantize(__uint_as_float(ww << 16), s);
-            int8_t q1 = quantize(__uint_as_float(ww & 0xFFFF0000u), s);
-            o |= ((uint32_t)(uint8_t)q0) << (16 * e);
-            o |= ((uint32_t)(uint8_t)q1) << (16 * e + 8);
-          }
-          out[h] = o;
-        }
-        reinterpret_cast<uint2*>(qrow)[v] = make_uint2(out[0], out[1]);
-      } else {
-        float f[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
-                      __uint_as_float(u.w)};
-        uint32_t o = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o |= ((uint32_t)(uint8_t)quantize(f[e], s)) << (8 * e);
-        reinterpret_cast<uint32_t*>(qrow)[v] = o;
-      }
-    }
+    for (int64_t v = tid; v < nvec; v += kThreads)
+      vec_quant_store<BF16>(reinterpret_cast<const uint4*>(xrow)[v], s, qrow, v);
   } else {
     for (int64_t i = tid; i < k; i += kThreads) qrow[i] = quantize(load_elem(xrow, i, BF16), s);
   }
@@ -130,6 +178,23 @@ hipError_t launch_quant_act(const void* x, bool bf16, int64_t m, int64_t k, int6
   const size_t esz = bf16 ? 2 : 4;
   const bool vec = ((uintptr_t)x % 16 == 0) && ((k * esz) % 16 == 0);
   dim3 grid((unsigned)m), block(kThreads);
+  if (vec) {
+    const int64_t per = cdiv(k * (int64_t)esz / 16, kThreads);   // vectors per thread
+#define BL_QREG(R)                                                                           \
+  do {                                                                                       \
+    if (bf16)                                                                                \
+      quant_act_reg_kernel<true, R><<<grid, block, 0, stream>>>(x, k, kpad, eps, xq, scale); \
+    else                                                                                     \
+      quant_act_reg_kernel<false, R><<<grid, block, 0, stream>>>(x, k, kpad, eps, xq, scale); \
+    return hipGetLastError();                                                                \
+  } while (0)
+    if (per <= 1) BL_QREG(1);
+    if (per <= 2) BL_QREG(2);
+    if (per <= 4) BL_QREG(4);
+    if (per <= 8) BL_QREG(8);
+    if (per <= 16) BL_QREG(16);
+#undef BL_QREG
+  }
   if (bf16) {
     if (vec)
       quant_act_kernel<true, true><<<grid, block, 0, stream>>>(x, k, kpad, eps, xq, scale);

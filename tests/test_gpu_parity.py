@@ -21,9 +21,12 @@ def B():
 
 
 # ------------------------------------------------------------ activations --
+# rows held in registers (1 to 16 16-byte vectors per thread), rows read
+# twice (longer, or not a whole number of 16-byte vectors)
 QA_CASES = [(1, 1, "f32"), (1, 7, "bf16"), (3, 256, "f32"), (4, 272, "bf16"), (5, 1000, "f32"),
             (9, 2560, "bf16"), (2, 6912, "bf16"), (64, 300, "f32"), (33, 8, "bf16"),
-            (1, 28672, "bf16"), (130, 520, "f32")]
+            (1, 28672, "bf16"), (130, 520, "f32"), (3, 16000, "bf16"), (2, 16384, "f32"),
+            (2, 40000, "bf16"), (3, 20000, "f32"), (4, 1001, "f32")]
 
 
 @pytest.mark.parametrize("m,k,xdt", QA_CASES)
