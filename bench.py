@@ -49,6 +49,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA, 5.0 POPS
 CACHE_BYTES = (256 + 32) << 20   # Infinity Cache + 8 x 4 MB L2
+SIMDS = 256 * 4                  # 256 CUs x 4 SIMDs
+XCDS = 8
 
 
 def log(msg: str) -> None:
@@ -498,9 +500,26 @@ def recorded_traffic():
 
 
 def pmc_driver(B, torch, args):
-    """Launches to read counters from: a plain copy of COPY_BYTES (the
-    calibration), then eager fused decode steps over rotating weight copies."""
+    """Launches to read counters from.  decode: a plain copy of COPY_BYTES
+    (the calibration), then eager fused decode steps over rotating weight
+    copies.  prefill: the two 2048-token prefill GEMMs, `steps` times each."""
     import datagen
+    if args.pmc_driver == "prefill":
+        wl = datagen.WORKLOADS["c4"]
+        for name in ("up", "down"):
+            n, k, relu2, group = wl.matrices[name]
+            w = torch.from_numpy(datagen.workload_weights(wl, name)).cuda()
+            packed, gamma = B.pack_weights(w)
+            del w
+            bits, _ = datagen.activations(wl, group, 2048)
+            x = torch.from_numpy(bits.view("int16")).view(torch.bfloat16).cuda()
+            xq, s = B.quant_act(x)
+            y = torch.empty((2048, n), dtype=torch.bfloat16, device="cuda")
+            for _ in range(args.steps):
+                B.forward(xq, s, packed, gamma, n, k, relu2=relu2, y=y)
+            torch.cuda.synchronize()
+        print(json.dumps({"pmc_driver": "prefill", "steps": args.steps}))
+        return
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -514,7 +533,7 @@ def pmc_driver(B, torch, args):
     for i in range(args.steps):
         fused[i % copies]()
     torch.cuda.synchronize()
-    print(json.dumps({"pmc_driver": "done", "steps": args.steps, "copies": copies,
+    print(json.dumps({"pmc_driver": "decode", "steps": args.steps, "copies": copies,
                       "step_bytes": int(ds.bytes_step_fused())}))
 
 
@@ -522,8 +541,11 @@ def _kname(s):
     return s.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
 
 
-def summarize(directory, command):
-    """Write profiles/ summaries from rocprofv3 CSV output in `directory`."""
+def summarize(directory, command, name):
+    """Write profiles/ summaries from rocprofv3 CSV output in `directory`:
+    <name>_kernel_stats.md from a kernel trace; from counter runs, the
+    fused decode kernel's HBM traffic (FETCH_SIZE / WRITE_SIZE against the
+    copy calibration) or the GEMM kernels' MFMA counters."""
     import csv
     import glob
     import statistics
@@ -537,18 +559,23 @@ def summarize(directory, command):
         for r in rows:
             lines.append(f"| {_kname(r['Name'])} | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
                          f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | {float(r['Percentage']):.2f} |")
-        out.append(("gemv_fused_decode_2b_kernel_stats.md", "\n".join(lines) + "\n"))
+        out.append((f"{name}_kernel_stats.md", "\n".join(lines) + "\n"))
     pmc = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
-    if pmc:
-        vals = {}
-        for f in pmc:
-            for r in csv.DictReader(open(f)):
-                vals.setdefault((_kname(r["Kernel_Name"]), r["Counter_Name"]), []).append(
-                    float(r["Counter_Value"]))
-        def med(kern_sub, ctr):
-            v = [x for (k, c), xs in vals.items() if kern_sub in k and c == ctr for x in xs]
-            return statistics.median(v) if v else None
+    vals, durs = {}, {}
+    for f in pmc:
+        for r in csv.DictReader(open(f)):
+            k = _kname(r["Kernel_Name"])
+            vals.setdefault((k, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+            if "Start_Timestamp" in r:
+                durs.setdefault(k, []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    ctrs = {c for (_, c) in vals}
 
+    def med(kern_sub, ctr):
+        v = [x for (k, c), xs in vals.items() if kern_sub in k and c == ctr for x in xs]
+        return statistics.median(v) if v else None
+
+    if "FETCH_SIZE" in ctrs or "WRITE_SIZE" in ctrs:
         def largest(kern_sub, ctr):
             # the calibration copy is the largest copy the driver makes
             v = [x for (k, c), xs in vals.items() if kern_sub in k and c == ctr for x in xs]
@@ -569,11 +596,37 @@ def summarize(directory, command):
                  f"- traffic_bytes_per_launch: {traffic}",
                  f"- kernel_source_sha256_16: {kernel_source_hash()}", ""]
         out.append(("gemv_fused_decode_2b_traffic.md", "\n".join(lines)))
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in ctrs:
+        kernels = sorted({k for (k, c), xs in vals.items()
+                          if c == "SQ_VALU_MFMA_BUSY_CYCLES" and max(xs) > 0})
+        lines = ["# MFMA counters of the prefill GEMM kernels (rocprofv3 --pmc)", "",
+                 f"Command: `{command}`", "",
+                 "Medians per dispatch (the profiler serialises dispatches, so durations run "
+                 "a little above graph replay).  GRBM_GUI_ACTIVE is reported summed over the "
+                 f"{XCDS} XCDs; per XCD it counts the kernel's GPU cycles, so cycles / duration "
+                 "is the clock.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD "
+                 f"x {SIMDS} SIMDs), the MfmaUtil expression rocprofv3 lists for gfx950; int8 ops "
+                 "= SQ_INSTS_VALU_MFMA_MOPS_I8 x 512 (padded tiles included).", "",
+                 "| kernel | us | GHz | SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | MFMA busy | "
+                 "int8 ops | int8 TOPS |", "|---|---|---|---|---|---|---|---|"]
+        for k in kernels:
+            busy, act = med(k, "SQ_VALU_MFMA_BUSY_CYCLES"), med(k, "GRBM_GUI_ACTIVE")
+            mops = med(k, "SQ_INSTS_VALU_MFMA_MOPS_I8")
+            us = statistics.median(durs[k]) if durs.get(k) else None
+            per_xcd = act / XCDS if act else None
+            ghz = per_xcd / (us * 1e3) if per_xcd and us else None
+            util = busy / (per_xcd * SIMDS) if busy and per_xcd else None
+            ops = mops * 512 if mops is not None else None
+            tops = ops / (us * 1e-6) / 1e12 if ops and us else None
+            f = lambda v, fmt: "-" if v is None else format(v, fmt)
+            lines.append(f"| {k} | {f(us, '.2f')} | {f(ghz, '.3f')} | {f(busy, '.0f')} | "
+                         f"{f(act, '.0f')} | {f(util, '.3f')} | {f(ops, '.4g')} | {f(tops, '.0f')} |")
+        out.append((f"{name}_mfma_counters.md", "\n".join(lines) + "\n"))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    for name, text in out:
-        with open(os.path.join(ROOT, "profiles", name), "w") as f:
+    for fname, text in out:
+        with open(os.path.join(ROOT, "profiles", fname), "w") as f:
             f.write(text)
-        print(f"wrote profiles/{name}")
+        print(f"wrote profiles/{fname}")
 
 
 def main():
@@ -583,17 +636,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip prefill and 100B-class legs")
-    ap.add_argument("--pmc-driver", action="store_true",
-                    help="only launch what the HBM-traffic counters are read from")
+    ap.add_argument("--pmc-driver", nargs="?", const="decode", choices=["decode", "prefill"],
+                    help="only launch what the counters are read from: the fused decode "
+                         "step (HBM traffic) or the prefill GEMMs (MFMA)")
     ap.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSVs")
+    ap.add_argument("--name", default="gemv_fused_decode_2b",
+                    help="kernel and workload the summaries are named for")
     ap.add_argument("--command", default="", help="command line recorded in the summaries")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize, args.command)
+        summarize(args.summarize, args.command, args.name)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU split is described in DESIGN.md, not built).", file=sys.stderr)
+              "(the multi-GPU split is designed, not built).", file=sys.stderr)
         sys.exit(2)
 
     import torch
