@@ -293,9 +293,9 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
     sg.nc = (int)cdiv(o.k, kSuperK);
     sg.splits = plan.splits[i];
     sg.wg_begin = begin;
-    sg.relu2 = o.epilogue == BL_EPI_RELU2;
-    sg.y_bf16 = o.y_dtype == BL_BF16;
-    sg.x_bf16 = o.x_dtype == BL_BF16;
+    sg.flags = (o.epilogue == BL_EPI_RELU2 ? 1 : 0) | (o.y_dtype == BL_BF16 ? 2 : 0) |
+               (o.x_dtype == BL_BF16 ? 4 : 0);
+    args.wg_begin[i] = begin;
     if (sg.splits > 1)
       sg.slots = reinterpret_cast<int64_t*>(reinterpret_cast<char*>(workspace) + plan.slot_off[i]);
     begin += (int)(cdiv(o.n, kRowBlock) * (4 / plan.qpl) * sg.splits);

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <cstddef>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -44,22 +45,34 @@ hipError_t launch_fill_zero(uint32_t* p, size_t words, hipStream_t stream);
 // Fused decode step: a table of BitLinear products that share a token batch
 // (M <= 4), each quantizing its own activations in the kernel prologue.
 constexpr int kMaxFused = 16;
-struct FusedSeg {
+// One entry of the fused decode step.  The fields a workgroup needs first
+// share the first 64-byte line (one scalar load after the entry is known);
+// the optional outputs sit in the second line and are read at the end.
+struct alignas(64) FusedSeg {
   const void* x;          // [m][k] activations (fp32 or bf16)
   const void* packed;     // packed weights (n, k)
   const float* gamma;
   void* y;                // [m][n]
+  int64_t* slots;         // split-K slots, [row block][m][64] (splits > 1)
+  int n, k, nc, splits, wg_begin;
+  int flags;              // bit 0: ReLU^2, bit 1: y bf16, bit 2: x bf16
   int32_t* acc_out;       // nullable
   int8_t* xq_out;         // nullable, [m][padded_k(k)]
   float* scale_out;       // nullable, [m]
-  int64_t* slots;         // split-K slots, [row block][m][64] (splits > 1)
-  int n, k, nc, splits, wg_begin, relu2, y_bf16, x_bf16;
+  __host__ __device__ bool relu2() const { return (flags & 1) != 0; }
+  __host__ __device__ bool y_bf16() const { return (flags & 2) != 0; }
+  __host__ __device__ bool x_bf16() const { return (flags & 4) != 0; }
 };
+// The entries' first workgroups share one 64-byte line, so a workgroup
+// finds its entry with one scalar load.
 struct FusedArgs {
-  FusedSeg seg[kMaxFused];
+  int wg_begin[kMaxFused];
   int nseg;
   float eps;
+  FusedSeg seg[kMaxFused];
 };
+static_assert(kMaxFused * sizeof(int) == 64, "entry starts in one line");
+static_assert(offsetof(FusedSeg, acc_out) == 64, "first-use fields in the first line");
 hipError_t launch_gemv_mfma(int variant, const int8_t* xq, const float* scale,
                             const uint32_t* packed, const float* gamma, int64_t m, int64_t n,
                             int64_t k, bool relu2, bool bf16, void* y, int32_t* acc_out,

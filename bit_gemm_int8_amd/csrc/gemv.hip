@@ -298,7 +298,7 @@ struct XRow {
 
 __device__ __forceinline__ XRow x_row_info(const FusedSeg& sg) {
   XRow r;
-  const int esize = sg.x_bf16 ? 2 : 4;
+  const int esize = sg.x_bf16() ? 2 : 4;
   r.epu = 16 / esize;
   r.nu = (sg.k + r.epu - 1) / r.epu;
   r.fast = ((int64_t)sg.k * esize % 16 == 0) && ((uintptr_t)sg.x % 16 == 0);
@@ -306,7 +306,7 @@ __device__ __forceinline__ XRow x_row_info(const FusedSeg& sg) {
 }
 
 __device__ __forceinline__ const char* x_row(const FusedSeg& sg, int m) {
-  return reinterpret_cast<const char*>(sg.x) + (int64_t)m * sg.k * (sg.x_bf16 ? 2 : 4);
+  return reinterpret_cast<const char*>(sg.x) + (int64_t)m * sg.k * (sg.x_bf16() ? 2 : 4);
 }
 
 // Unit u of a row as it lies in memory (elements past K read as 0).
@@ -317,7 +317,7 @@ __device__ __forceinline__ uint4 load_unit(const FusedSeg& sg, const XRow& xr, c
   for (int i = 0; i < xr.epu; ++i) {
     const int kk = u * xr.epu + i;
     if (kk >= sg.k) break;
-    if (sg.x_bf16)
+    if (sg.x_bf16())
       w[i >> 1] |= ((uint32_t)reinterpret_cast<const uint16_t*>(row)[kk]) << (16 * (i & 1));
     else
       w[i] = reinterpret_cast<const uint32_t*>(row)[kk];
@@ -400,7 +400,7 @@ __device__ __forceinline__ void quantize_into_lds(const FusedSeg& sg, int g0, in
   constexpr int NT = 64 * WAVES;
   constexpr int XV = kXV<NT, LONGX>;
   const XRow xr = x_row_info(sg);
-  const bool bf16 = sg.x_bf16 != 0;
+  const bool bf16 = sg.x_bf16();
   const int ubase = g0 * 256 / xr.epu;
   uint32_t mx[M];
 #pragma unroll
@@ -462,8 +462,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) 
   extern __shared__ uint4 xs_lds[];
   // segment of this workgroup
   int si = 0;
-  for (int i = 1; i < args.nseg; ++i)
-    if ((int)blockIdx.x >= args.seg[i].wg_begin) si = i;
+#pragma unroll
+  for (int i = 1; i < kMaxFused; ++i)
+    if (i < args.nseg && (int)blockIdx.x >= args.wg_begin[i]) si = i;
   const FusedSeg& sg = args.seg[si];
   const int local = (int)blockIdx.x - sg.wg_begin;
   const int splits = sg.splits;
@@ -521,8 +522,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) 
   float fac[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) fac[m] = gamma_over_s(g, sv[m]);
-  write_rows<M>(acc, own, fac, (int64_t)b * 64 + rb, sg.n, sg.y, sg.acc_out, sg.relu2 != 0,
-                sg.y_bf16 != 0);
+  write_rows<M>(acc, own, fac, (int64_t)b * 64 + rb, sg.n, sg.y, sg.acc_out, sg.relu2(),
+                sg.y_bf16());
 }
 
 }  // namespace
