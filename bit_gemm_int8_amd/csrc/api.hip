@@ -13,9 +13,8 @@ hipError_t launch_gemv(int m, int waves, int pf, int qpl, const int8_t* xq, cons
                        int splits, bool relu2, bool bf16, void* y, int32_t* acc_out,
                        int64_t* ws_slots, hipStream_t stream);
 hipError_t launch_gemm(int variant, const int8_t* xq, const float* scale, const uint32_t* packed,
-                       const float* gamma, int64_t m, int64_t n, int64_t k, int splits,
-                       bool relu2, bool bf16, void* y, int32_t* acc_out, int64_t* ws_slots,
-                       hipStream_t stream);
+                       const float* gamma, int64_t m, int64_t n, int64_t k, bool relu2,
+                       bool bf16, void* y, int32_t* acc_out, hipStream_t stream);
 void gemm_tile_shape(int variant, int* bm, int* bn);
 
 namespace {
@@ -30,8 +29,6 @@ constexpr int64_t kGemvMaxM = 2;           // dot4 GEMV up to here
 constexpr int64_t kMfmaGemvMaxM = 64;      // windowed MFMA GEMV up to here (4 token groups)
 constexpr int64_t kGemvTargetGroups = 512;
 constexpr int64_t kGemvMaxLds = 48 * 1024;
-constexpr int64_t kGemmTargetGroups = 512;
-constexpr int64_t kGemmFullTiles = 192;   // 3/4 of the 256 CUs
 constexpr int64_t kCUs = 256;
 
 }  // namespace
@@ -96,35 +93,33 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     // MFMA GEMM, wide waves.  The tile shape maximises the work the first
     // rounds of tiles over the 256 CUs keep busy, weighted by how well each
     // shape runs (128 x 512 best, 64 x 512 then 64 x 256 and 96 x 256).
-    // Split-K (one atomic combine per output) only when the tiles leave most
-    // CUs idle.  (Tuned on MI355X over the 2048- and 512-token prefills.)
-    p.kind = 1;
+    // When even that leaves more than half the CUs without a tile, the
+    // windowed MFMA GEMV takes the product in token blocks of 64 (it needs
+    // no split of K).  (Tuned on MI355X over the 2048- and 512-token
+    // prefills and the 100B-class k/v products.)
     static const double kRate[4] = {1.0, 0.9, 0.85, 0.85};
     double best = -1.0;
+    int64_t tiles = 0;
     for (int v = 0; v < 4; ++v) {
       int bm, bn;
       gemm_tile_shape(v, &bm, &bn);
-      const int64_t tiles = cdiv(m, bm) * cdiv(nb * 64, bn);
+      const int64_t t = cdiv(m, bm) * cdiv(nb * 64, bn);
       const double useful = (double)m * (double)(nb * 64) / ((double)bm * bn);
-      const double score = kRate[v] * useful / (double)(cdiv(tiles, kCUs) * kCUs);
+      const double score = kRate[v] * useful / (double)(cdiv(t, kCUs) * kCUs);
       if (score > best) {
         best = score;
         p.variant = v;
+        tiles = t;
       }
     }
-    int bm, bn;
-    gemm_tile_shape(p.variant, &bm, &bn);
-    const int64_t tiles = cdiv(m, bm) * cdiv(nb * 64, bn);
-    int64_t s = 1;
-    if (tiles < kGemmFullTiles / 4) {
-      s = cdiv(kGemmTargetGroups, tiles);
-      int64_t smax = nc / 2 > 1 ? nc / 2 : 1;
-      if (s > smax) s = smax;
-      if (s > 4) s = 4;
-      if (s < 1) s = 1;
+    if (tiles < kCUs / 2) {
+      p.kind = 2;
+      p.variant = nb >= 256 ? 6 : 5;
+    } else {
+      p.kind = 1;
     }
-    p.splits = (int)s;
-    p.slots = s > 1 ? (size_t)(tiles * bm * bn) : 0;
+    p.splits = 1;
+    p.slots = 0;
   }
   p.ws_bytes = p.slots * 8;
   return p;
@@ -141,8 +136,8 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
   if (plan.kind == 2)
     return launch_gemv_mfma(plan.variant, xq, scale, packed, gamma, m, n, k, relu2, bf16, y,
                             acc_out, stream);
-  return launch_gemm(plan.variant, xq, scale, packed, gamma, m, n, k, plan.splits, relu2, bf16,
-                     y, acc_out, slots, stream);
+  return launch_gemm(plan.variant, xq, scale, packed, gamma, m, n, k, relu2, bf16, y, acc_out,
+                     stream);
 }
 
 struct FusedPlan {

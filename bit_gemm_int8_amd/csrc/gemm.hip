@@ -5,9 +5,9 @@
 // Multiplication as Pure Integer Addition": acc = x~ W~^T (integer), then
 // y = acc * gamma / s.  With many tokens the product is a dense contraction,
 // so it runs on the matrix cores: the 2-bit codes are expanded to int8
-// (64 * W~) in registers right before each MFMA.  Split-K over super-chunks
-// (small outputs only) combines each element through a 64-bit workspace slot
-// with one device-scope atomic, as in the GEMV.
+// (64 * W~) in registers right before each MFMA.  Outputs too small to give
+// the chip enough tiles go to the windowed MFMA GEMV in token blocks instead,
+// so K is never split here.
 #include "bl_device.h"
 #include "bl_internal.h"
 
@@ -77,13 +77,12 @@ __device__ __forceinline__ int tile_of_block(int bid, int tiles, int tiles_m, in
   return tm * tiles_n + tn;
 }
 
-template <int FM, int WN, int KS, bool SPLIT>
+template <int FM, int WN, int KS>
 __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ scale,
     const uint4* __restrict__ packed, const float* __restrict__ gamma, int m, int n,
-    int nb, int nc, int64_t kpad, int splits, int tiles_m, int tiles_n, int band, int relu2,
-    int bf16, int vec_out, void* __restrict__ y, int32_t* __restrict__ acc_out,
-    int64_t* __restrict__ ws_slots) {
+    int nb, int nc, int64_t kpad, int tiles_m, int tiles_n, int band, int relu2,
+    int bf16, int vec_out, void* __restrict__ y, int32_t* __restrict__ acc_out) {
   using T = TileW<FM, WN, KS>;
   constexpr int BM = T::BM, BN = T::BN, NT = T::NT, UA = T::UA;
   // two stages as separate arrays: the compiler then sees that the copies
@@ -95,14 +94,11 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t B1[T::B_BYTES];
 
   const int tiles = tiles_m * tiles_n;
-  const int bid = (int)blockIdx.x / splits;
-  const int s = (int)blockIdx.x - bid * splits;
-  const int tile = tile_of_block(bid, tiles, tiles_m, tiles_n, band);
+  const int tile = tile_of_block((int)blockIdx.x, tiles, tiles_m, tiles_n, band);
   const int tm = tile / tiles_n;
   const int tn = tile - tm * tiles_n;
   const int m0 = tm * BM;
-  const int c0 = (int)((int64_t)s * nc / splits);
-  const int c1 = (int)((int64_t)(s + 1) * nc / splits);
+  const int c0 = 0, c1 = nc;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -250,25 +246,6 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
     }
   }
 
-  if constexpr (SPLIT) {
-    int64_t* slot = ws_slots + (int64_t)tile * (BM * BN) + tid;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      int64_t old[2][16];
-#pragma unroll
-      for (int fn = 0; fn < 2; ++fn)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          old[fn][e] = split_add(slot + ((fm * 2 + fn) * 16 + e) * NT, acc[fm][fn][e]);
-#pragma unroll
-      for (int fn = 0; fn < 2; ++fn)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          acc[fm][fn][e] = split_finish(slot + ((fm * 2 + fn) * 16 + e) * NT, old[fn][e],
-                                        acc[fm][fn][e], splits);
-    }
-  }
-
   // rescale factors per tile row (in the now idle first A stage)
   float* fac = reinterpret_cast<float*>(A0);
   const float gam = *gamma;
@@ -279,8 +256,8 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
   __syncthreads();
   // Each group of four accumulator elements is four consecutive columns of
   // one row: whole groups go out as one 16-byte (fp32, int32) or 8-byte
-  // (bf16) store when vec_out (n % 4 == 0 and aligned outputs); split
-  // groups, the column tail and unaligned outputs go element by element.
+  // (bf16) store when vec_out (n % 4 == 0 and aligned outputs); the column
+  // tail and unaligned outputs go element by element.
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     const int gm = m0 + 32 * fm + c;
@@ -295,7 +272,7 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
         int v[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[t] = acc[fm][fn][4 * g + t];
-        if (!SPLIT && vec_out && gn + 3 < n) {
+        if (vec_out && gn + 3 < n) {
           float o[4];
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
@@ -314,7 +291,7 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
         } else {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            if (gn + t >= n || (v[t] & 63) != 0) continue;
+            if (gn + t >= n) continue;
             const int a = v[t] >> 6;
             if (acc_out != nullptr) acc_out[idx + t] = a;
             store_out(y, idx + t, a, f, relu2 != 0, bf16 != 0);
@@ -327,20 +304,19 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
 
 template <int FM, int WN, int KS>
 hipError_t runw(const int8_t* xq, const float* scale, const uint32_t* packed, const float* gamma,
-                int64_t m, int64_t n, int64_t k, int splits, int band, bool relu2, bool bf16,
-                void* y, int32_t* acc_out, int64_t* slots, hipStream_t stream) {
+                int64_t m, int64_t n, int64_t k, int band, bool relu2, bool bf16, void* y,
+                int32_t* acc_out, hipStream_t stream) {
   using T = TileW<FM, WN, KS>;
   const int nb = (int)cdiv(n, kRowBlock);
   const int nc = (int)cdiv(k, kSuperK);
   const int tiles_m = (int)cdiv(m, T::BM);
   const int tiles_n = (int)cdiv(padded_n(n), T::BN);
-  const int64_t grid = (int64_t)tiles_m * tiles_n * splits;
+  const int64_t grid = (int64_t)tiles_m * tiles_n;
   const int vec_out = n % 4 == 0 && (uintptr_t)y % (bf16 ? 8 : 16) == 0 &&
                       (acc_out == nullptr || (uintptr_t)acc_out % 16 == 0);
-  auto kern = splits > 1 ? gemmw_kernel<FM, WN, KS, true> : gemmw_kernel<FM, WN, KS, false>;
-  kern<<<(unsigned)grid, T::NT, 0, stream>>>(
+  gemmw_kernel<FM, WN, KS><<<(unsigned)grid, T::NT, 0, stream>>>(
       xq, scale, reinterpret_cast<const uint4*>(packed), gamma, (int)m, (int)n, nb, nc,
-      padded_k(k), splits, tiles_m, tiles_n, band, relu2, bf16, vec_out, y, acc_out, slots);
+      padded_k(k), tiles_m, tiles_n, band, relu2, bf16, vec_out, y, acc_out);
   return hipGetLastError();
 }
 
@@ -361,12 +337,11 @@ void gemm_tile_shape(int variant, int* bm, int* bn) {
 constexpr int kBand = 4;
 
 hipError_t launch_gemm(int variant, const int8_t* xq, const float* scale, const uint32_t* packed,
-                       const float* gamma, int64_t m, int64_t n, int64_t k, int splits,
-                       bool relu2, bool bf16, void* y, int32_t* acc_out, int64_t* slots,
-                       hipStream_t stream) {
+                       const float* gamma, int64_t m, int64_t n, int64_t k, bool relu2,
+                       bool bf16, void* y, int32_t* acc_out, hipStream_t stream) {
 #define BL_GEMMW(FM, WN)                                                                     \
-  return runw<FM, WN, 1>(xq, scale, packed, gamma, m, n, k, splits, kBand, relu2, bf16, y, \
-                         acc_out, slots, stream)
+  return runw<FM, WN, 1>(xq, scale, packed, gamma, m, n, k, kBand, relu2, bf16, y, acc_out, \
+                         stream)
   switch (variant) {
     case 0: BL_GEMMW(4, 8);
     case 1: BL_GEMMW(2, 8);

@@ -51,7 +51,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 // LDS windows, with one workgroup barrier per step; each wave keeps PF
 // super-chunks of its weights and of its share of x~ in flight in registers.
 // In LDS the 16-byte unit u of token t sits at unit u ^ (t % 16), so the 16
-// tokens of one operand read hit 16 different bank groups.
+// tokens of one operand read hit 16 different bank groups.  More tokens than
+// 16 * TG run as token blocks of 16 * TG on blockIdx.y.
 template <int WR, int WK, int SB, int TG, int PF>
 __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_win_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ scale,
@@ -62,6 +63,15 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_win_kernel(
   static_assert(PF == 2 || PF == 4, "the loop is unrolled by PF, an even number");
   constexpr int NTS = 64 * WR;                      // threads staging one slice
   constexpr int MT = 16 * TG;                       // token columns
+  // token block blockIdx.y: tokens MT * blockIdx.y .. + MT - 1
+  {
+    const int t0 = MT * (int)blockIdx.y;
+    xq += (int64_t)t0 * kpad;
+    scale += t0;
+    y = reinterpret_cast<uint8_t*>(y) + (int64_t)t0 * n * (bf16 ? 2 : 4);
+    if (acc_out != nullptr) acc_out += (int64_t)t0 * n;
+    m = min(m - t0, MT);
+  }
   constexpr int XU = MT * 16 / NTS;                 // x~ units per thread and super-chunk
   static_assert(MT * 16 % NTS == 0, "x~ staging split");
   __shared__ bl_v4i xs[WK][2][MT * 16];
@@ -230,8 +240,9 @@ hipError_t run_gemv_mfma_win(const int8_t* xq, const float* scale, const uint32_
                              bool bf16, void* y, int32_t* acc_out, hipStream_t stream) {
   const int nb = (int)cdiv(n, kRowBlock);
   const int nc = (int)cdiv(k, kSuperK);
-  if (m < 1 || m > 16 * TG || nc < 1) return hipErrorInvalidValue;
-  dim3 grid((unsigned)cdiv((int64_t)nb * 4, WR * SB)), block(64 * WR * WK);
+  if (m < 1 || nc < 1) return hipErrorInvalidValue;
+  dim3 grid((unsigned)cdiv((int64_t)nb * 4, WR * SB), (unsigned)cdiv(m, 16 * TG)),
+      block(64 * WR * WK);
   const int vec_out = n % 4 == 0 && (uintptr_t)y % (bf16 ? 8 : 16) == 0 &&
                       (acc_out == nullptr || (uintptr_t)acc_out % 16 == 0);
   gemv_mfma_win_kernel<WR, WK, SB, TG, PF><<<grid, block, 0, stream>>>(
