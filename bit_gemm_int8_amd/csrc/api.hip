@@ -79,14 +79,14 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
   } else if (m <= kMfmaGemvMaxM) {
     // Windowed MFMA GEMV: 16, 32 or 64 token columns.  Many row blocks
     // (>= 256): wide row groups, the whole K per wave; fewer: slices of K
-    // over the waves of a workgroup, 8 slices for few (<= 64) long (>= 24
-    // super-chunks) rows at 16 tokens.  (Tuned on MI355X over the 2B- and
+    // over the waves of a workgroup, more slices (8 at 16 tokens, 4 at 64)
+    // for long rows (>= 24 super-chunks) or few (<= 64) row blocks.  (Tuned on MI355X over the 2B- and
     // 100B-class decode shapes.)
     p.kind = 2;
     const bool wide = nb >= 256;
     if (m <= 16) p.variant = wide ? 2 : (nb <= 64 && nc >= 24) ? 1 : 0;
     else if (m <= 32) p.variant = wide ? 4 : 3;
-    else p.variant = wide ? 6 : 5;
+    else p.variant = wide ? 6 : (nc >= 24 || nb <= 64) ? 7 : 5;
     p.splits = 1;
     p.slots = 0;
   } else {
@@ -114,7 +114,7 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     }
     if (tiles < kCUs / 2) {
       p.kind = 2;
-      p.variant = nb >= 256 ? 6 : 5;
+      p.variant = nb >= 256 ? 6 : (nc >= 24 || nb <= 64) ? 7 : 5;
     } else {
       p.kind = 1;
     }

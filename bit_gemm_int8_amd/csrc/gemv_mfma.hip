@@ -257,7 +257,7 @@ hipError_t run_gemv_mfma_win(const int8_t* xq, const float* scale, const uint32_
 // token groups, super-chunks in flight):
 //   0: 2 x 4 x 1, 1 group, 2     1: 1 x 8 x 1, 1 group, 2    2: 4 x 1 x 2, 1 group, 4
 //   3: 2 x 4 x 1, 2 groups, 2    4: 8 x 1 x 1, 2 groups, 4
-//   5: 4 x 2 x 1, 4 groups, 2    6: 8 x 1 x 1, 4 groups, 2
+//   5: 4 x 2 x 1, 4 groups, 2    6: 8 x 1 x 1, 4 groups, 2    7: 2 x 4 x 1, 4 groups, 2
 hipError_t launch_gemv_mfma(int variant, const int8_t* xq, const float* scale,
                             const uint32_t* packed, const float* gamma, int64_t m, int64_t n,
                             int64_t k, bool relu2, bool bf16, void* y, int32_t* acc_out,
@@ -273,6 +273,7 @@ hipError_t launch_gemv_mfma(int variant, const int8_t* xq, const float* scale,
     case 4: BL_WIN(8, 1, 1, 2, 4);
     case 5: BL_WIN(4, 2, 1, 4, 2);
     case 6: BL_WIN(8, 1, 1, 4, 2);
+    case 7: BL_WIN(2, 4, 1, 4, 2);
     default: return hipErrorInvalidValue;
   }
 #undef BL_WIN

@@ -184,6 +184,8 @@ FWD_CASES = [
     # ... 33 to 64 tokens (4 token groups)
     (33, 100, 257, True, "f32", "f32"),
     (64, 512, 2560, False, "bf16", "bf16"),
+    (48, 2000, 7000, True, "bf16", "f32"),       # long rows: 4 K-slices
+    (40, 6000, 2000, False, "f32", "bf16"),      # short rows, many blocks: 2 K-slices
     (50, 16400, 700, False, "f32", "bf16"),      # wide row groups
     (64, 16385, 512, True, "bf16", "f32"),       # wide, odd N
     # ... more than 64 tokens with few output tiles: token blocks of 64
@@ -192,6 +194,7 @@ FWD_CASES = [
     (129, 260, 5000, True, "f32", "bf16"),
     (256, 384, 768, False, "f32", "bf16"),
     (200, 1001, 700, False, "bf16", "f32"),      # odd N: element stores
+    (200, 6000, 512, True, "bf16", "bf16"),      # short rows, many blocks
     # wide-wave MFMA GEMM (more than 64 tokens, >= 128 tiles)
     (1000, 6100, 300, True, "bf16", "bf16"),     # 64 x 512 tiles, ragged M, N, K
     (1024, 6144, 512, False, "f32", "bf16"),     # 64 x 512, vector stores
