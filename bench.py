@@ -343,9 +343,10 @@ def run_stack_c3(B, torch, args):
     """The c3 stack: the 2B-class set as 30 layers, each with its own copy of
     the packed weights (388 MB in all, past the caches).  One pass = every
     layer in order: q/k/v (one shared input), o, up (ReLU^2), down, at 1, 8,
-    32 and 64 tokens with Student-t activations.  Up to 4 tokens each group
-    is one fused decode launch (activation quant in its prologue); above,
-    one activation quant per distinct input and one GEMM per matrix.  A pass
+    32 and 64 tokens with Student-t activations.  Each group is one fused
+    decode launch (activation quant in its prologue) at 1-2 tokens, and at
+    3-16 tokens when it holds several matrices; otherwise one activation
+    quant per distinct input and one forward per matrix.  A pass
     is captured as one graph; the best of a few replays is reported."""
     import datagen
     wl = datagen.WORKLOADS["c3"]
@@ -369,32 +370,35 @@ def run_stack_c3(B, torch, args):
               for nm, d in mats.items()}
         ws = B.Workspace()
         calls = []
-        if m <= 4:
-            for l in range(layers):
-                for grp in order:
+        # a group runs as one fused step (activation quant in the kernel)
+        # at 1-2 tokens, and at 3-16 tokens when it has several matrices
+        # sharing its input (q, k, v); otherwise as one activation quant plus
+        # one forward per matrix (at 3-16 tokens a fused step re-quantizes
+        # the input in every workgroup, which a single matrix does not repay)
+        xq = {g: torch.empty((m, B.padded_k(x.shape[1])), dtype=torch.int8, device="cuda")
+              for g, x in xs.items()}
+        sc = {g: torch.empty(m, dtype=torch.float32, device="cuda") for g in xs}
+        ws.get(max(B.forward_workspace_bytes(m, d["n"], d["k"]) for d in mats.values()))
+
+        def quant(g):
+            x = xs[g]
+            B._check("quant", lib.bitlinear_quant_act(
+                x.data_ptr(), B.BL_BF16, m, x.shape[1], B.EPS_DEFAULT, xq[g].data_ptr(),
+                sc[g].data_ptr(), B._stream()))
+
+        def gemm(nm, l):
+            d = mats[nm]
+            B.forward(xq[d["group"]], sc[d["group"]], d["packed"][l], d["gamma"], d["n"],
+                      d["k"], relu2=d["relu2"], y=ys[nm], workspace=ws)
+
+        for l in range(layers):
+            for grp in order:
+                if m <= 2 or (m <= B.BL_FUSED_MAX_M and len(grp) > 1):
                     ops = [dict(x=xs[mats[nm]["group"]], packed=mats[nm]["packed"][l],
                                 gamma=mats[nm]["gamma"], n=mats[nm]["n"], k=mats[nm]["k"],
                                 y=ys[nm], relu2=mats[nm]["relu2"]) for nm in grp]
                     calls.append(B.FusedStep(ops, workspace=ws))
-        else:
-            xq = {g: torch.empty((m, B.padded_k(x.shape[1])), dtype=torch.int8, device="cuda")
-                  for g, x in xs.items()}
-            sc = {g: torch.empty(m, dtype=torch.float32, device="cuda") for g in xs}
-            ws.get(max(B.forward_workspace_bytes(m, d["n"], d["k"]) for d in mats.values()))
-
-            def quant(g):
-                x = xs[g]
-                B._check("quant", lib.bitlinear_quant_act(
-                    x.data_ptr(), B.BL_BF16, m, x.shape[1], B.EPS_DEFAULT, xq[g].data_ptr(),
-                    sc[g].data_ptr(), B._stream()))
-
-            def gemm(nm, l):
-                d = mats[nm]
-                B.forward(xq[d["group"]], sc[d["group"]], d["packed"][l], d["gamma"], d["n"],
-                          d["k"], relu2=d["relu2"], y=ys[nm], workspace=ws)
-
-            for l in range(layers):
-                for grp in order:
+                else:
                     calls.append(lambda g=mats[grp[0]]["group"]: quant(g))
                     for nm in grp:
                         calls.append(lambda nm=nm, l=l: gemm(nm, l))

@@ -141,6 +141,8 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
 }
 
 struct FusedPlan {
+  bool mfma = false;                    // 3..16 tokens: the fused MFMA kernel
+  int variant = 0;                      // its wave layout
   int waves = 8;
   int qpl = 4;                          // 16-byte q-parts per lane (rows per group / 16)
   int groups = 0;
@@ -157,6 +159,24 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   // ~T-chunk ranges.  4 waves per group for decode-sized sets (T < 16), 8
   // for large ones.  (Tuned on MI355X over the 2B- and 100B-class shapes.)
   FusedPlan p;
+  if (m >= 3) {
+    // Matrix cores: two 16-row groups x 4 K-slices per workgroup, or for
+    // sets with >= 256 row blocks in an entry four 32-row groups with the
+    // whole K per wave; no K split over workgroups, no workspace.
+    int64_t nbmax = 0;
+    for (int i = 0; i < nops; ++i) {
+      const int64_t nb = cdiv(ops[i].n, kRowBlock);
+      if (nb > nbmax) nbmax = nb;
+    }
+    p.mfma = true;
+    p.variant = nbmax >= 256 ? 1 : 0;
+    const int rows_per_group = p.variant == 0 ? 2 : 8;   // 16-row sub-blocks per workgroup
+    for (int i = 0; i < nops; ++i) {
+      p.splits[i] = 1;
+      p.groups += (int)cdiv(cdiv(ops[i].n, kRowBlock) * 4, rows_per_group);
+    }
+    return p;
+  }
   int64_t units = 0;
   for (int i = 0; i < nops; ++i) units += cdiv(ops[i].n, kRowBlock) * cdiv(ops[i].k, kSuperK);
   int64_t t = cdiv(units, 512);
@@ -293,7 +313,19 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
     args.wg_begin[i] = begin;
     if (sg.splits > 1)
       sg.slots = reinterpret_cast<int64_t*>(reinterpret_cast<char*>(workspace) + plan.slot_off[i]);
-    begin += (int)(cdiv(o.n, kRowBlock) * (4 / plan.qpl) * sg.splits);
+    begin += plan.mfma ? (int)cdiv(cdiv(o.n, kRowBlock) * 4, plan.variant == 0 ? 2 : 8)
+                       : (int)(cdiv(o.n, kRowBlock) * (4 / plan.qpl) * sg.splits);
+  }
+  if (plan.mfma) {
+    bool all_bf16 = true, all_fast = true;
+    for (int i = 0; i < nops; ++i) {
+      const int64_t esize = ops[i].x_dtype == BL_BF16 ? 2 : 4;
+      all_bf16 = all_bf16 && ops[i].x_dtype == BL_BF16;
+      all_fast = all_fast && ops[i].k * esize % 16 == 0 && aligned(ops[i].x, 16);
+    }
+    const hipError_t e = launch_gemv_mfma_fused(args, (int)m, plan.variant, all_bf16, all_fast,
+                                                begin, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BL_OK : BL_ERR_HIP;
   }
   bool long_rows = false;                            // a row of more than 1024 16-byte units
   for (int i = 0; i < nops; ++i)

@@ -4,10 +4,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 typedef int32_t bl_v4i __attribute__((ext_vector_type(4)));
 typedef int32_t bl_v16i __attribute__((ext_vector_type(16)));
 
 namespace bl {
+
+// f(std::integral_constant<int, 0>{}), ..., f(<N - 1>): array slots chosen
+// at compile time stay in registers
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr int kRowBlock = 64;     // rows per packed block
 constexpr int kSuperK = 256;      // inputs per packed super-chunk

@@ -77,6 +77,8 @@ hipError_t launch_gemv_mfma(int variant, const int8_t* xq, const float* scale,
                             const uint32_t* packed, const float* gamma, int64_t m, int64_t n,
                             int64_t k, bool relu2, bool bf16, void* y, int32_t* acc_out,
                             hipStream_t stream);
+hipError_t launch_gemv_mfma_fused(const FusedArgs& args, int m, int variant, bool all_bf16,
+                                  bool all_fast, int groups, hipStream_t stream);
 hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, int qpl, bool long_rows,
                              int groups, size_t lds, hipStream_t stream);
 

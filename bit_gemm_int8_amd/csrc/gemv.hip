@@ -526,6 +526,257 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) 
                 sg.y_bf16());
 }
 
+// ----------------------------------------------------- fused MFMA decode --
+// The fused decode step for 3 to 16 tokens: the entries' products on
+// v_mfma_i32_16x16x64_i8 as in the windowed MFMA GEMV (unpacked weights of
+// 16 rows as the first operand, x~ of 16 tokens as the second, x~ through
+// two LDS windows per K-slice, one barrier per super-chunk), with the
+// activation quant of each entry done by every workgroup:
+//   1. the first weight loads are issued;
+//   2. max|x| per token over its whole row (every thread reads units of
+//      every token; idempotent, so loads past the row or past token m-1
+//      read a valid unit again), reduced with DPP and across waves in LDS,
+//      and s = 127 / max(beta, eps) exactly as bitlinear_quant_act;
+//   3. each window is staged from x itself: the 16 inputs of an x~ unit are
+//      loaded (two bf16 or four fp32 16-byte units), quantized with the
+//      token's s and stored to LDS (and to xq_out by the entry's first
+//      workgroup).
+// Workgroup g of an entry owns WR row groups of SB 16-row sub-blocks; its
+// WK waves per group split the super-chunks and meet in LDS at the end.
+template <int WR, int WK, int SB, int PF, int RPU, int MT, bool FAST>
+__global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(FusedArgs args, int m) {
+  static_assert(RPU == 2 || RPU == 4, "16-byte activation units per x~ unit: 2 (bf16 only), 4");
+  // FAST: every entry's rows are whole 16-byte units at 16-byte alignment,
+  // so the activation loads are plain vector loads with no branch (a load
+  // behind a branch makes the compiler wait for every load in flight)
+  static_assert(SB == 1 || SB == 2 || SB == 4, "a wave's sub-blocks lie in one packed block");
+  static_assert(PF == 2 || PF == 4, "the loop is unrolled by PF, an even number");
+  static_assert(MT == 8 || MT == 16, "tokens handled: m <= MT");
+  constexpr int WAVES = WR * WK, NT = 64 * WAVES;
+  constexpr int NTS = 64 * WR;                      // threads staging one slice
+  constexpr int XU = MT * 16 / NTS;                 // x~ units per staging thread and step
+  static_assert(MT * 16 % NTS == 0, "x~ staging split");
+  __shared__ bl_v4i xs[WK][2][256];
+  __shared__ int red[WK > 1 ? (WK - 1) * WR : 1][SB * 4][64];
+  __shared__ uint32_t bmax[WAVES][MT];
+  __shared__ float s_lds[16];
+  __shared__ float fac_lds[16];
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxFused; ++i)
+    if (i < args.nseg && (int)blockIdx.x >= args.wg_begin[i]) si = i;
+  const FusedSeg& sg = args.seg[si];
+  const int local = (int)blockIdx.x - sg.wg_begin;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wr = wave / WK, wk = wave - wr * WK;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int nc = sg.nc;
+  const int nsub = (sg.n + kRowBlock - 1) / kRowBlock * 4;
+  int u0 = (local * WR + wr) * SB;
+  const bool live = u0 < nsub;
+  if (!live) u0 = nsub - SB;
+  const int b = u0 >> 2, sub0 = u0 & 3;
+  const int L = (nc + WK - 1) / WK;
+  const int c0 = wk * L;
+  const int c1 = min(c0 + L, nc);
+  const int clast = c1 > c0 ? c1 - 1 : nc - 1;
+  const uint4* blk = reinterpret_cast<const uint4*>(sg.packed) + (int64_t)b * nc * kBlockU4 +
+                     g * 64 + sub0 * 16 + r;
+
+  // 1. weights of the first PF super-chunks
+  uint4 wb[PF][SB];
+  static_for<PF>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    const int c = min(c0 + p, clast);
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) wb[p][sb] = blk[(int64_t)c * kBlockU4 + sb * 16];
+  });
+  const float gam = *sg.gamma;
+
+  // 2. per-token max|x| (tokens >= m repeat token m-1)
+  const XRow xrow = x_row_info(sg);
+  const bool xbf = sg.x_bf16();
+  {
+    uint32_t mx[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) mx[t] = 0;
+    const int iters = (xrow.nu + NT - 1) / NT;       // the same count in every thread
+    for (int it = 0; it < iters; ++it) {
+      const int uu = min((int)threadIdx.x + NT * it, xrow.nu - 1);
+      uint4 v[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        v[t] = FAST ? reinterpret_cast<const uint4*>(x_row(sg, min(t, m - 1)))[uu]
+                    : load_unit(sg, xrow, x_row(sg, min(t, m - 1)), uu);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) mx[t] = max(mx[t], absmax_unit(xbf, v[t]));
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint32_t w = wave_max_u32(mx[t]);
+      if (lane == 0) bmax[wave][t] = w;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < MT) {
+    uint32_t bt = bmax[0][threadIdx.x];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) bt = max(bt, bmax[w][threadIdx.x]);
+    const float sv = (float)(127.0 / (double)fmaxf(__uint_as_float(bt), args.eps));
+    s_lds[threadIdx.x] = sv;
+    fac_lds[threadIdx.x] = gamma_over_s(gam, sv);
+    if (local == 0 && sg.scale_out != nullptr && (int)threadIdx.x < m)
+      sg.scale_out[threadIdx.x] = sv;
+  }
+  __syncthreads();
+
+  // 3. this thread's x~ units of its slice: token t = q / 16, unit q % 16
+  //    (inputs 16 (q % 16) .. + 15 of each super-chunk)
+  const int epu = xrow.epu;                         // activations per 16-byte unit: 8 or 4
+  const char* xsrc[XU];
+  int xdst[XU], xtok[XU], xq16[XU];
+  float xsc[XU];
+#pragma unroll
+  for (int i = 0; i < XU; ++i) {
+    const int q = wr * 64 + lane + NTS * i;
+    const int t = q >> 4, u = q & 15;
+    xtok[i] = t;
+    xq16[i] = u;
+    xsrc[i] = x_row(sg, min(t, m - 1));
+    xdst[i] = t * 16 + (u ^ (t & 15));
+    xsc[i] = s_lds[t];
+  }
+  // raw activations of a step's units: RPU 16-byte units each (bf16 uses
+  // the first two of four)
+  uint4 xr[PF][XU][RPU];
+  auto load_x = [&](auto P, int c) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+#pragma unroll
+    for (int i = 0; i < XU; ++i)
+#pragma unroll
+      for (int e = 0; e < RPU; ++e) {
+        const int u = (c * 256 + xq16[i] * 16) / epu + e;
+        xr[p][i][e] = FAST ? reinterpret_cast<const uint4*>(xsrc[i])[min(u, xrow.nu - 1)]
+                           : load_unit(sg, xrow, xsrc[i], min(u, xrow.nu - 1));
+      }
+  };
+  // x~ of one unit from its raw activations (zero past the row)
+  auto quant_unit = [&](const uint4 (&raw)[RPU], float sc, int c, int q16)
+      __attribute__((always_inline)) {
+    const int k0 = c * 256 + q16 * 16;
+    uint32_t d[4];
+    if (xbf) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t e[8];
+        expand_unit(true, raw[h], e);
+        d[2 * h] = quant4(e, sc);
+        d[2 * h + 1] = quant4(e + 4, sc);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        uint32_t e[8];
+        expand_unit(false, raw[h < RPU ? h : 0], e);
+        d[h] = quant4(e, sc);
+      }
+    }
+    bl_v4i out = {(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
+    if (k0 >= sg.k) out = bl_v4i{0, 0, 0, 0};
+    else if (k0 + 16 > sg.k) {                      // the row ends inside this unit
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = k0 + 4 * j;                  // bytes of dword j: inputs kk .. kk+3
+        const int keep = max(0, min(4, sg.k - kk));
+        const uint32_t mask = keep >= 4 ? 0xFFFFFFFFu : (1u << (8 * keep)) - 1u;
+        out[j] = (int)((uint32_t)out[j] & mask);
+      }
+    }
+    return out;
+  };
+  static_for<PF>([&](auto P) { load_x(P, min(c0 + (int)P, clast)); });
+
+  bl_v4i acc[SB];
+#pragma unroll
+  for (int sb = 0; sb < SB; ++sb) acc[sb] = bl_v4i{0, 0, 0, 0};
+  const bool write_xq = local == 0 && sg.xq_out != nullptr;
+  const int64_t kpad = (int64_t)nc * 256;
+  auto step = [&](auto P, int c) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    bl_v4i* win = xs[wk][p & 1];
+#pragma unroll
+    for (int i = 0; i < XU; ++i) {
+      const bl_v4i qv = quant_unit(xr[p][i], xsc[i], c, xq16[i]);
+      win[xdst[i]] = qv;
+      if (write_xq && c < c1 && xtok[i] < m)
+        *reinterpret_cast<bl_v4i*>(sg.xq_out + (int64_t)xtok[i] * kpad + c * 256 + xq16[i] * 16) =
+            qv;
+    }
+    __syncthreads();
+    const int cn = min(c + PF, clast);
+    load_x(P, cn);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c < c1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bl_v4i xv = win[r * 16 + ((4 * j + g) ^ r)];
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+          const uint32_t wj = j == 0 ? wb[p][sb].x : j == 1 ? wb[p][sb].y
+                            : j == 2 ? wb[p][sb].z : wb[p][sb].w;
+          const bl_v4i a = {(int)unpack_x64(wj, 0), (int)unpack_x64(wj, 1),
+                            (int)unpack_x64(wj, 2), (int)unpack_x64(wj, 3)};
+          acc[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xv, acc[sb], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) wb[p][sb] = blk[(int64_t)cn * kBlockU4 + sb * 16];
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int t = 0;
+  for (; t + PF <= L; t += PF) static_for<PF>([&](auto P) { step(P, c0 + t + (int)P); });
+  static_for<PF - 1>([&](auto P) {
+    if (t + (int)P < L) step(P, c0 + t + (int)P);
+  });
+
+  // the slices' sums into the group's first wave
+  if (WK > 1) {
+    if (wk > 0) {
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wr * (WK - 1) + wk - 1][sb * 4 + i][lane] = acc[sb][i];
+    }
+    __syncthreads();
+    if (wk > 0) return;
+#pragma unroll
+    for (int w = 0; w < WK - 1; ++w)
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[sb][i] += red[wr * (WK - 1) + w][sb * 4 + i][lane];
+  }
+  // lane (r, g) holds rows 4g..4g+3 of each sub-block for token r (columns
+  // of tokens >= MT read window slots never staged; they are dropped)
+  if (!live || r >= m) return;
+  const float f = fac_lds[r];
+  const bool relu2 = sg.relu2(), ybf = sg.y_bf16();
+#pragma unroll
+  for (int sb = 0; sb < SB; ++sb) {
+    const int row0 = b * 64 + (sub0 + sb) * 16 + 4 * g;
+    const int64_t idx = (int64_t)r * sg.n + row0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (row0 + i >= sg.n) continue;
+      const int a = acc[sb][i] >> 6;
+      if (sg.acc_out != nullptr) sg.acc_out[idx + i] = a;
+      store_out(sg.y, idx + i, a, f, relu2, ybf);
+    }
+  }
+}
+
 }  // namespace
 
 // Plain GEMV: x~ and s given.
@@ -559,6 +810,34 @@ hipError_t launch_gemv(int m, int waves, int pf, int qpl, const int8_t* xq, cons
 #undef BL_GEMV
 }
 
+// Fused decode step for 3 to 16 tokens on the matrix cores: variant 0 = two
+// 16-row groups x 4 K-slices, 1 = four 32-row groups (whole K per wave).
+// all_bf16: every entry's x is bf16 (two 16-byte loads per x~ unit, not
+// four); all_fast: every entry's rows are whole, aligned 16-byte units.
+hipError_t launch_gemv_mfma_fused(const FusedArgs& args, int m, int variant, bool all_bf16,
+                                  bool all_fast, int groups, hipStream_t stream) {
+  if (m < 1 || m > 16) return hipErrorInvalidValue;
+#define BL_MF(WR, WK, SB, PF, RPU, MT, FAST)                                         \
+  gemv_mfma_fused_kernel<WR, WK, SB, PF, RPU, MT, FAST>                              \
+      <<<(unsigned)groups, 64 * WR * WK, 0, stream>>>(args, m)
+#define BL_MF_X(WR, WK, SB, PF, MT)               \
+  if (all_fast && all_bf16) BL_MF(WR, WK, SB, PF, 2, MT, true); \
+  else if (all_fast) BL_MF(WR, WK, SB, PF, 4, MT, true);       \
+  else BL_MF(WR, WK, SB, PF, 4, MT, false)
+  if (variant == 0) {
+    if (m <= 8) {
+      BL_MF_X(2, 4, 1, 2, 8);
+    } else {
+      BL_MF_X(2, 4, 1, 2, 16);
+    }
+  } else {
+    BL_MF_X(4, 1, 2, 4, 16);
+  }
+#undef BL_MF_X
+#undef BL_MF
+  return hipGetLastError();
+}
+
 // Fused decode step over a complete segment table (wg_begin, splits and
 // workspace pointers filled in).  long_rows: one token and some row longer
 // than 1024 16-byte units.
@@ -588,8 +867,6 @@ hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, int qpl, b
       }
       BL_FUSED_W(1, false);
     case 2: BL_FUSED_W(2, false);
-    case 3: BL_FUSED_W(3, false);
-    case 4: BL_FUSED_W(4, false);
     default: return hipErrorInvalidValue;
   }
 #undef BL_FUSED_W

@@ -21,25 +21,11 @@
 // x~ passes through LDS one super-chunk at a time, shared by the waves of a
 // workgroup, so the rows may be of any length and K is never split over
 // workgroups.
-#include <type_traits>
-#include <utility>
-
 #include "bl_device.h"
 #include "bl_internal.h"
 
 namespace bl {
 namespace {
-
-// f(std::integral_constant<int, 0>{}), ..., f(<N - 1>): array slots chosen
-// at compile time stay in registers
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 // ---------------------------------------------------- windowed MFMA GEMV --
 // Up to 16 * TG tokens.  A workgroup has WR x WK waves: WR row groups,

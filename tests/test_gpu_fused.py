@@ -69,6 +69,14 @@ FUSED_CASES = [
     (4, [(129, 300, True, "f32", "bf16"), (64, 30000, False, "bf16", "f32"),
          (1000, 777, False, "bf16", "bf16")]),
     (1, [(64, 256, False, "f32", "f32")] * 16),
+    # 3 to 16 tokens: int8 matrix cores
+    (8, [(2560, 2560, False, "bf16", "bf16"), (640, 2560, False, "bf16", "bf16"),
+         (6912, 2560, True, "bf16", "bf16")]),                                        # all bf16
+    (16, [(300, 1000, True, "f32", "bf16"), (64, 8200, False, "bf16", "bf16")]),    # K % 16 != 0
+    (12, [(500, 777, False, "bf16", "f32"), (129, 300, True, "f32", "bf16")]),     # odd K, mixed x
+    (5, [(16400, 512, False, "bf16", "bf16")]),                                    # >= 256 row blocks
+    (9, [(64, 64, False, "f32", "f32"), (65, 320, True, "bf16", "bf16")]),         # empty K-slices
+    (16, [(64, 256, False, "f32", "f32")] * 16),
 ]
 
 
@@ -99,25 +107,27 @@ def test_fused_shared_inputs_and_unfused_agree(B):
     assert ws.buf is None or not host(ws.buf).any()
 
 
-def test_fused_c2_decode_set(B):
-    """The batch-1 decode set at 2B-class shapes, full size, one launch."""
+@pytest.mark.parametrize("m", [1, 8])
+def test_fused_c2_decode_set(B, m):
+    """The decode set at 2B-class shapes, full size, one launch (1 token: the
+    dot4 kernel; 8 tokens: the matrix cores)."""
     import torch
     import datagen
     wl = datagen.WORKLOADS["c2"]
     ops, refs = [], []
     xin = {}
     for g in wl.groups():
-        bits, _ = datagen.activations(wl, g, 1)
+        bits, _ = datagen.activations(wl, g, m)
         from gpu_util import dev_bf16
         xin[g] = (dev_bf16(bits), datagen.bf16_bits_to_f32(bits))
     for name, (n, k, relu2, grp) in wl.matrices.items():
         w = datagen.workload_weights(wl, name)
         packed, gamma = B.pack_weights(dev(w))
         ops.append(dict(x=xin[grp][0], packed=packed, gamma=gamma, n=n, k=k, relu2=relu2,
-                        y=torch.empty((1, n), dtype=torch.bfloat16, device="cuda"),
-                        acc_out=torch.empty((1, n), dtype=torch.int32, device="cuda"),
-                        xq_out=torch.empty((1, O.padded_k(k)), dtype=torch.int8, device="cuda"),
-                        scale_out=torch.empty(1, dtype=torch.float32, device="cuda")))
+                        y=torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
+                        acc_out=torch.empty((m, n), dtype=torch.int32, device="cuda"),
+                        xq_out=torch.empty((m, O.padded_k(k)), dtype=torch.int8, device="cuda"),
+                        scale_out=torch.empty(m, dtype=torch.float32, device="cuda")))
         refs.append((w, xin[grp][1], relu2, "bf16"))
     step = B.FusedStep(ops)
     for _ in range(3):                      # repeated calls reuse the workspace
@@ -127,9 +137,9 @@ def test_fused_c2_decode_set(B):
 
 def test_fused_rejects(B):
     import torch
-    x = torch.zeros((5, 256), dtype=torch.float32, device="cuda")
+    x = torch.zeros((17, 256), dtype=torch.float32, device="cuda")
     packed, gamma = B.pack_weights(torch.zeros((64, 256), dtype=torch.float32, device="cuda"))
-    y = torch.empty((5, 64), dtype=torch.float32, device="cuda")
+    y = torch.empty((17, 64), dtype=torch.float32, device="cuda")
     with pytest.raises(B.BitLinearError) as e:
         B.forward_fused([dict(x=x, packed=packed, gamma=gamma, n=64, k=256, y=y)])
-    assert e.value.status == 2        # m = 5 > 4
+    assert e.value.status == 2        # m = 17 > 16
