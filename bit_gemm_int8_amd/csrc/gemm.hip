@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ scale,
     const uint4* __restrict__ packed, const float* __restrict__ gamma, int m, int n,
     int nb, int nc, int64_t kpad, int tiles_m, int tiles_n, int band, int relu2,
-    int bf16, int vec_out, void* __restrict__ y, int32_t* __restrict__ acc_out) {
+    int bf16, int vec_out, int line_out, void* __restrict__ y, int32_t* __restrict__ acc_out) {
   using T = TileW<FM, WN, KS>;
   constexpr int BM = T::BM, BN = T::BN, NT = T::NT, UA = T::UA;
   // two stages as separate arrays: the compiler then sees that the copies
@@ -254,6 +254,92 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
     fac[t] = gm < m ? gamma_over_s(gam, scale[gm]) : 0.0f;
   }
   __syncthreads();
+  // bf16 output in whole lines: a wave's 32*FM x 64 block is one 128-byte
+  // line per row.  The scaled values go to LDS (row-major, 16-byte chunk q of
+  // row r at q ^ (r % 8), so neither side conflicts on banks) and come back
+  // as 16-byte pieces, eight lanes per line: every store instruction writes
+  // eight whole lines, which the memory system takes far better than the
+  // accumulator layout's 16-byte pieces of 32 rows.  Tall tiles (one round
+  // of tiles that all end together) store non-temporally, which measured
+  // faster there; the 64-row tiles run in several rounds and keep ordinary
+  // stores, which measured faster for them.
+  if (line_out) {                                        // uniform
+    float fr[FM];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) fr[fm] = fac[32 * fm + c];
+    __syncthreads();                                     // all fac reads done
+    constexpr int S = 32 * FM * 128;                     // LDS bytes per wave
+    constexpr int NA = T::A_BYTES / S, NB = T::B_BYTES / S;
+    static_assert(2 * NA + 2 * NB >= WN, "line staging space");
+    uint8_t* buf = wave < NA ? A0 + wave * S
+                 : wave < 2 * NA ? A1 + (wave - NA) * S
+                 : wave < 2 * NA + NB ? B0 + (wave - 2 * NA) * S
+                 : B1 + (wave - 2 * NA - NB) * S;
+    const int col0 = (tn * WN + wave) * 64;
+    if (col0 + 64 <= n) {                                // whole block inside the output
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int r = 32 * fm + c;
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            int v[4];
+            float o[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              v[t] = acc[fm][fn][4 * g + t] >> 6;
+              o[t] = (float)v[t] * fr[fm];
+              if (relu2) o[t] = o[t] > 0.0f ? o[t] * o[t] : 0.0f;
+            }
+            if (acc_out != nullptr && m0 + r < m)
+              *reinterpret_cast<int4*>(acc_out + (int64_t)(m0 + r) * n + col0 + 32 * fn + 8 * g + 4 * ph) =
+                  make_int4(v[0], v[1], v[2], v[3]);
+            const int q = 4 * fn + g;
+            *reinterpret_cast<uint2*>(buf + r * 128 + ((q ^ (r & 7)) << 4) + ph * 8) =
+                make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+          }
+      }
+      // the wave reads back only its own block: LDS operations of one wave
+      // complete in order, and the barrier keeps the compiler from moving
+      // the reads above the writes
+      __builtin_amdgcn_wave_barrier();
+      const int q = lane & 7;
+#pragma unroll
+      for (int i = 0; i < 4 * FM; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        const bl_v4i v = *reinterpret_cast<const bl_v4i*>(buf + r * 128 + ((q ^ (r & 7)) << 4));
+        if (m0 + r < m) {
+          bl_v4i* dst = reinterpret_cast<bl_v4i*>(reinterpret_cast<uint16_t*>(y) +
+                                                 (int64_t)(m0 + r) * n + col0 + 8 * q);
+          if (FM >= 3)
+            __builtin_nontemporal_store(v, dst);
+          else
+            *dst = v;
+        }
+      }
+    } else {                                             // the column tail
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int gm = m0 + 32 * fm + c;
+        if (gm >= m) continue;
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int gn = col0 + 32 * fn + 8 * g + 4 * ph;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              if (gn + t >= n) continue;
+              const int a = acc[fm][fn][4 * g + t] >> 6;
+              if (acc_out != nullptr) acc_out[(int64_t)gm * n + gn + t] = a;
+              store_out(y, (int64_t)gm * n + gn + t, a, fr[fm], relu2 != 0, true);
+            }
+          }
+      }
+    }
+    return;
+  }
   // Each group of four accumulator elements is four consecutive columns of
   // one row: whole groups go out as one 16-byte (fp32, int32) or 8-byte
   // (bf16) store when vec_out (n % 4 == 0 and aligned outputs); the column
@@ -314,9 +400,11 @@ hipError_t runw(const int8_t* xq, const float* scale, const uint32_t* packed, co
   const int64_t grid = (int64_t)tiles_m * tiles_n;
   const int vec_out = n % 4 == 0 && (uintptr_t)y % (bf16 ? 8 : 16) == 0 &&
                       (acc_out == nullptr || (uintptr_t)acc_out % 16 == 0);
+  // whole 16-byte pieces of bf16 rows: n % 8 == 0 and a 16-byte aligned y
+  const int line_out = bf16 && vec_out && n % 8 == 0 && (uintptr_t)y % 16 == 0;
   gemmw_kernel<FM, WN, KS><<<(unsigned)grid, T::NT, 0, stream>>>(
       xq, scale, reinterpret_cast<const uint4*>(packed), gamma, (int)m, (int)n, nb, nc,
-      padded_k(k), tiles_m, tiles_n, band, relu2, bf16, vec_out, y, acc_out);
+      padded_k(k), tiles_m, tiles_n, band, relu2, bf16, vec_out, line_out, y, acc_out);
   return hipGetLastError();
 }
 

@@ -202,6 +202,8 @@ FWD_CASES = [
     (1100, 9001, 300, True, "bf16", "bf16"),     # 64 x 256, ragged M, odd N
     (1536, 10240, 300, True, "bf16", "bf16"),    # 128 x 512 tiles
     (2000, 2560, 320, False, "bf16", "bf16"),    # 96 x 256 tiles, ragged M
+    (1000, 6200, 300, True, "bf16", "bf16"),     # whole-line bf16 rows, a column-tail wave
+    (1500, 4104, 520, False, "bf16", "f32"),     # whole lines, 8-column tail
 ]
 
 
@@ -314,6 +316,22 @@ def test_forward_no_write_past_output(B):
         assert torch.all(buf[m * n:] == -7.0).item()
         r = O.forward(x, w, gamma=host(gamma)[0])
         assert_y_close(host(y), r["y"], "f32")
+
+
+def test_gemm_bf16_lines_stay_inside_output(B):
+    # bf16 rows leave the GEMM as whole 16-byte pieces; nothing past the
+    # output (ragged M and N) may change
+    import torch
+    for (m, n, k) in [(1000, 6200, 300), (1100, 8192, 256)]:
+        w, x = random_case(m + n + 1, m, n, k, x_kind="t3")
+        packed, gamma = B.pack_weights(dev(w))
+        xq, s = B.quant_act(dev(x))
+        buf = torch.full((m * n + 8192,), -7.0, dtype=torch.bfloat16, device="cuda")
+        y = buf[: m * n].view(m, n)
+        B.forward(xq, s, packed, gamma, n, k, y=y, relu2=True)
+        assert torch.all(buf[m * n:] == -7.0).item()
+        r = O.forward(x, w, relu2=True, y_dtype="bf16", gamma=host(gamma)[0])
+        assert_y_close(host(y), r["y"], "bf16", f"m={m} n={n}")
 
 
 def test_forward_empty_batch(B):
