@@ -43,7 +43,7 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
 hipError_t launch_fill_zero(uint32_t* p, size_t words, hipStream_t stream);
 
 // Fused decode step: a table of BitLinear products that share a token batch
-// (M <= 4), each quantizing its own activations in the kernel prologue.
+// (M <= 16), each quantizing its own activations in the kernel prologue.
 constexpr int kMaxFused = 16;
 // One entry of the fused decode step.  The fields a workgroup needs first
 // share the first 64-byte line (one scalar load after the entry is known);

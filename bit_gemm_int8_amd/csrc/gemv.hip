@@ -1,6 +1,6 @@
-// Decode ternary GEMV for a few tokens (M <= 4) with the fused dequant, and
-// the fused decode step (activation quantization + GEMV for several matrices
-// in one launch).
+// Decode ternary GEMV for one or two tokens with the fused dequant, and the
+// fused decode step (activation quantization + products of several matrices
+// in one launch): v_dot4 for 1-2 tokens, int8 matrix cores for 3-16.
 //
 // "BitNet b1.58 2B4T Guide: Scaling Native 1-Bit LLMs", section "Matrix
 // Multiplication as Pure Integer Addition": acc = x~ W~^T in an integer
