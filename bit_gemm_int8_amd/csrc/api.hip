@@ -157,7 +157,11 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   // groups, kept within [8, 32].  Entries with up to 2T super-chunks keep
   // one group per row block; longer ones are split (atomic combine) into
   // ~T-chunk ranges.  4 waves per group for decode-sized sets (T < 16), 8
-  // for large ones.  (Tuned on MI355X over the 2B- and 100B-class shapes.)
+  // for large ones.  Rows per group: 16 (four lanes per row) when that
+  // keeps the set within 512 groups, else 64 (a lane per row): small sets
+  // are bound by each lane's unpack + dot4 work after the data arrive, large
+  // ones by the number of groups, each of which reads and quantizes its x
+  // range.  (Tuned on MI355X over the 2B- and 100B-class shapes.)
   FusedPlan p;
   if (m >= 3) {
     // Matrix cores: two 16-row groups x 4 K-slices per workgroup, or for
@@ -182,12 +186,20 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   int64_t t = cdiv(units, 512);
   t = t < 8 ? 8 : t > 32 ? 32 : t;
   p.waves = t >= 16 ? 8 : 4;
-  size_t slots = 0;
-  for (int i = 0; i < nops; ++i) {
-    const int64_t nb = cdiv(ops[i].n, kRowBlock), nc = cdiv(ops[i].k, kSuperK);
+  auto splits_of = [&](int64_t nc) {
     int64_t s = nc <= 2 * t ? 1 : cdiv(nc, t);
     if (s > 8) s = 8;
     while (m * cdiv(nc, s) * 256 > kGemvMaxLds) ++s;
+    return s;
+  };
+  int64_t groups16 = 0;                              // groups with 16 rows each
+  for (int i = 0; i < nops; ++i)
+    groups16 += cdiv(ops[i].n, kRowBlock) * 4 * splits_of(cdiv(ops[i].k, kSuperK));
+  p.qpl = groups16 <= 512 ? 1 : 4;
+  size_t slots = 0;
+  for (int i = 0; i < nops; ++i) {
+    const int64_t nb = cdiv(ops[i].n, kRowBlock), nc = cdiv(ops[i].k, kSuperK);
+    const int64_t s = splits_of(nc);
     p.splits[i] = (int)s;
     p.groups += (int)(nb * (4 / p.qpl) * s);
     const size_t lds = (size_t)(m * cdiv(nc, s) * 256);

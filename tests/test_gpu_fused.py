@@ -69,6 +69,9 @@ FUSED_CASES = [
     (4, [(129, 300, True, "f32", "bf16"), (64, 30000, False, "bf16", "f32"),
          (1000, 777, False, "bf16", "bf16")]),
     (1, [(64, 256, False, "f32", "f32")] * 16),
+    (1, [(100, 20000, True, "bf16", "bf16")]),                                     # long row, split K, 16-row groups
+    (1, [(2560, 2560, False, "bf16", "bf16"), (6912, 2560, True, "bf16", "bf16"),
+         (2560, 6912, False, "bf16", "bf16")]),                                     # 64-row groups
     # 3 to 16 tokens: int8 matrix cores
     (8, [(2560, 2560, False, "bf16", "bf16"), (640, 2560, False, "bf16", "bf16"),
          (6912, 2560, True, "bf16", "bf16")]),                                        # all bf16
