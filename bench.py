@@ -51,6 +51,7 @@ INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA, 5.0 POPS
 CACHE_BYTES = (256 + 32) << 20   # Infinity Cache + 8 x 4 MB L2
 SIMDS = 256 * 4                  # 256 CUs x 4 SIMDs
 XCDS = 8
+CLOCK_GHZ = 2.4                 # MI355X peak engine clock
 
 
 def log(msg: str) -> None:
@@ -506,8 +507,24 @@ def recorded_traffic():
 def pmc_driver(B, torch, args):
     """Launches to read counters from.  decode: a plain copy of COPY_BYTES
     (the calibration), then eager fused decode steps over rotating weight
-    copies.  prefill: the two 2048-token prefill GEMMs, `steps` times each."""
+    copies.  prefill: the two 2048-token prefill GEMMs, `steps` times each.
+    gemv: the 100B-class up and down products at one token (plain GEMV),
+    `steps` times each over rotating weight copies."""
     import datagen
+    if args.pmc_driver == "gemv":
+        wl = datagen.WORKLOADS["c5"]
+        ds = DecodeSet(B, torch, wl, 1, 1, names=["up", "down"])
+        copies = max(2, math.ceil(2 * CACHE_BYTES / B.packed_bytes(*wl.matrices["up"][:2])))
+        for name in ("up", "down"):
+            d = ds.mats[name]
+            d["packed"] = d["packed"] + [d["packed"][0].clone() for _ in range(copies - 1)]
+            for i in range(args.steps):
+                ds.forward_one(name, i % copies)
+            torch.cuda.synchronize()
+            d["packed"] = d["packed"][:1]
+            torch.cuda.empty_cache()
+        print(json.dumps({"pmc_driver": "gemv", "steps": args.steps, "copies": copies}))
+        return
     if args.pmc_driver == "prefill":
         wl = datagen.WORKLOADS["c4"]
         for name in ("up", "down"):
@@ -626,6 +643,29 @@ def summarize(directory, command, name):
             lines.append(f"| {k} | {f(us, '.2f')} | {f(ghz, '.3f')} | {f(busy, '.0f')} | "
                          f"{f(act, '.0f')} | {f(util, '.3f')} | {f(ops, '.4g')} | {f(tops, '.0f')} |")
         out.append((f"{name}_mfma_counters.md", "\n".join(lines) + "\n"))
+    if "SQ_ACTIVE_INST_VALU" in ctrs:
+        kernels = sorted({k for (k, c), xs in vals.items()
+                          if c == "SQ_INSTS_VALU" and max(xs) > 0 and "gemv" in k})
+        lines = ["# VALU counters of the batch-1 GEMV (rocprofv3 --pmc)", "",
+                 f"Command: `{command}`", "",
+                 "Medians per dispatch.  VALU busy = SQ_ACTIVE_INST_VALU x 4 (the counter is in "
+                 f"quad-cycles) / ({SIMDS} SIMDs x the kernel's duration at {CLOCK_GHZ} GHz); for "
+                 "dispatches this short GRBM_GUI_ACTIVE / 8 XCDs implies a clock above the "
+                 "part's peak (the counter window is wider than the kernel), so it is shown but "
+                 "not used.  VALU lane-ops per 1000 weights = SQ_INSTS_VALU x 64 lanes / weights "
+                 "of the matrix x 1000 (one 28672 x 8192 matrix per dispatch).", "",
+                 "| kernel | us | SQ_INSTS_VALU | SQ_ACTIVE_INST_VALU | GRBM_GUI_ACTIVE | "
+                 "VALU busy | VALU lane-ops per 1000 weights |", "|---|---|---|---|---|---|---|"]
+        for k in kernels:
+            insts, act_v, act = (med(k, "SQ_INSTS_VALU"), med(k, "SQ_ACTIVE_INST_VALU"),
+                                 med(k, "GRBM_GUI_ACTIVE"))
+            us = statistics.median(durs[k]) if durs.get(k) else None
+            busy = act_v * 4 / (SIMDS * us * 1e3 * CLOCK_GHZ) if act_v and us else None
+            per_w = insts * 64 / (28672 * 8192) * 1000 if insts else None
+            f = lambda v, fmt: "-" if v is None else format(v, fmt)
+            lines.append(f"| {k} | {f(us, '.2f')} | {f(insts, '.0f')} | "
+                         f"{f(act_v, '.0f')} | {f(act, '.0f')} | {f(busy, '.3f')} | {f(per_w, '.0f')} |")
+        out.append((f"{name}_valu_counters.md", "\n".join(lines) + "\n"))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for fname, text in out:
         with open(os.path.join(ROOT, "profiles", fname), "w") as f:
@@ -640,9 +680,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip prefill and 100B-class legs")
-    ap.add_argument("--pmc-driver", nargs="?", const="decode", choices=["decode", "prefill"],
+    ap.add_argument("--pmc-driver", nargs="?", const="decode", choices=["decode", "prefill", "gemv"],
                     help="only launch what the counters are read from: the fused decode "
-                         "step (HBM traffic) or the prefill GEMMs (MFMA)")
+                         "step (HBM traffic), the prefill GEMMs (MFMA) or the batch-1 "
+                         "100B-class GEMVs (VALU)")
     ap.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSVs")
     ap.add_argument("--name", default="gemv_fused_decode_2b",
                     help="kernel and workload the summaries are named for")
