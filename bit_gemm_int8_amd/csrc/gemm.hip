@@ -25,11 +25,14 @@ __device__ __forceinline__ void lds_copy16(const void* src, void* lds_wave_base)
 // Waves sit side by side along N (one row of WN waves); each wave owns one
 // 64-row packed block (two 32-column fragments) and 32*FM tile rows, so
 // every unpacked weight word feeds FM MFMAs and no block is unpacked by two
-// waves.  x~ and the packed blocks go
-// global -> LDS by DMA (each wave copies and reads only its own block), two
-// stages of KS super-chunks each: the copies of the next stage are in flight
-// while the current one is computed, so larger KS covers a longer load
-// latency.
+// waves.  x~, which all waves share, goes global -> LDS by DMA in two
+// stages of KS super-chunks each: the copies of the next stage are in
+// flight while the current one is computed.  The packed words are private
+// to their wave, so they skip LDS: each lane loads its 16 words of a
+// super-chunk as dwords straight into registers, component j of the next
+// super-chunk into the registers that component j of the current one has
+// just left (no LDS traffic for the weights, no extra registers, and the
+// barrier only publishes x~).
 //
 // v_mfma_i32_32x32x32_i8 lanes: lane l = c + 32 ph (c = l % 32, ph = l / 32)
 // supplies row/column c of its operand for 16 inputs; a super-chunk is 8
@@ -55,11 +58,9 @@ struct TileW {
   static constexpr int NT = 64 * WN;
   static constexpr int UA = BM * 16 / NT;          // A copy instructions per thread and chunk
   static constexpr int A_CHUNK = BM * 256;         // x~ bytes per super-chunk
-  static constexpr int B_CHUNK = WN * 4096;        // packed bytes per super-chunk
   static constexpr int A_BYTES = KS * A_CHUNK;     // one stage
-  static constexpr int B_BYTES = KS * B_CHUNK;
   static_assert(BM * 16 % NT == 0, "copy split");
-  static_assert(2 * (A_BYTES + B_BYTES) <= 160 * 1024, "LDS");
+  static_assert(2 * A_BYTES <= 160 * 1024, "LDS");
 };
 
 __device__ __forceinline__ int tile_of_block(int bid, int tiles, int tiles_m, int tiles_n,
@@ -77,8 +78,10 @@ __device__ __forceinline__ int tile_of_block(int bid, int tiles, int tiles_m, in
   return tm * tiles_n + tn;
 }
 
+// At least two waves per SIMD (registers within 256 per lane): one wave's
+// waits are covered by the other's MFMAs.
 template <int FM, int WN, int KS>
-__global__ __launch_bounds__(64 * WN) void gemmw_kernel(
+__global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) void gemmw_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ scale,
     const uint4* __restrict__ packed, const float* __restrict__ gamma, int m, int n,
     int nb, int nc, int64_t kpad, int tiles_m, int tiles_n, int band, int relu2,
@@ -90,8 +93,6 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
   // the LDS reads of the stage being computed
   __shared__ __attribute__((aligned(16))) uint8_t A0[T::A_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t A1[T::A_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t B0[T::B_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t B1[T::B_BYTES];
 
   const int tiles = tiles_m * tiles_n;
   const int tile = tile_of_block((int)blockIdx.x, tiles, tiles_m, tiles_n, band);
@@ -116,9 +117,12 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
     const int gm = min(m0 + row, m - 1);
     a_src[u] = xq + (int64_t)gm * kpad + ((slot ^ (row & 15)) << 4);
   }
-  const uint4* b_src = packed + (int64_t)blk * nc * kBlockU4 + lane;
+  // this lane's packed words of super-chunk sc: fragment fn, half h, component j
+  // at dword ((blk * nc + sc) * 1024 + (2h + ph) * 256 + (32 fn + c) * 4 + j
+  const uint32_t* b_words = reinterpret_cast<const uint32_t*>(packed) +
+                            (int64_t)blk * nc * 1024 + ph * 256 + c * 4;
   // one stage: super-chunks cc .. cc+KS-1 (those < c1)
-  auto copy_stage = [&](uint8_t* As, uint8_t* Bs, int cc) {
+  auto copy_stage = [&](uint8_t* As, int cc) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       if (cc + k < c1) {
@@ -126,10 +130,6 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
         for (int u = 0; u < UA; ++u)
           lds_copy16(a_src[u] + (int64_t)(cc + k) * 256,
                      As + k * T::A_CHUNK + (u * NT + wave * 64) * 16);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          lds_copy16(b_src + (int64_t)(cc + k) * kBlockU4 + u * 64,
-                     Bs + k * T::B_CHUNK + wave * 4096 + u * 1024);
       }
     }
   };
@@ -148,34 +148,35 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
   // One super-chunk: 8 k-steps (j, h) = (st / 2, st % 2), software
   // pipelined: during step st the A operands of step st+RING-1 are read
   // from LDS and the B operands of step st+1 unpacked, while step st's
-  // MFMAs run; the group barriers interleave the unpack VALU between the
-  // MFMAs and a scheduling barrier closes each step.
-  auto unpack_b = [&](const uint4 (&bw)[2][2], int st, bl_v4i (&bop)[2]) {
+  // MFMAs run.  The packed words live in registers bw[j][fn][h]; once
+  // component j is unpacked for both halves, the same registers receive
+  // component j of the next super-chunk (plain dword loads), so the words
+  // need no LDS and no extra registers.
+  auto unpack_b = [&](const uint32_t (&bw)[4][2][2], int st, bl_v4i (&bop)[2]) __attribute__((always_inline)) {
     const int j = st >> 1, h = st & 1;
 #pragma unroll
     for (int fn = 0; fn < 2; ++fn) {
-      const uint4 wv = bw[fn][h];
-      const uint32_t wj = j == 0 ? wv.x : j == 1 ? wv.y : j == 2 ? wv.z : wv.w;
+      const uint32_t wj = bw[j][fn][h];
       bop[fn] = bl_v4i{(int)unpack_x64(wj, 0), (int)unpack_x64(wj, 1), (int)unpack_x64(wj, 2),
                        (int)unpack_x64(wj, 3)};
     }
   };
-  auto read_a = [&](const uint8_t* As, int st, bl_v4i (&a)[FM]) {
+  auto load_j = [&](uint32_t (&bw)[4][2][2], int sc, int j) __attribute__((always_inline)) {
+    const int scc = min(sc, c1 - 1);                 // past the end: reload the last (unused)
+    const uint32_t* p = b_words + (int64_t)scc * 1024 + j;
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) bw[j][fn][h] = p[2 * h * 256 + 32 * fn * 4];
+  };
+  auto read_a = [&](const uint8_t* As, int st, bl_v4i (&a)[FM]) __attribute__((always_inline)) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
       a[fm] = *reinterpret_cast<const bl_v4i*>(As + a_row + fm * 32 * 256 + a_unit[st]);
   };
-  // this lane's packed words: fragment fn, half h -> uint4 (q = 2h + ph, row 32fn + c)
-  auto read_b = [&](const uint8_t* Bs, uint4 (&bw)[2][2]) {
-#pragma unroll
-    for (int fn = 0; fn < 2; ++fn)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        bw[fn][h] = *reinterpret_cast<const uint4*>(Bs + wave * 4096 + (2 * h + ph) * 1024 +
-                                                    (32 * fn + c) * 16);
-  };
   constexpr int RING = FM >= 4 ? 2 : 3;             // A reads run RING-1 steps ahead
-  auto compute = [&](const uint8_t* As, const uint4 (&bw)[2][2]) {
+  uint32_t bw[4][2][2];
+  auto compute = [&](const uint8_t* As, int sc) __attribute__((always_inline)) {
     bl_v4i a[RING][FM];
     bl_v4i bop[2][2];
 #pragma unroll
@@ -185,6 +186,8 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
     for (int st = 0; st < 8; ++st) {
       if (st + RING - 1 < 8) read_a(As, st + RING - 1, a[(st + RING - 1) % RING]);
       if (st + 1 < 8) unpack_b(bw, st + 1, bop[(st + 1) & 1]);
+      // component j is dead once step (j, 1) is unpacked
+      if (st + 1 < 8 && ((st + 1) & 1) == 1) load_j(bw, sc + 1, (st + 1) >> 1);
 #pragma unroll
       for (int fn = 0; fn < 2; ++fn)
 #pragma unroll
@@ -192,9 +195,6 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
           acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bop[st & 1][fn], a[st % RING][fm],
                                                              acc[fm][fn], 0, 0, 0);
       if (st + 1 < 8) {
-        // interleave: the first MFMA (after the wait for this step's
-        // operands), then the LDS reads for a later step, then one MFMA per
-        // two unpack VALU ops
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, FM, 0);     // DS read
 #pragma unroll
@@ -205,45 +205,33 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // the last component (j = 3) was unpacked at step 6 -> loaded there
   };
-  // A stage's packed words are read into registers before the copies of
-  // the next stage are issued: LDS reads issued after a copy may be made to
-  // wait for it.
-  auto read_b_stage = [&](const uint8_t* Bs, uint4 (&bw)[KS][2][2]) {
-#pragma unroll
-    for (int k = 0; k < KS; ++k) read_b(Bs + k * T::B_CHUNK, bw[k]);
-  };
-  auto compute_stage = [&](const uint8_t* As, const uint4 (&bw)[KS][2][2], int cc) {
+  auto compute_stage = [&](const uint8_t* As, int cc) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < KS; ++k)
-      if (cc + k < c1) compute(As + k * T::A_CHUNK, bw[k]);
+      if (cc + k < c1) compute(As + k * T::A_CHUNK, cc + k);
   };
 
-  // Pairs of stages, then an odd last one (a loop without early exits keeps
-  // the accumulators in place).
-  uint4 bw[KS][2][2];
-  if (c0 < c1) copy_stage(A0, B0, c0);
+  // Pairs of stages, then an odd last one.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) load_j(bw, c0, j);
+  if (c0 < c1) copy_stage(A0, c0);
   __syncthreads();
   int cc = c0;
   for (; cc + 2 * KS <= c1; cc += 2 * KS) {
-    read_b_stage(B0, bw);
-    copy_stage(A1, B1, cc + KS);
-    compute_stage(A0, bw, cc);
+    copy_stage(A1, cc + KS);
+    compute_stage(A0, cc);
     __syncthreads();
-    read_b_stage(B1, bw);
-    if (cc + 2 * KS < c1) copy_stage(A0, B0, cc + 2 * KS);
-    compute_stage(A1, bw, cc + KS);
+    if (cc + 2 * KS < c1) copy_stage(A0, cc + 2 * KS);
+    compute_stage(A1, cc + KS);
     __syncthreads();
   }
   if (cc < c1) {
-    read_b_stage(B0, bw);
-    if (cc + KS < c1) copy_stage(A1, B1, cc + KS);
-    compute_stage(A0, bw, cc);
+    if (cc + KS < c1) copy_stage(A1, cc + KS);
+    compute_stage(A0, cc);
     __syncthreads();
-    if (cc + KS < c1) {
-      read_b_stage(B1, bw);
-      compute_stage(A1, bw, cc + KS);
-    }
+    if (cc + KS < c1) compute_stage(A1, cc + KS);
   }
 
   // rescale factors per tile row (in the now idle first A stage)
@@ -269,12 +257,9 @@ __global__ __launch_bounds__(64 * WN) void gemmw_kernel(
     for (int fm = 0; fm < FM; ++fm) fr[fm] = fac[32 * fm + c];
     __syncthreads();                                     // all fac reads done
     constexpr int S = 32 * FM * 128;                     // LDS bytes per wave
-    constexpr int NA = T::A_BYTES / S, NB = T::B_BYTES / S;
-    static_assert(2 * NA + 2 * NB >= WN, "line staging space");
-    uint8_t* buf = wave < NA ? A0 + wave * S
-                 : wave < 2 * NA ? A1 + (wave - NA) * S
-                 : wave < 2 * NA + NB ? B0 + (wave - 2 * NA) * S
-                 : B1 + (wave - 2 * NA - NB) * S;
+    constexpr int NA = T::A_BYTES / S;
+    static_assert(2 * NA >= WN, "line staging space");
+    uint8_t* buf = wave < NA ? A0 + wave * S : A1 + (wave - NA) * S;
     const int col0 = (tn * WN + wave) * 64;
     if (col0 + 64 <= n) {                                // whole block inside the output
 #pragma unroll
@@ -410,12 +395,14 @@ hipError_t runw(const int8_t* xq, const float* scale, const uint32_t* packed, co
 
 }  // namespace
 
-// Tile variants: rows per tile x columns per tile (32x32x32 MFMA, wide waves).
-//   0: 128 x 512   1: 64 x 512   2: 64 x 256   3: 96 x 256
+// Tile variants: rows per tile x columns per tile (32x32x32 MFMA, wide waves),
+// super-chunks per stage.  Eight-wave tiles stage two super-chunks (fewer
+// barriers, and room in LDS for their whole-line output staging).
+//   0: 128 x 512, 2   1: 64 x 512, 2   2: 64 x 256, 1   3: 96 x 256, 1
 void gemm_tile_shape(int variant, int* bm, int* bn) {
   switch (variant) {
-    case 0: *bm = TileW<4, 8, 1>::BM; *bn = TileW<4, 8, 1>::BN; break;
-    case 1: *bm = TileW<2, 8, 1>::BM; *bn = TileW<2, 8, 1>::BN; break;
+    case 0: *bm = TileW<4, 8, 2>::BM; *bn = TileW<4, 8, 2>::BN; break;
+    case 1: *bm = TileW<2, 8, 2>::BM; *bn = TileW<2, 8, 2>::BN; break;
     case 2: *bm = TileW<2, 4, 1>::BM; *bn = TileW<2, 4, 1>::BN; break;
     default: *bm = TileW<3, 4, 1>::BM; *bn = TileW<3, 4, 1>::BN; break;
   }
@@ -427,14 +414,14 @@ constexpr int kBand = 4;
 hipError_t launch_gemm(int variant, const int8_t* xq, const float* scale, const uint32_t* packed,
                        const float* gamma, int64_t m, int64_t n, int64_t k, bool relu2,
                        bool bf16, void* y, int32_t* acc_out, hipStream_t stream) {
-#define BL_GEMMW(FM, WN)                                                                     \
-  return runw<FM, WN, 1>(xq, scale, packed, gamma, m, n, k, kBand, relu2, bf16, y, acc_out, \
-                         stream)
+#define BL_GEMMW(FM, WN, KS)                                                                  \
+  return runw<FM, WN, KS>(xq, scale, packed, gamma, m, n, k, kBand, relu2, bf16, y, acc_out, \
+                          stream)
   switch (variant) {
-    case 0: BL_GEMMW(4, 8);
-    case 1: BL_GEMMW(2, 8);
-    case 2: BL_GEMMW(2, 4);
-    case 3: BL_GEMMW(3, 4);
+    case 0: BL_GEMMW(4, 8, 2);
+    case 1: BL_GEMMW(2, 8, 2);
+    case 2: BL_GEMMW(2, 4, 1);
+    case 3: BL_GEMMW(3, 4, 1);
     default: return hipErrorInvalidValue;
   }
 #undef BL_GEMMW
