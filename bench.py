@@ -346,7 +346,7 @@ def run_stack_c3(B, torch, args):
     layer in order: q/k/v (one shared input), o, up (ReLU^2), down, at 1, 8,
     32 and 64 tokens with Student-t activations.  Each group is one fused
     decode launch (activation quant in its prologue) at 1-2 tokens, and at
-    3-16 tokens when it holds several matrices; otherwise one activation
+    3-64 tokens when it holds several matrices; otherwise one activation
     quant per distinct input and one forward per matrix.  A pass
     is captured as one graph; the best of a few replays is reported."""
     import datagen
@@ -372,9 +372,9 @@ def run_stack_c3(B, torch, args):
         ws = B.Workspace()
         calls = []
         # a group runs as one fused step (activation quant in the kernel)
-        # at 1-2 tokens, and at 3-16 tokens when it has several matrices
+        # at 1-2 tokens, and at 3-64 tokens when it has several matrices
         # sharing its input (q, k, v); otherwise as one activation quant plus
-        # one forward per matrix (at 3-16 tokens a fused step re-quantizes
+        # one forward per matrix (from 3 tokens a fused step re-quantizes
         # the input in every workgroup, which a single matrix does not repay)
         xq = {g: torch.empty((m, B.padded_k(x.shape[1])), dtype=torch.int8, device="cuda")
               for g, x in xs.items()}

@@ -38,7 +38,7 @@ EXPORTS = [
     "bitlinear_forward_fused_workspace_bytes", "bitlinear_forward_fused",
 ]
 BL_MAX_FUSED = 16
-BL_FUSED_MAX_M = 16
+BL_FUSED_MAX_M = 64
 
 
 class BLLinear(ctypes.Structure):

@@ -141,7 +141,7 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
 }
 
 struct FusedPlan {
-  bool mfma = false;                    // 3..16 tokens: the fused MFMA kernel
+  bool mfma = false;                    // 3..64 tokens: the fused MFMA kernel
   int variant = 0;                      // its wave layout
   int waves = 8;
   int qpl = 4;                          // 16-byte q-parts per lane (rows per group / 16)

@@ -546,11 +546,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) 
 }
 
 // ----------------------------------------------------- fused MFMA decode --
-// The fused decode step for 3 to 16 tokens: the entries' products on
+// The fused decode step for 3 to 64 tokens: the entries' products on
 // v_mfma_i32_16x16x64_i8 as in the windowed MFMA GEMV (unpacked weights of
 // 16 rows as the first operand, x~ of 16 tokens as the second, x~ through
-// two LDS windows per K-slice, one barrier per super-chunk), with the
-// activation quant of each entry done by every workgroup:
+// two LDS windows per K-slice, one barrier per super-chunk), in token
+// blocks of 16 on blockIdx.y, with the activation quant of each entry's
+// block done by every workgroup of the block:
 //   1. the first weight loads are issued;
 //   2. max|x| per token over its whole row (every thread reads units of
 //      every token; idempotent, so loads past the row or past token m-1
@@ -563,7 +564,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) 
 // Workgroup g of an entry owns WR row groups of SB 16-row sub-blocks; its
 // WK waves per group split the super-chunks and meet in LDS at the end.
 template <int WR, int WK, int SB, int PF, int RPU, int MT, bool FAST>
-__global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(FusedArgs args, int m) {
+__global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(FusedArgs args, int m_all) {
   static_assert(RPU == 2 || RPU == 4, "16-byte activation units per x~ unit: 2 (bf16 only), 4");
   // FAST: every entry's rows are whole 16-byte units at 16-byte alignment,
   // so the activation loads are plain vector loads with no branch (a load
@@ -580,6 +581,9 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(FusedArgs
   __shared__ uint32_t bmax[MT];
   __shared__ float s_lds[16];
   __shared__ float fac_lds[16];
+  // token block blockIdx.y: tokens t0 .. t0 + m - 1 (16 per block)
+  const int t0 = 16 * (int)blockIdx.y;
+  const int m = min(m_all - t0, MT);
   int si = 0;
 #pragma unroll
   for (int i = 1; i < kMaxFused; ++i)
@@ -619,7 +623,7 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(FusedArgs
   const XRow xrow = x_row_info(sg);
   const bool xbf = sg.x_bf16();
   for (int t = wave; t < m; t += WAVES) {
-    const char* row = x_row(sg, t);
+    const char* row = x_row(sg, t0 + t);
     uint32_t mx = 0;
     for (int ub = 0; ub < xrow.nu; ub += 64 * 8) {
       uint4 v[8];
@@ -642,7 +646,7 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(FusedArgs
     s_lds[threadIdx.x] = sv;
     fac_lds[threadIdx.x] = gamma_over_s(gam, sv);
     if (local == 0 && sg.scale_out != nullptr && (int)threadIdx.x < m)
-      sg.scale_out[threadIdx.x] = sv;
+      sg.scale_out[t0 + threadIdx.x] = sv;
   }
   __syncthreads();
 
@@ -658,7 +662,7 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(FusedArgs
     const int t = q >> 4, u = q & 15;
     xtok[i] = t;
     xq16[i] = u;
-    xsrc[i] = x_row(sg, min(t, m - 1));
+    xsrc[i] = x_row(sg, t0 + min(t, m - 1));
     xdst[i] = t * 16 + (u ^ (t & 15));
     xsc[i] = s_lds[t];
   }
@@ -725,7 +729,7 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(FusedArgs
       const bl_v4i qv = quant_unit(xr[p][i], xsc[i], c, xq16[i]);
       win[xdst[i]] = qv;
       if (write_xq && c < c1 && xtok[i] < m)
-        *reinterpret_cast<bl_v4i*>(sg.xq_out + (int64_t)xtok[i] * kpad + c * 256 + xq16[i] * 16) =
+        *reinterpret_cast<bl_v4i*>(sg.xq_out + (int64_t)(t0 + xtok[i]) * kpad + c * 256 + xq16[i] * 16) =
             qv;
     }
     __syncthreads();
@@ -781,7 +785,7 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(FusedArgs
 #pragma unroll
   for (int sb = 0; sb < SB; ++sb) {
     const int row0 = b * 64 + (sub0 + sb) * 16 + 4 * g;
-    const int64_t idx = (int64_t)r * sg.n + row0;
+    const int64_t idx = (int64_t)(t0 + r) * sg.n + row0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (row0 + i >= sg.n) continue;
@@ -825,16 +829,18 @@ hipError_t launch_gemv(int m, int waves, int pf, int qpl, const int8_t* xq, cons
 #undef BL_GEMV
 }
 
-// Fused decode step for 3 to 16 tokens on the matrix cores: variant 0 = two
-// 16-row groups x 4 K-slices, 1 = four 32-row groups (whole K per wave).
+// Fused decode step for 3 to 64 tokens on the matrix cores, token blocks of
+// 16 on grid.y: variant 0 = two 16-row groups x 4 K-slices, 1 = four 32-row
+// groups (whole K per wave).
 // all_bf16: every entry's x is bf16 (two 16-byte loads per x~ unit, not
 // four); all_fast: every entry's rows are whole, aligned 16-byte units.
 hipError_t launch_gemv_mfma_fused(const FusedArgs& args, int m, int variant, bool all_bf16,
                                   bool all_fast, int groups, hipStream_t stream) {
-  if (m < 1 || m > 16) return hipErrorInvalidValue;
+  if (m < 1 || m > 64) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)groups, (unsigned)((m + 15) / 16));   // token blocks of 16
 #define BL_MF(WR, WK, SB, PF, RPU, MT, FAST)                                         \
   gemv_mfma_fused_kernel<WR, WK, SB, PF, RPU, MT, FAST>                              \
-      <<<(unsigned)groups, 64 * WR * WK, 0, stream>>>(args, m)
+      <<<grid, 64 * WR * WK, 0, stream>>>(args, m)
 #define BL_MF_X(WR, WK, SB, PF, MT)               \
   if (all_fast && all_bf16) BL_MF(WR, WK, SB, PF, 2, MT, true); \
   else if (all_fast) BL_MF(WR, WK, SB, PF, 4, MT, true);       \

@@ -179,12 +179,13 @@ bl_status bitlinear_forward(const int8_t* xq, const float* scale, const void* pa
  *              with the contract of bitlinear_forward's workspace.
  * Every workgroup recomputes its entry's per-token absmax from the whole row
  * of x (all workgroups get the same s and x~), so the activations are read
- * from cache once (1-2 tokens) or twice (3-16 tokens, int8 matrix cores)
- * per workgroup; meant for decode-sized batches.  From 3 tokens no
- * workspace is needed (the size query returns 0).
+ * from cache once (1-2 tokens) or twice (3-64 tokens, int8 matrix cores,
+ * one block of up to 16 tokens per workgroup) per workgroup; meant for
+ * decode-sized batches.  From 3 tokens no workspace is needed (the size
+ * query returns 0).
  * ---------------------------------------------------------------------- */
 #define BL_MAX_FUSED 16
-#define BL_FUSED_MAX_M 16
+#define BL_FUSED_MAX_M 64
 typedef struct {
   const void* x;        /* [m][k] fp32 or bf16 activations, 4-byte aligned */
   int x_dtype;          /* BL_F32 or BL_BF16 */

@@ -80,6 +80,10 @@ FUSED_CASES = [
     (5, [(16400, 512, False, "bf16", "bf16")]),                                    # >= 256 row blocks
     (9, [(64, 64, False, "f32", "f32"), (65, 320, True, "bf16", "bf16")]),         # empty K-slices
     (16, [(64, 256, False, "f32", "f32")] * 16),
+    # 17 to 64 tokens: token blocks of 16
+    (17, [(300, 1000, True, "f32", "bf16"), (64, 8200, False, "bf16", "bf16")]),    # a block of 1
+    (40, [(2560, 2560, False, "bf16", "bf16"), (640, 2560, False, "bf16", "bf16")]),
+    (64, [(500, 777, False, "bf16", "f32"), (16400, 512, True, "bf16", "bf16")]),  # >= 256 row blocks
 ]
 
 
@@ -140,9 +144,10 @@ def test_fused_c2_decode_set(B, m):
 
 def test_fused_rejects(B):
     import torch
-    x = torch.zeros((17, 256), dtype=torch.float32, device="cuda")
+    m = B.BL_FUSED_MAX_M + 1
+    x = torch.zeros((m, 256), dtype=torch.float32, device="cuda")
     packed, gamma = B.pack_weights(torch.zeros((64, 256), dtype=torch.float32, device="cuda"))
-    y = torch.empty((17, 64), dtype=torch.float32, device="cuda")
+    y = torch.empty((m, 64), dtype=torch.float32, device="cuda")
     with pytest.raises(B.BitLinearError) as e:
         B.forward_fused([dict(x=x, packed=packed, gamma=gamma, n=64, k=256, y=y)])
-    assert e.value.status == 2        # m = 17 > 16
+    assert e.value.status == 2        # m above the limit
