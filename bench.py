@@ -466,9 +466,35 @@ def run_cpu_baseline(budget_s=12.0):
             break
     per = el / steps
     return {"value": round(step_bytes / per / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "ms_per_step": round(per * 1e3, 2),
+            "kind": "oracle", "ms_per_step": round(per * 1e3, 2), "host_cpu": host_cpu_model(),
             "sample": f"{steps} full decode steps of the same workload (4 act quants, 6 products, "
                       f"dequant; codes prepared untimed), {el:.1f} s"}
+
+
+def host_cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo) and the
+    logical CPUs this process may use."""
+    name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{name}, {len(os.sched_getaffinity(0))} logical CPUs available"
+
+
+def environment(torch):
+    """Software and device the numbers were taken on."""
+    rocm = "unknown"
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"gpu": torch.cuda.get_device_name(0), "rocm": rocm, "torch": torch.__version__}
 
 
 # ---------------------------------------------------------- profiling aids --
@@ -737,6 +763,7 @@ def main():
         "prefill": prefill,
         "c5": c5,
         "stack_c3": stack,
+        "env": environment(torch),
         "wall_s": round(time.time() - t0, 1),
     }
     print(json.dumps(line))
