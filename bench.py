@@ -137,6 +137,21 @@ class DecodeSet:
         for name in self.names:
             self.forward_one(name, copy)
 
+    def step_multi(self, copy):
+        """As step, but the matrices that share an input (q, k, v) go to
+        one bitlinear_forward_multi call."""
+        self.quant_into()
+        for g in self.groups:
+            names = [nm for nm in self.names if self.mats[nm]["group"] == g]
+            if len(names) == 1:
+                self.forward_one(names[0], copy)
+                continue
+            d0 = self.mats[names[0]]
+            ops = [dict(packed=self.mats[nm]["packed"][copy], gamma=self.mats[nm]["gamma"],
+                        n=self.mats[nm]["n"], relu2=self.mats[nm]["relu2"], y=self.y[nm])
+                   for nm in names]
+            self.B.forward_multi(self.xq[g], self.s[g], d0["k"], ops, workspace=self.ws)
+
     def fused_steps(self):
         """One prepared fused call (all matrices, one launch) per weight copy."""
         out = []
@@ -292,8 +307,9 @@ def run_c5(B, torch, args):
     """The 100B-class layer (q, o 8192x8192; k, v 1024x8192; up 28672x8192
     with ReLU^2; down 8192x28672) at 1, 16 and 512 tokens, weights rotated
     past the caches: each matrix's forward alone (x~ given) and the whole
-    layer (one activation quant per distinct input + the six forwards);
-    at 1 token also the fused step of up and of down alone."""
+    layer (one activation quant per distinct input + the six forwards),
+    also with q, k and v in one bitlinear_forward_multi call; at 1 token
+    also the fused step of up and of down alone."""
     import datagen
     wl = datagen.WORKLOADS["c5"]
     set_bytes = sum(B.packed_bytes(n, k) for (n, k, _, _) in wl.matrices.values())
@@ -312,10 +328,13 @@ def run_c5(B, torch, args):
                        "GBs": round(b / (t * 1e-3) / 1e9, 1),
                        "TOPS": round(ops / (t * 1e-3) / 1e12, 2)}
         tl = time_launches(torch, lambda c: ds.step(c), copies, 2 * copies)
+        tm = time_launches(torch, lambda c: ds.step_multi(c), copies, 2 * copies)
         ops = 2.0 * m * sum(d["n"] * d["k"] for d in ds.mats.values())
         res = {"layer_us": round(tl * 1e3, 2),
                "layer_GBs": round(ds.bytes_step() / (tl * 1e-3) / 1e9, 1),
-               "layer_TOPS": round(ops / (tl * 1e-3) / 1e12, 2), "per_matrix": per}
+               "layer_TOPS": round(ops / (tl * 1e-3) / 1e12, 2),
+               "layer_qkv_multi_us": round(tm * 1e3, 2),
+               "layer_qkv_multi_TOPS": round(ops / (tm * 1e-3) / 1e12, 2), "per_matrix": per}
         if m == 1:
             fused = {}
             for nm in ("up", "down"):
@@ -494,7 +513,10 @@ def environment(torch):
             rocm = f.read().strip()
     except OSError:
         pass
-    return {"gpu": torch.cuda.get_device_name(0), "rocm": rocm, "torch": torch.__version__}
+    props = torch.cuda.get_device_properties(0)
+    return {"gpu": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", "unknown"),
+            "compute_units": props.multi_processor_count, "rocm": rocm,
+            "torch": torch.__version__}
 
 
 # ---------------------------------------------------------- profiling aids --

@@ -24,6 +24,7 @@ BL_OK = 0
 BL_F32, BL_BF16 = 0, 1
 BL_EPI_NONE, BL_EPI_RELU2 = 0, 1
 BL_MAX_K = 262144
+BL_MAX_MN = 16777216
 EPS_DEFAULT = 1e-5
 
 STATUS_NAMES = {0: "BL_OK", 1: "BL_ERR_INVALID_ARG", 2: "BL_ERR_UNSUPPORTED_SHAPE",
@@ -36,9 +37,11 @@ EXPORTS = [
     "bitlinear_forward_workspace_bytes", "bitlinear_forward", "bitlinear_workspace_init",
     "bitlinear_status_string", "bitlinear_abi_version",
     "bitlinear_forward_fused_workspace_bytes", "bitlinear_forward_fused",
+    "bitlinear_forward_multi_workspace_bytes", "bitlinear_forward_multi",
 ]
 BL_MAX_FUSED = 16
 BL_FUSED_MAX_M = 64
+BL_MAX_MULTI = 16
 
 
 class BLLinear(ctypes.Structure):
@@ -48,6 +51,13 @@ class BLLinear(ctypes.Structure):
                 ("epilogue", ctypes.c_int), ("y_dtype", ctypes.c_int), ("y", ctypes.c_void_p),
                 ("acc_out", ctypes.c_void_p), ("xq_out", ctypes.c_void_p),
                 ("scale_out", ctypes.c_void_p)]
+
+
+class BLProduct(ctypes.Structure):
+    """bl_product of include/bitlinear.h."""
+    _fields_ = [("packed", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("epilogue", ctypes.c_int), ("y_dtype", ctypes.c_int), ("y", ctypes.c_void_p),
+                ("acc_out", ctypes.c_void_p)]
 
 
 class BitLinearError(RuntimeError):
@@ -77,6 +87,8 @@ def _load() -> ctypes.CDLL:
         "bitlinear_abi_version": (i32, []),
         "bitlinear_forward_fused_workspace_bytes": (sz, [vp, i32, i64]),
         "bitlinear_forward_fused": (i32, [vp, i32, i64, f32, vp, sz, vp]),
+        "bitlinear_forward_multi_workspace_bytes": (sz, [vp, i32, i64, i64]),
+        "bitlinear_forward_multi": (i32, [vp, vp, i64, i64, vp, i32, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -243,6 +255,28 @@ class FusedStep:
         _check("bitlinear_forward_fused", lib.bitlinear_forward_fused(
             self.arr, len(self.ops), self.m, self.eps, _ptr(ws), 0 if ws is None else ws.numel(),
             _stream(stream)))
+
+
+def forward_multi(xq, scale, k: int, ops, workspace: Optional[Workspace] = None,
+                  stream=None) -> None:
+    """bitlinear_forward_multi: several products sharing x~ and s.
+
+    ops: list of dicts with keys packed, gamma, n, y and optional relu2,
+    acc_out (tensors on the device); y's dtype picks the output type."""
+    if not 1 <= len(ops) <= BL_MAX_MULTI:
+        raise ValueError(f"1..{BL_MAX_MULTI} entries")
+    m = int(xq.shape[0])
+    arr = (BLProduct * len(ops))()
+    for e, o in zip(arr, ops):
+        e.packed, e.gamma, e.n = _ptr(o["packed"]), _ptr(o["gamma"]), int(o["n"])
+        e.epilogue = BL_EPI_RELU2 if o.get("relu2") else BL_EPI_NONE
+        e.y_dtype, e.y = _dtype_code(o["y"].dtype), _ptr(o["y"])
+        e.acc_out = _ptr(o.get("acc_out"))
+    nbytes = int(lib.bitlinear_forward_multi_workspace_bytes(arr, len(ops), m, int(k)))
+    ws = (workspace or _workspace_for(xq.device)).get(nbytes, stream)
+    _check("bitlinear_forward_multi", lib.bitlinear_forward_multi(
+        _ptr(xq), _ptr(scale), m, int(k), arr, len(ops), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def forward_fused(ops, eps: float = EPS_DEFAULT, workspace: Optional[Workspace] = None,

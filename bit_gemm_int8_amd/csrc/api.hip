@@ -394,6 +394,86 @@ bl_status bitlinear_quant_act(const void* x, int x_dtype, int64_t m, int64_t k, 
   return e == hipSuccess ? BL_OK : BL_ERR_HIP;
 }
 
+// A table of products sharing x~: the plan of one product over the summed
+// output width decides.  If it is the GEMM, one launch over the table;
+// otherwise each product gets its own plan and launch (the same numbers).
+static bl_status check_multi(const int8_t* xq, const float* scale, int64_t m, int64_t k,
+                             const bl_product* ops, int nops, int64_t* n_total) {
+  if (ops == nullptr || nops < 1 || nops > BL_MAX_MULTI) return BL_ERR_INVALID_ARG;
+  if (m < 0 || k < 1) return BL_ERR_INVALID_ARG;
+  if (m > BL_MAX_MN || k > BL_MAX_K) return BL_ERR_UNSUPPORTED_SHAPE;
+  int64_t nt = 0;
+  for (int i = 0; i < nops; ++i) {
+    const bl_product& o = ops[i];
+    if (!valid_dtype(o.y_dtype)) return BL_ERR_INVALID_ARG;
+    if (o.epilogue != BL_EPI_NONE && o.epilogue != BL_EPI_RELU2) return BL_ERR_INVALID_ARG;
+    if (o.n < 1) return BL_ERR_INVALID_ARG;
+    if (o.n > BL_MAX_MN) return BL_ERR_UNSUPPORTED_SHAPE;
+    nt += padded_n(o.n);
+  }
+  if (nt > BL_MAX_MN) return BL_ERR_UNSUPPORTED_SHAPE;
+  *n_total = nt;
+  if (m == 0) return BL_OK;
+  if (xq == nullptr || scale == nullptr) return BL_ERR_INVALID_ARG;
+  if (!aligned(xq, 16) || !aligned(scale, 4)) return BL_ERR_MISALIGNED;
+  for (int i = 0; i < nops; ++i) {
+    const bl_product& o = ops[i];
+    if (o.packed == nullptr || o.gamma == nullptr || o.y == nullptr) return BL_ERR_INVALID_ARG;
+    if (!aligned(o.packed, 16) || !aligned(o.gamma, 4) ||
+        !aligned(o.y, o.y_dtype == BL_BF16 ? 2 : 4) ||
+        (o.acc_out != nullptr && !aligned(o.acc_out, 4)))
+      return BL_ERR_MISALIGNED;
+  }
+  return BL_OK;
+}
+
+size_t bitlinear_forward_multi_workspace_bytes(const bl_product* ops, int nops, int64_t m,
+                                               int64_t k) {
+  int64_t nt = 0;
+  if (check_multi(nullptr, nullptr, 0, k, ops, nops, &nt) != BL_OK || m <= 0 || m > BL_MAX_MN)
+    return 0;
+  if (forward_plan(m, nt, k).kind == 1) return 0;
+  size_t need = 0;
+  for (int i = 0; i < nops; ++i) {
+    const size_t b = forward_plan(m, ops[i].n, k).ws_bytes;
+    if (b > need) need = b;
+  }
+  return need;
+}
+
+bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t m, int64_t k,
+                                  const bl_product* ops, int nops, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  int64_t nt = 0;
+  const bl_status st = check_multi(xq, scale, m, k, ops, nops, &nt);
+  if (st != BL_OK) return st;
+  if (m == 0) return BL_OK;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const FwdPlan whole = forward_plan(m, nt, k);
+  if (whole.kind == 1) {
+    GemmProduct g[kMaxMulti];
+    for (int i = 0; i < nops; ++i)
+      g[i] = GemmProduct{ops[i].packed, ops[i].gamma, ops[i].n, ops[i].epilogue == BL_EPI_RELU2,
+                         ops[i].y_dtype == BL_BF16, ops[i].y, ops[i].acc_out};
+    return launch_gemm_multi(whole.variant, xq, scale, m, k, g, nops, hs) == hipSuccess
+               ? BL_OK : BL_ERR_HIP;
+  }
+  const size_t need = bitlinear_forward_multi_workspace_bytes(ops, nops, m, k);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return BL_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return BL_ERR_MISALIGNED;
+  }
+  for (int i = 0; i < nops; ++i) {
+    const bl_product& o = ops[i];
+    const FwdPlan plan = forward_plan(m, o.n, k);
+    const hipError_t e = launch_forward(plan, xq, scale, reinterpret_cast<const uint32_t*>(o.packed),
+                                        o.gamma, m, o.n, k, o.epilogue == BL_EPI_RELU2,
+                                        o.y_dtype == BL_BF16, o.y, o.acc_out, workspace, hs);
+    if (e != hipSuccess) return BL_ERR_HIP;
+  }
+  return BL_OK;
+}
+
 bl_status bitlinear_forward(const int8_t* xq, const float* scale, const void* packed,
                             const float* gamma, int64_t m, int64_t n, int64_t k, int epilogue,
                             int y_dtype, void* y, int32_t* acc_out, void* workspace,

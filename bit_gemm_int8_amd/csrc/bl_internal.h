@@ -42,6 +42,21 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
 
 hipError_t launch_fill_zero(uint32_t* p, size_t words, hipStream_t stream);
 
+// GEMM over a table of products that share x~ and s (each with its own
+// packed weights, gamma, N and output): one launch, the products' column
+// tiles side by side.  A single bitlinear_forward is the one-entry table.
+constexpr int kMaxMulti = 16;
+struct GemmProduct {
+  const void* packed;
+  const float* gamma;
+  int64_t n;
+  bool relu2, bf16;
+  void* y;
+  int32_t* acc_out;       // nullable
+};
+hipError_t launch_gemm_multi(int variant, const int8_t* xq, const float* scale, int64_t m,
+                             int64_t k, const GemmProduct* ops, int nops, hipStream_t stream);
+
 // Fused decode step: a table of BitLinear products that share a token batch
 // (M <= 16), each quantizing its own activations in the kernel prologue.
 constexpr int kMaxFused = 16;

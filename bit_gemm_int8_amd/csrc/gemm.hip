@@ -51,6 +51,25 @@ __device__ __forceinline__ void lds_copy16(const void* src, void* lds_wave_base)
 // same XCD (workgroups are dispatched to the 8 XCDs round-robin), so the
 // workgroups that share an XCD's L2 cover a compact block of the output and
 // share its x~ rows and packed columns.
+// One product of the table in the kernel arguments; the first column tile
+// of every product shares one 64-byte line (tn_begin), so a workgroup finds
+// its product with one scalar load.
+struct GemmSegK {
+  const uint4* packed;
+  const float* gamma;
+  void* y;
+  int32_t* acc_out;
+  int n, nb, flags;        // flags: 1 ReLU^2, 2 bf16 y, 4 vector stores, 8 whole-line bf16 rows
+};
+struct GemmArgs {
+  int tn_begin[kMaxMulti];
+  const int8_t* xq;
+  const float* scale;
+  int64_t kpad;
+  int m, nc, tiles_m, tiles_n, band, nseg;
+  GemmSegK seg[kMaxMulti];
+};
+
 template <int FM, int WN, int KS>
 struct TileW {
   static constexpr int BM = 32 * FM;
@@ -80,12 +99,12 @@ __device__ __forceinline__ int tile_of_block(int bid, int tiles, int tiles_m, in
 
 // At least two waves per SIMD (registers within 256 per lane): one wave's
 // waits are covered by the other's MFMAs.
-template <int FM, int WN, int KS>
+// MULTI: the table may hold several products (a scalar lookup finds this
+// workgroup's); otherwise it is product 0 at fixed offsets, so its fields
+// load together with the other arguments.
+template <int FM, int WN, int KS, bool MULTI>
 __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) void gemmw_kernel(
-    const int8_t* __restrict__ xq, const float* __restrict__ scale,
-    const uint4* __restrict__ packed, const float* __restrict__ gamma, int m, int n,
-    int nb, int nc, int64_t kpad, int tiles_m, int tiles_n, int band, int relu2,
-    int bf16, int vec_out, int line_out, void* __restrict__ y, int32_t* __restrict__ acc_out) {
+    GemmArgs args) {
   using T = TileW<FM, WN, KS>;
   constexpr int BM = T::BM, BN = T::BN, NT = T::NT, UA = T::UA;
   // two stages as separate arrays: the compiler then sees that the copies
@@ -94,10 +113,30 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ __attribute__((aligned(16))) uint8_t A0[T::A_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t A1[T::A_BYTES];
 
-  const int tiles = tiles_m * tiles_n;
-  const int tile = tile_of_block((int)blockIdx.x, tiles, tiles_m, tiles_n, band);
-  const int tm = tile / tiles_n;
-  const int tn = tile - tm * tiles_n;
+  // this workgroup's tile over all products' column tiles, then its product
+  const int tiles_m = args.tiles_m;
+  const int tiles = tiles_m * args.tiles_n;
+  const int tile = tile_of_block((int)blockIdx.x, tiles, tiles_m, args.tiles_n, args.band);
+  const int tm = tile / args.tiles_n;
+  const int tng = tile - tm * args.tiles_n;
+  int si = 0;
+  if (MULTI) {
+#pragma unroll
+    for (int i = 1; i < kMaxMulti; ++i)
+      if (i < args.nseg && tng >= args.tn_begin[i]) si = i;
+  }
+  const GemmSegK& sg = args.seg[si];
+  const int tn = tng - args.tn_begin[si];
+  const int8_t* __restrict__ xq = args.xq;
+  const float* __restrict__ scale = args.scale;
+  const uint4* __restrict__ packed = sg.packed;
+  const float* __restrict__ gamma = sg.gamma;
+  void* __restrict__ y = sg.y;
+  int32_t* __restrict__ acc_out = sg.acc_out;
+  const int m = args.m, n = sg.n, nb = sg.nb, nc = args.nc;
+  const int64_t kpad = args.kpad;
+  const int relu2 = sg.flags & 1, bf16 = (sg.flags >> 1) & 1, vec_out = (sg.flags >> 2) & 1,
+            line_out = (sg.flags >> 3) & 1;
   const int m0 = tm * BM;
   const int c0 = 0, c1 = nc;
 
@@ -148,26 +187,28 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
   // One super-chunk: 8 k-steps (j, h) = (st / 2, st % 2), software
   // pipelined: during step st the A operands of step st+RING-1 are read
   // from LDS and the B operands of step st+1 unpacked, while step st's
-  // MFMAs run.  The packed words live in registers bw[j][fn][h]; once
-  // component j is unpacked for both halves, the same registers receive
-  // component j of the next super-chunk (plain dword loads), so the words
-  // need no LDS and no extra registers.
-  auto unpack_b = [&](const uint32_t (&bw)[4][2][2], int st, bl_v4i (&bop)[2]) __attribute__((always_inline)) {
+  // MFMAs run.  A lane's packed words of a super-chunk are four 16-byte
+  // loads bw[fn][h] (component j = step j); those of the next super-chunk
+  // are issued right after step 1 is unpacked into a second set, which
+  // becomes the current one at the end of the super-chunk.
+  auto unpack_b = [&](const uint4 (&bw)[2][2], int st, bl_v4i (&bop)[2]) __attribute__((always_inline)) {
     const int j = st >> 1, h = st & 1;
 #pragma unroll
     for (int fn = 0; fn < 2; ++fn) {
-      const uint32_t wj = bw[j][fn][h];
+      const uint4 wv = bw[fn][h];
+      const uint32_t wj = j == 0 ? wv.x : j == 1 ? wv.y : j == 2 ? wv.z : wv.w;
       bop[fn] = bl_v4i{(int)unpack_x64(wj, 0), (int)unpack_x64(wj, 1), (int)unpack_x64(wj, 2),
                        (int)unpack_x64(wj, 3)};
     }
   };
-  auto load_j = [&](uint32_t (&bw)[4][2][2], int sc, int j) __attribute__((always_inline)) {
+  auto load_b = [&](uint4 (&bw)[2][2], int sc) __attribute__((always_inline)) {
     const int scc = min(sc, c1 - 1);                 // past the end: reload the last (unused)
-    const uint32_t* p = b_words + (int64_t)scc * 1024 + j;
+    const uint32_t* p = b_words + (int64_t)scc * 1024;
 #pragma unroll
     for (int fn = 0; fn < 2; ++fn)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) bw[j][fn][h] = p[2 * h * 256 + 32 * fn * 4];
+      for (int h = 0; h < 2; ++h)
+        bw[fn][h] = *reinterpret_cast<const uint4*>(p + 2 * h * 256 + 32 * fn * 4);
   };
   auto read_a = [&](const uint8_t* As, int st, bl_v4i (&a)[FM]) __attribute__((always_inline)) {
 #pragma unroll
@@ -175,7 +216,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
       a[fm] = *reinterpret_cast<const bl_v4i*>(As + a_row + fm * 32 * 256 + a_unit[st]);
   };
   constexpr int RING = FM >= 4 ? 2 : 3;             // A reads run RING-1 steps ahead
-  uint32_t bw[4][2][2];
+  uint4 bw[2][2], bwn[2][2];
   auto compute = [&](const uint8_t* As, int sc) __attribute__((always_inline)) {
     bl_v4i a[RING][FM];
     bl_v4i bop[2][2];
@@ -186,8 +227,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int st = 0; st < 8; ++st) {
       if (st + RING - 1 < 8) read_a(As, st + RING - 1, a[(st + RING - 1) % RING]);
       if (st + 1 < 8) unpack_b(bw, st + 1, bop[(st + 1) & 1]);
-      // component j is dead once step (j, 1) is unpacked
-      if (st + 1 < 8 && ((st + 1) & 1) == 1) load_j(bw, sc + 1, (st + 1) >> 1);
+      if (st == 0) load_b(bwn, sc + 1);
 #pragma unroll
       for (int fn = 0; fn < 2; ++fn)
 #pragma unroll
@@ -205,7 +245,10 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the last component (j = 3) was unpacked at step 6 -> loaded there
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) bw[fn][h] = bwn[fn][h];
   };
   auto compute_stage = [&](const uint8_t* As, int cc) __attribute__((always_inline)) {
 #pragma unroll
@@ -214,8 +257,7 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
   };
 
   // Pairs of stages, then an odd last one.
-#pragma unroll
-  for (int j = 0; j < 4; ++j) load_j(bw, c0, j);
+  load_b(bw, c0);
   if (c0 < c1) copy_stage(A0, c0);
   __syncthreads();
   int cc = c0;
@@ -374,22 +416,43 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 template <int FM, int WN, int KS>
-hipError_t runw(const int8_t* xq, const float* scale, const uint32_t* packed, const float* gamma,
-                int64_t m, int64_t n, int64_t k, int band, bool relu2, bool bf16, void* y,
-                int32_t* acc_out, hipStream_t stream) {
+hipError_t runw_multi(const int8_t* xq, const float* scale, int64_t m, int64_t k, int band,
+                      const GemmProduct* ops, int nops, hipStream_t stream) {
   using T = TileW<FM, WN, KS>;
-  const int nb = (int)cdiv(n, kRowBlock);
-  const int nc = (int)cdiv(k, kSuperK);
-  const int tiles_m = (int)cdiv(m, T::BM);
-  const int tiles_n = (int)cdiv(padded_n(n), T::BN);
-  const int64_t grid = (int64_t)tiles_m * tiles_n;
-  const int vec_out = n % 4 == 0 && (uintptr_t)y % (bf16 ? 8 : 16) == 0 &&
-                      (acc_out == nullptr || (uintptr_t)acc_out % 16 == 0);
-  // whole 16-byte pieces of bf16 rows: n % 8 == 0 and a 16-byte aligned y
-  const int line_out = bf16 && vec_out && n % 8 == 0 && (uintptr_t)y % 16 == 0;
-  gemmw_kernel<FM, WN, KS><<<(unsigned)grid, T::NT, 0, stream>>>(
-      xq, scale, reinterpret_cast<const uint4*>(packed), gamma, (int)m, (int)n, nb, nc,
-      padded_k(k), tiles_m, tiles_n, band, relu2, bf16, vec_out, line_out, y, acc_out);
+  if (nops < 1 || nops > kMaxMulti) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.xq = xq;
+  a.scale = scale;
+  a.kpad = padded_k(k);
+  a.m = (int)m;
+  a.nc = (int)cdiv(k, kSuperK);
+  a.tiles_m = (int)cdiv(m, T::BM);
+  a.band = band;
+  a.nseg = nops;
+  int tn = 0;
+  for (int i = 0; i < nops; ++i) {
+    const GemmProduct& o = ops[i];
+    GemmSegK& sg = a.seg[i];
+    sg.packed = reinterpret_cast<const uint4*>(o.packed);
+    sg.gamma = o.gamma;
+    sg.y = o.y;
+    sg.acc_out = o.acc_out;
+    sg.n = (int)o.n;
+    sg.nb = (int)cdiv(o.n, kRowBlock);
+    const bool vec_out = o.n % 4 == 0 && (uintptr_t)o.y % (o.bf16 ? 8 : 16) == 0 &&
+                         (o.acc_out == nullptr || (uintptr_t)o.acc_out % 16 == 0);
+    // whole 16-byte pieces of bf16 rows: n % 8 == 0 and a 16-byte aligned y
+    const bool line_out = o.bf16 && vec_out && o.n % 8 == 0 && (uintptr_t)o.y % 16 == 0;
+    sg.flags = (o.relu2 ? 1 : 0) | (o.bf16 ? 2 : 0) | (vec_out ? 4 : 0) | (line_out ? 8 : 0);
+    a.tn_begin[i] = tn;
+    tn += (int)cdiv(padded_n(o.n), T::BN);
+  }
+  a.tiles_n = tn;
+  const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
+  if (nops > 1)
+    gemmw_kernel<FM, WN, KS, true><<<(unsigned)grid, T::NT, 0, stream>>>(a);
+  else
+    gemmw_kernel<FM, WN, KS, false><<<(unsigned)grid, T::NT, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -411,12 +474,10 @@ void gemm_tile_shape(int variant, int* bm, int* bn) {
 // band: tile rows per band of the XCD-grouped order.
 constexpr int kBand = 4;
 
-hipError_t launch_gemm(int variant, const int8_t* xq, const float* scale, const uint32_t* packed,
-                       const float* gamma, int64_t m, int64_t n, int64_t k, bool relu2,
-                       bool bf16, void* y, int32_t* acc_out, hipStream_t stream) {
-#define BL_GEMMW(FM, WN, KS)                                                                  \
-  return runw<FM, WN, KS>(xq, scale, packed, gamma, m, n, k, kBand, relu2, bf16, y, acc_out, \
-                          stream)
+hipError_t launch_gemm_multi(int variant, const int8_t* xq, const float* scale, int64_t m,
+                             int64_t k, const GemmProduct* ops, int nops, hipStream_t stream) {
+#define BL_GEMMW(FM, WN, KS) \
+  return runw_multi<FM, WN, KS>(xq, scale, m, k, kBand, ops, nops, stream)
   switch (variant) {
     case 0: BL_GEMMW(4, 8, 2);
     case 1: BL_GEMMW(2, 8, 2);
@@ -425,6 +486,13 @@ hipError_t launch_gemm(int variant, const int8_t* xq, const float* scale, const 
     default: return hipErrorInvalidValue;
   }
 #undef BL_GEMMW
+}
+
+hipError_t launch_gemm(int variant, const int8_t* xq, const float* scale, const uint32_t* packed,
+                       const float* gamma, int64_t m, int64_t n, int64_t k, bool relu2,
+                       bool bf16, void* y, int32_t* acc_out, hipStream_t stream) {
+  const GemmProduct one{packed, gamma, n, relu2, bf16, y, acc_out};
+  return launch_gemm_multi(variant, xq, scale, m, k, &one, 1, stream);
 }
 
 }  // namespace bl

@@ -164,6 +164,44 @@ bl_status bitlinear_forward(const int8_t* xq, const float* scale, const void* pa
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * bitlinear_forward_multi -- several BitLinear products that read the same
+ * quantized activations (e.g. the q, k and v projections of one token
+ * batch), each y_i = (x~ W~_i^T) * gamma_i / s as in bitlinear_forward
+ * ("Matrix Multiplication as Pure Integer Addition"), with the same
+ * numbers as one bitlinear_forward per entry.  When the products together
+ * are wide enough for the matrix-core GEMM (more than 64 tokens), they run
+ * as one launch whose output tiles cover all entries; otherwise one launch
+ * per entry.
+ *
+ *   xq, scale  from bitlinear_quant_act (m tokens, k inputs), shared.
+ *   ops        host array of nops (1..BL_MAX_MULTI) entries: packed
+ *              weights (n_i, k) 16-byte aligned, gamma_i, epilogue, y
+ *              dtype, y_i [m][n_i], acc_out_i (nullable), as in
+ *              bitlinear_forward.  The summed padded widths (64 *
+ *              ceil(n_i / 64)) must not exceed BL_MAX_MN.
+ *   workspace  bitlinear_forward_multi_workspace_bytes(ops, nops, m, k)
+ *              bytes, with the contract of bitlinear_forward's workspace
+ *              (the entries run in order and share it).
+ * m == 0 is a no-op.  Errors as bitlinear_forward, checked for every entry
+ * before any launch.
+ * ---------------------------------------------------------------------- */
+#define BL_MAX_MULTI 16
+typedef struct {
+  const void* packed;   /* packed weights (n, k), 16-byte aligned */
+  const float* gamma;   /* device fp32 */
+  int64_t n;
+  int epilogue;         /* BL_EPI_NONE or BL_EPI_RELU2 */
+  int y_dtype;          /* BL_F32 or BL_BF16 */
+  void* y;              /* [m][n] */
+  int32_t* acc_out;     /* nullable, int32 [m][n] */
+} bl_product;
+size_t bitlinear_forward_multi_workspace_bytes(const bl_product* ops, int nops, int64_t m,
+                                               int64_t k);
+bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t m, int64_t k,
+                                  const bl_product* ops, int nops, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * bitlinear_forward_fused -- the decode step of several BitLinear layers that
  * read the same token batch size, in one launch: for each entry, per-token
  * absmax int8 quantization of its activations ("8-Bit Activation

@@ -123,6 +123,47 @@ def test_forward_rejects(bl):
     assert call(m=0, xq=None, y=None) == 0        # empty batch: no-op
 
 
+def test_forward_multi_rejects(bl):
+    f = bl.lib.bitlinear_forward_multi
+
+    def table(*entries):
+        arr = (bl.BLProduct * max(1, len(entries)))()
+        for e, d in zip(arr, entries):
+            e.packed, e.gamma, e.n = d.get("pk", FAKE), d.get("g", FAKE), d.get("n", 64)
+            e.epilogue, e.y_dtype = d.get("epi", 0), d.get("yd", 0)
+            e.y, e.acc_out = d.get("y", FAKE), d.get("acc", None)
+        return arr
+
+    def call(entries, m=4, k=256, xq=FAKE, s=FAKE, ws=FAKE, wsb=1 << 30, nops=None):
+        arr = table(*entries)
+        return f(xq, s, m, k, arr, len(entries) if nops is None else nops, ws, wsb, None)
+
+    one = [{}]
+    assert f(FAKE, FAKE, 4, 256, None, 1, FAKE, 1 << 30, None) == 1
+    assert call(one, nops=0) == 1
+    assert call(one * 17) == 1
+    assert call([{"n": 0}]) == 1
+    assert call([{}, {"epi": 2}]) == 1
+    assert call([{"yd": 2}]) == 1
+    assert call([{}, {"pk": None}]) == 1
+    assert call([{"y": None}]) == 1
+    assert call(one, m=-1) == 1
+    assert call(one, k=0) == 1
+    assert call(one, k=bl.BL_MAX_K + 1) == 2
+    assert call([{"n": bl.BL_MAX_MN}, {"n": 64}]) == 2   # summed widths past the limit
+    assert call(one, xq=FAKE + 4) == 3
+    assert call([{}, {"y": FAKE + 2}]) == 3
+    # products that run one by one and split K need the workspace
+    need = bl.lib.bitlinear_forward_multi_workspace_bytes(table({}, {"n": 200}), 2, 1, 65536)
+    assert need == bl.forward_workspace_bytes(1, 200, 65536) > 0
+    assert call([{}, {"n": 200}], m=1, k=65536, ws=None) == 4
+    assert call([{}, {"n": 200}], m=1, k=65536, wsb=need - 4) == 4
+    assert call(one, m=0, xq=None, s=None) == 0            # empty batch: no-op
+    # one GEMM launch over the table needs none
+    qkv = table({"n": 8192}, {"n": 1024}, {"n": 1024})
+    assert bl.lib.bitlinear_forward_multi_workspace_bytes(qkv, 3, 512, 8192) == 0
+
+
 def test_workspace_init_rejects(bl):
     w = bl.lib.bitlinear_workspace_init
     assert w(None, 0, None) == 0

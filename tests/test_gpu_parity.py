@@ -334,6 +334,69 @@ def test_gemm_bf16_lines_stay_inside_output(B):
         assert_y_close(host(y), r["y"], "bf16", f"m={m} n={n}")
 
 
+MULTI_CASES = [
+    # m, k, [(n, relu2, y dtype)]
+    (1024, 512, [(4096, True, "bf16"), (1000, False, "f32"), (640, False, "bf16")]),   # one GEMM
+    (300, 1000, [(130, True, "bf16"), (2560, False, "bf16"), (6000, True, "f32")]),   # ragged
+    (1024, 256, [(512, i % 2 == 1, "bf16" if i % 3 else "f32") for i in range(16)]),  # 16 entries
+    (3, 2560, [(2560, False, "bf16"), (640, False, "bf16"), (640, False, "bf16")]),   # one by one
+    (1, 16384, [(200, False, "f32"), (64, True, "bf16")]),                           # split K
+]
+
+
+@pytest.mark.parametrize("m,k,specs", MULTI_CASES)
+def test_forward_multi_matches_forward(B, m, k, specs):
+    # the same numbers as one bitlinear_forward per entry, bit for bit
+    import torch
+    log(f"forward_multi m={m} k={k} entries={len(specs)}")
+    _, x = random_case(m * 7 + k, m, 1, k, x_kind="t3")
+    xq, s = B.quant_act(x_device(x, "bf16")[0])
+    ops, refs = [], []
+    for i, (n, relu2, ydt) in enumerate(specs):
+        w, _ = random_case(1000 + 31 * i + n, 1, n, k)
+        packed, gamma = B.pack_weights(dev(w))
+        dt = torch.bfloat16 if ydt == "bf16" else torch.float32
+        ops.append(dict(packed=packed, gamma=gamma, n=n, relu2=relu2,
+                        y=torch.empty((m, n), dtype=dt, device="cuda"),
+                        acc_out=torch.empty((m, n), dtype=torch.int32, device="cuda")))
+        refs.append(B.forward(xq, s, packed, gamma, n, k, relu2=relu2, out_dtype=dt,
+                              acc_out=True))
+    B.forward_multi(xq, s, k, ops)
+    for i, (o, (y, acc)) in enumerate(zip(ops, refs)):
+        np.testing.assert_array_equal(host(o["acc_out"]), host(acc), err_msg=f"acc of entry {i}")
+        np.testing.assert_array_equal(host(o["y"].view(torch.int16 if o["y"].dtype == torch.bfloat16
+                                                       else torch.int32)),
+                                      host(y.view(torch.int16 if y.dtype == torch.bfloat16
+                                                  else torch.int32)), err_msg=f"y of entry {i}")
+
+
+def test_forward_multi_against_oracle(B):
+    # a table that runs as one GEMM launch, checked against the oracle
+    m, k = 520, 300
+    specs = [(3000, True, "bf16"), (136, False, "f32"), (4100, False, "bf16")]
+    assert B.lib.bitlinear_forward_multi_workspace_bytes(
+        (B.BLProduct * 3)(*[B.BLProduct(n=n) for (n, _, _) in specs]), 3, m, k) == 0
+    _, x = random_case(77, m, 1, k, x_kind="t3")
+    xd, xo = x_device(x, "f32")
+    xq, s = B.quant_act(xd)
+    import torch
+    ops, ws = [], []
+    for i, (n, relu2, ydt) in enumerate(specs):
+        w, _ = random_case(500 + i, 1, n, k)
+        packed, gamma = B.pack_weights(dev(w))
+        dt = torch.bfloat16 if ydt == "bf16" else torch.float32
+        ops.append(dict(packed=packed, gamma=gamma, n=n, relu2=relu2,
+                        y=torch.empty((m, n), dtype=dt, device="cuda"),
+                        acc_out=torch.empty((m, n), dtype=torch.int32, device="cuda")))
+        ws.append(w)
+    B.forward_multi(xq, s, k, ops)
+    for i, (o, w, (n, relu2, ydt)) in enumerate(zip(ops, ws, specs)):
+        g = host(o["gamma"])[0]
+        r = O.forward(xo, w, relu2=relu2, y_dtype=ydt, gamma=g)
+        np.testing.assert_array_equal(host(o["acc_out"]), r["acc"], err_msg=f"entry {i}")
+        assert_y_close(host(o["y"]), r["y"], ydt, f"entry {i}")
+
+
 def test_forward_empty_batch(B):
     import torch
     w, _ = random_case(1, 1, 64, 256)
