@@ -28,11 +28,10 @@ __device__ __forceinline__ void lds_copy16(const void* src, void* lds_wave_base)
 // waves.  x~, which all waves share, goes global -> LDS by DMA in two
 // stages of KS super-chunks each: the copies of the next stage are in
 // flight while the current one is computed.  The packed words are private
-// to their wave, so they skip LDS: each lane loads its 16 words of a
-// super-chunk as dwords straight into registers, component j of the next
-// super-chunk into the registers that component j of the current one has
-// just left (no LDS traffic for the weights, no extra registers, and the
-// barrier only publishes x~).
+// to their wave, so they skip LDS: each lane loads its 64 bytes of a
+// super-chunk as four 16-byte loads straight into registers, those of the
+// next super-chunk early in the current one (no LDS traffic for the
+// weights, and the barrier only publishes x~).
 //
 // v_mfma_i32_32x32x32_i8 lanes: lane l = c + 32 ph (c = l % 32, ph = l / 32)
 // supplies row/column c of its operand for 16 inputs; a super-chunk is 8
@@ -50,7 +49,9 @@ __device__ __forceinline__ void lds_copy16(const void* src, void* lds_wave_base)
 // rows each, column-major inside a band) and consecutive numbers go to the
 // same XCD (workgroups are dispatched to the 8 XCDs round-robin), so the
 // workgroups that share an XCD's L2 cover a compact block of the output and
-// share its x~ rows and packed columns.
+// share its x~ rows and packed columns.  With several products (q, k, v
+// sharing x~) their column tiles sit side by side in one grid.
+
 // One product of the table in the kernel arguments; the first column tile
 // of every product shares one 64-byte line (tn_begin), so a workgroup finds
 // its product with one scalar load.
@@ -98,10 +99,10 @@ __device__ __forceinline__ int tile_of_block(int bid, int tiles, int tiles_m, in
 }
 
 // At least two waves per SIMD (registers within 256 per lane): one wave's
-// waits are covered by the other's MFMAs.
-// MULTI: the table may hold several products (a scalar lookup finds this
-// workgroup's); otherwise it is product 0 at fixed offsets, so its fields
-// load together with the other arguments.
+// waits are covered by the other's MFMAs.  MULTI: the table may hold
+// several products (a scalar lookup finds this workgroup's); otherwise it
+// is product 0 at fixed offsets, so its fields load together with the
+// other arguments.
 template <int FM, int WN, int KS, bool MULTI>
 __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) void gemmw_kernel(
     GemmArgs args) {
