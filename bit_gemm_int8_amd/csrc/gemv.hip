@@ -23,6 +23,8 @@
 //   - the waves' sums meet in LDS; when the row blocks alone cannot fill the
 //     chip, `splits` workgroups share a row block and combine through one
 //     64-bit device-scope atomic per output (no counters, no fences).
+#include <climits>
+
 #include "bl_device.h"
 #include "bl_internal.h"
 
@@ -474,16 +476,28 @@ __device__ __forceinline__ void quantize_into_lds(const FusedSeg& sg, int g0, in
 }
 
 template <int M, int WAVES, int PF, int QPL, bool LONGX>
-__global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(FusedArgs args) {
+// The entry count and the first workgroup of entries 1..13 lead the kernel
+// arguments as plain ints (entries past nseg: INT_MAX), which the hardware
+// can preload into scalar registers: a workgroup then finds its entry with
+// no memory access and reads that entry's fields with a single load.
+__global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(
+    int nseg, int wb1, int wb2, int wb3, int wb4, int wb5, int wb6, int wb7, int wb8, int wb9,
+    int wb10, int wb11, int wb12, int wb13, FusedArgs args) {
   constexpr int RPW = 16 * QPL, SUBS = 4 / QPL;     // rows per group, groups per row block
   __shared__ int red[WAVES > 1 ? WAVES - 1 : 1][M][64];
   __shared__ uint32_t red_max[WAVES][M];
   extern __shared__ uint4 xs_lds[];
   // segment of this workgroup
+  const int bid = (int)blockIdx.x;
+  const int wb[13] = {wb1, wb2, wb3, wb4, wb5, wb6, wb7, wb8, wb9, wb10, wb11, wb12, wb13};
   int si = 0;
 #pragma unroll
-  for (int i = 1; i < kMaxFused; ++i)
-    if (i < args.nseg && (int)blockIdx.x >= args.wg_begin[i]) si = i;
+  for (int i = 0; i < 13; ++i) si = bid >= wb[i] ? i + 1 : si;
+  if (nseg > 14) {
+#pragma unroll
+    for (int i = 14; i < kMaxFused; ++i)
+      if (i < nseg && bid >= args.wg_begin[i]) si = i;
+  }
   const FusedSeg& sg = args.seg[si];
   const int local = (int)blockIdx.x - sg.wg_begin;
   const int splits = sg.splits;
@@ -864,10 +878,14 @@ hipError_t launch_gemv_mfma_fused(const FusedArgs& args, int m, int variant, boo
 // than 1024 16-byte units.
 hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, int qpl, bool long_rows,
                              int groups, size_t lds, hipStream_t stream) {
+  int wb[14];
+  for (int i = 1; i < 14; ++i) wb[i] = i < args.nseg ? args.wg_begin[i] : INT_MAX;
 #define BL_FUSED(MM, WW, QQ, LL)                                                       \
   do {                                                                                 \
     gemv_fused_kernel<MM, WW, (QQ == 1 ? 4 : 2), QQ, LL>                               \
-        <<<(unsigned)groups, 64 * WW, lds, stream>>>(args);                            \
+        <<<(unsigned)groups, 64 * WW, lds, stream>>>(                                  \
+            args.nseg, wb[1], wb[2], wb[3], wb[4], wb[5], wb[6], wb[7], wb[8], wb[9],     \
+            wb[10], wb[11], wb[12], wb[13], args);                                         \
     return hipGetLastError();                                                          \
   } while (0)
 #define BL_FUSED_Q(MM, WW, LL) \
