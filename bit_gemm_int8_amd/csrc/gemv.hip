@@ -578,7 +578,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(
 // Workgroup g of an entry owns WR row groups of SB 16-row sub-blocks; its
 // WK waves per group split the super-chunks and meet in LDS at the end.
 template <int WR, int WK, int SB, int PF, int RPU, int MT, bool FAST>
-__global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(FusedArgs args, int m_all) {
+// Leading scalar arguments (preloadable into SGPRs, as in gemv_fused_kernel):
+// the token count, the entry count and the first workgroup of entries 1..12
+// (INT_MAX past nseg).
+__global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(
+    int m_all, int nseg, int wb1, int wb2, int wb3, int wb4, int wb5, int wb6, int wb7, int wb8,
+    int wb9, int wb10, int wb11, int wb12, FusedArgs args) {
   static_assert(RPU == 2 || RPU == 4, "16-byte activation units per x~ unit: 2 (bf16 only), 4");
   // FAST: every entry's rows are whole 16-byte units at 16-byte alignment,
   // so the activation loads are plain vector loads with no branch (a load
@@ -598,10 +603,16 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(FusedArgs
   // token block blockIdx.y: tokens t0 .. t0 + m - 1 (16 per block)
   const int t0 = 16 * (int)blockIdx.y;
   const int m = min(m_all - t0, MT);
+  const int bid = (int)blockIdx.x;
+  const int wgb[12] = {wb1, wb2, wb3, wb4, wb5, wb6, wb7, wb8, wb9, wb10, wb11, wb12};
   int si = 0;
 #pragma unroll
-  for (int i = 1; i < kMaxFused; ++i)
-    if (i < args.nseg && (int)blockIdx.x >= args.wg_begin[i]) si = i;
+  for (int i = 0; i < 12; ++i) si = bid >= wgb[i] ? i + 1 : si;
+  if (nseg > 13) {
+#pragma unroll
+    for (int i = 13; i < kMaxFused; ++i)
+      if (i < nseg && bid >= args.wg_begin[i]) si = i;
+  }
   const FusedSeg& sg = args.seg[si];
   const int local = (int)blockIdx.x - sg.wg_begin;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -852,9 +863,13 @@ hipError_t launch_gemv_mfma_fused(const FusedArgs& args, int m, int variant, boo
                                   bool all_fast, int groups, hipStream_t stream) {
   if (m < 1 || m > 64) return hipErrorInvalidValue;
   const dim3 grid((unsigned)groups, (unsigned)((m + 15) / 16));   // token blocks of 16
+  int wb[13];
+  for (int i = 1; i < 13; ++i) wb[i] = i < args.nseg ? args.wg_begin[i] : INT_MAX;
 #define BL_MF(WR, WK, SB, PF, RPU, MT, FAST)                                         \
   gemv_mfma_fused_kernel<WR, WK, SB, PF, RPU, MT, FAST>                              \
-      <<<grid, 64 * WR * WK, 0, stream>>>(args, m)
+      <<<grid, 64 * WR * WK, 0, stream>>>(m, args.nseg, wb[1], wb[2], wb[3], wb[4], wb[5],  \
+                                          wb[6], wb[7], wb[8], wb[9], wb[10], wb[11], wb[12],  \
+                                          args)
 #define BL_MF_X(WR, WK, SB, PF, MT)               \
   if (all_fast && all_bf16) BL_MF(WR, WK, SB, PF, 2, MT, true); \
   else if (all_fast) BL_MF(WR, WK, SB, PF, 4, MT, true);       \
