@@ -405,3 +405,58 @@ def test_forward_empty_batch(B):
     s = torch.empty(0, dtype=torch.float32, device="cuda")
     y = B.forward(xq, s, packed, gamma, 64, 256)
     assert y.shape == (0, 64)
+
+
+def test_graph_replays_match_eager(B):
+    # captured launches (a split-K GEMV with its workspace, a fused decode
+    # step, a GEMM table) replayed several times, with eager work between
+    # the replays, give the eager bits every time
+    import torch
+    w1, x1 = random_case(11, 1, 300, 40000)            # dot4 GEMV, split K
+    p1, g1 = B.pack_weights(dev(w1))
+    xq1, s1 = B.quant_act(dev(x1))
+    w2, x2 = random_case(12, 1, 640, 2560, x_kind="t3")
+    p2, g2 = B.pack_weights(dev(w2))
+    x2d = x_device(x2, "bf16")[0]
+    _, x3 = random_case(13, 600, 1, 512, x_kind="t3")
+    xq3, s3 = B.quant_act(dev(x3))
+    mats3 = [B.pack_weights(dev(random_case(14 + i, 1, n, 512)[0])) for i, n in
+             enumerate((4096, 640, 1000))]
+    ws = B.Workspace()
+    y1 = torch.empty((1, 300), dtype=torch.float32, device="cuda")
+    y2 = torch.empty((1, 640), dtype=torch.bfloat16, device="cuda")
+    y3 = [torch.empty((600, n), dtype=torch.bfloat16, device="cuda") for n in (4096, 640, 1000)]
+    step = B.FusedStep([dict(x=x2d, packed=p2, gamma=g2, n=640, k=2560, y=y2)], workspace=ws)
+    ops3 = [dict(packed=p, gamma=g, n=n, y=y, relu2=(i == 0))
+            for i, ((p, g), n, y) in enumerate(zip(mats3, (4096, 640, 1000), y3))]
+
+    def work():
+        B.forward(xq1, s1, p1, g1, 300, 40000, y=y1, workspace=ws)
+        step()
+        B.forward_multi(xq3, s3, 512, ops3, workspace=ws)
+
+    work()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in [y1, y2] + y3]
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        work()                                         # warm on the capture stream
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in [y1, y2] + y3:
+            t.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip([y1, y2] + y3, ref)):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), \
+                f"replay {rep}, output {i}"
+        work()                                         # eager work between replays
+        torch.cuda.synchronize()
+    assert not host(ws.buf).any(), "workspace not left zero-filled"
