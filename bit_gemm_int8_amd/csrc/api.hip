@@ -394,6 +394,16 @@ bl_status bitlinear_quant_act(const void* x, int x_dtype, int64_t m, int64_t k, 
   return e == hipSuccess ? BL_OK : BL_ERR_HIP;
 }
 
+// Workgroups of a GEMM launch over products of widths ns[0..count-1]: the
+// kernel numbers its tiles with 32-bit ints, so larger grids are refused.
+static int64_t gemm_grid(int variant, int64_t m, const int64_t* ns, int count) {
+  int bm, bn;
+  gemm_tile_shape(variant, &bm, &bn);
+  int64_t tn = 0;
+  for (int i = 0; i < count; ++i) tn += cdiv(padded_n(ns[i]), bn);
+  return cdiv(m, bm) * tn;
+}
+
 // A table of products sharing x~: the plan of one product over the summed
 // output width decides.  If it is the GEMM, one launch over the table;
 // otherwise each product gets its own plan and launch (the same numbers).
@@ -451,6 +461,9 @@ bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t 
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const FwdPlan whole = forward_plan(m, nt, k);
   if (whole.kind == 1) {
+    int64_t ns[kMaxMulti];
+    for (int i = 0; i < nops; ++i) ns[i] = ops[i].n;
+    if (gemm_grid(whole.variant, m, ns, nops) > INT32_MAX) return BL_ERR_UNSUPPORTED_SHAPE;
     GemmProduct g[kMaxMulti];
     for (int i = 0; i < nops; ++i)
       g[i] = GemmProduct{ops[i].packed, ops[i].gamma, ops[i].n, ops[i].epilogue == BL_EPI_RELU2,
@@ -462,6 +475,11 @@ bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t 
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return BL_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return BL_ERR_MISALIGNED;
+  }
+  for (int i = 0; i < nops; ++i) {
+    const FwdPlan plan = forward_plan(m, ops[i].n, k);
+    if (plan.kind == 1 && gemm_grid(plan.variant, m, &ops[i].n, 1) > INT32_MAX)
+      return BL_ERR_UNSUPPORTED_SHAPE;
   }
   for (int i = 0; i < nops; ++i) {
     const bl_product& o = ops[i];
@@ -489,6 +507,8 @@ bl_status bitlinear_forward(const int8_t* xq, const float* scale, const void* pa
       !aligned(y, y_dtype == BL_BF16 ? 2 : 4) || (acc_out != nullptr && !aligned(acc_out, 4)))
     return BL_ERR_MISALIGNED;
   const FwdPlan plan = forward_plan(m, n, k);
+  if (plan.kind == 1 && gemm_grid(plan.variant, m, &n, 1) > INT32_MAX)
+    return BL_ERR_UNSUPPORTED_SHAPE;
   if (plan.ws_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return BL_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return BL_ERR_MISALIGNED;

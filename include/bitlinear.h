@@ -54,7 +54,8 @@ extern "C" {
 typedef enum {
   BL_OK = 0,
   BL_ERR_INVALID_ARG = 1,       /* null pointer, size < allowed minimum, bad enum, bad eps */
-  BL_ERR_UNSUPPORTED_SHAPE = 2, /* size above BL_MAX_K or BL_MAX_MN */
+  BL_ERR_UNSUPPORTED_SHAPE = 2, /* size above BL_MAX_K or BL_MAX_MN, or a matrix-core
+                                   GEMM of more than 2^31 - 1 output tiles */
   BL_ERR_MISALIGNED = 3,        /* pointer below its documented alignment */
   BL_ERR_WORKSPACE = 4,         /* workspace pointer NULL or smaller than required */
   BL_ERR_HIP = 5                /* the HIP runtime reported an error at launch */

@@ -121,6 +121,8 @@ def test_forward_rejects(bl):
     assert call(m=1, k=65536, wsb=need - 4) == 4
     assert call(m=1, k=65536, ws=FAKE + 16, wsb=need) == 3
     assert call(m=0, xq=None, y=None) == 0        # empty batch: no-op
+    # a GEMM grid past 32-bit tile numbering is refused before any launch
+    assert call(m=bl.BL_MAX_MN, n=bl.BL_MAX_MN, k=256) == 2
 
 
 def test_forward_multi_rejects(bl):
@@ -159,6 +161,7 @@ def test_forward_multi_rejects(bl):
     assert call([{}, {"n": 200}], m=1, k=65536, ws=None) == 4
     assert call([{}, {"n": 200}], m=1, k=65536, wsb=need - 4) == 4
     assert call(one, m=0, xq=None, s=None) == 0            # empty batch: no-op
+    assert call([{"n": bl.BL_MAX_MN // 2}, {"n": bl.BL_MAX_MN // 4}], m=bl.BL_MAX_MN) == 2
     # one GEMM launch over the table needs none
     qkv = table({"n": 8192}, {"n": 1024}, {"n": 1024})
     assert bl.lib.bitlinear_forward_multi_workspace_bytes(qkv, 3, 512, 8192) == 0
