@@ -58,7 +58,7 @@ hipError_t launch_gemm_multi(int variant, const int8_t* xq, const float* scale, 
                              int64_t k, const GemmProduct* ops, int nops, hipStream_t stream);
 
 // Fused decode step: a table of BitLinear products that share a token batch
-// (M <= 16), each quantizing its own activations in the kernel prologue.
+// (M <= 64), each quantizing its own activations in the kernel prologue.
 constexpr int kMaxFused = 16;
 // One entry of the fused decode step.  The fields a workgroup needs first
 // share the first 64-byte line (one scalar load after the entry is known);
