@@ -71,6 +71,10 @@ struct GemmArgs {
   GemmSegK seg[kMaxMulti];
 };
 
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt = 0 only:
+// vmcnt[3:0] = 0, expcnt[6:4] = 7, lgkmcnt[11:8] = 15, vmcnt[15:14] = 0.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 template <int FM, int WN, int KS>
 struct TileW {
   static constexpr int BM = 32 * FM;
@@ -257,21 +261,33 @@ __global__ __launch_bounds__(64 * WN) __attribute__((amdgpu_waves_per_eu(2))) vo
       if (cc + k < c1) compute(As + k * T::A_CHUNK, cc + k);
   };
 
+  // The compiler counts a global -> LDS copy as a flat access (global and
+  // LDS) and, while one is in flight, waits for every outstanding vector
+  // memory operation before any use of a loaded register.  The packed words
+  // a stage starts on were loaded a whole super-chunk earlier, so wait for
+  // them before the stage's copies are issued: then nothing the stage
+  // computes on is still in flight behind the copies, and they stay in
+  // flight until the weights of the next super-chunk are needed.
+  auto copy_stage_after_b = [&](uint8_t* As, int cc) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    copy_stage(As, cc);
+  };
+
   // Pairs of stages, then an odd last one.
   load_b(bw, c0);
   if (c0 < c1) copy_stage(A0, c0);
   __syncthreads();
   int cc = c0;
   for (; cc + 2 * KS <= c1; cc += 2 * KS) {
-    copy_stage(A1, cc + KS);
+    copy_stage_after_b(A1, cc + KS);
     compute_stage(A0, cc);
     __syncthreads();
-    if (cc + 2 * KS < c1) copy_stage(A0, cc + 2 * KS);
+    if (cc + 2 * KS < c1) copy_stage_after_b(A0, cc + 2 * KS);
     compute_stage(A1, cc + KS);
     __syncthreads();
   }
   if (cc < c1) {
-    if (cc + KS < c1) copy_stage(A1, cc + KS);
+    if (cc + KS < c1) copy_stage_after_b(A1, cc + KS);
     compute_stage(A0, cc);
     __syncthreads();
     if (cc + KS < c1) compute_stage(A1, cc + KS);
