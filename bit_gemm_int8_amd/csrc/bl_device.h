@@ -23,6 +23,16 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// 16 bytes of packed weights, which a product reads exactly once: a
+// non-temporal load (the "nt" cache policy), so the stream does not
+// displace reusable lines from the caches.  Measured on MI355X: a 58.7 MB
+// read in the GEMV's access pattern streams at 6.1 TB/s this way against
+// 5.7 TB/s with ordinary loads.
+__device__ __forceinline__ uint4 load_stream16(const uint4* p) {
+  const bl_v4i v = __builtin_nontemporal_load(reinterpret_cast<const bl_v4i*>(p));
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
 constexpr int kRowBlock = 64;     // rows per packed block
 constexpr int kSuperK = 256;      // inputs per packed super-chunk
 constexpr int kBlockU4 = 256;     // uint4 per 4 KiB packed block

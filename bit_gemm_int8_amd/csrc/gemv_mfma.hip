@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_win_kernel(
 #pragma unroll
     for (int i = 0; i < XU; ++i) xr[p][i] = xsrc[i][(int64_t)c * 16];
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) wb[p][sb] = blk[(int64_t)c * kBlockU4 + sb * 16];
+    for (int sb = 0; sb < SB; ++sb) wb[p][sb] = load_stream16(blk + (int64_t)c * kBlockU4 + sb * 16);
   };
   static_for<PF>([&](auto P) { load_chunk(P, min(c0 + (int)P, clast)); });
   if (threadIdx.x < MT) {
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_win_kernel(
       }
     }
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) wb[p][sb] = blk[(int64_t)cn * kBlockU4 + sb * 16];
+    for (int sb = 0; sb < SB; ++sb) wb[p][sb] = load_stream16(blk + (int64_t)cn * kBlockU4 + sb * 16);
     __builtin_amdgcn_sched_barrier(0);
   };
   int t = 0;
