@@ -1,6 +1,6 @@
 // Decode ternary GEMV for one or two tokens with the fused dequant, and the
 // fused decode step (activation quantization + products of several matrices
-// in one launch): v_dot4 for 1-2 tokens, int8 matrix cores for 3-16.
+// in one launch): v_dot4 for 1-2 tokens, int8 matrix cores for 3-64.
 //
 // "BitNet b1.58 2B4T Guide: Scaling Native 1-Bit LLMs", section "Matrix
 // Multiplication as Pure Integer Addition": acc = x~ W~^T in an integer
@@ -10,11 +10,14 @@
 // At batch 1 the product reads every packed weight once and does two integer
 // ops per 1/4 byte, so the kernel is bound by HBM bandwidth.  Layout of the
 // work (the packed layout is in include/bitlinear.h):
-//   - a workgroup owns one 64-row packed block (lane = row) and WAVES waves
-//     split its 256-input super-chunks into contiguous ranges;
-//   - per super-chunk a lane loads its row's 64 bytes as four 128-bit loads
-//     q = 0..3; each load instruction of a wave reads 1 KiB of contiguous
-//     memory, and PF super-chunks per wave are in flight at once;
+//   - a workgroup owns a group of rows, either 16 rows with four lanes per
+//     row (QPL = 1) or a 64-row packed block with one lane per row
+//     (QPL = 4), and WAVES waves split its 256-input super-chunks into
+//     contiguous ranges;
+//   - per super-chunk a lane loads QPL of the four 16-byte parts q of its
+//     row's 64 bytes; each load instruction of a wave reads 1 KiB of
+//     contiguous memory, non-temporally (the weights are read once), and PF
+//     super-chunks per wave are in flight at once;
 //   - all lanes of a wave work on the same inputs: the workgroup puts its
 //     slice of x~ in LDS once (after issuing its first weight loads) and the
 //     lanes read it at one shared address, which the LDS broadcasts;
