@@ -27,7 +27,7 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t words) {
 
 constexpr int64_t kGemvMaxM = 2;           // dot4 GEMV up to here
 constexpr int64_t kMfmaGemvMaxM = 64;      // windowed MFMA GEMV up to here (4 token groups)
-constexpr int64_t kGemvTargetGroups = 512;
+constexpr int64_t kGemvTargetGroups = 256;  // one token: about one workgroup per CU
 constexpr int64_t kGemvMaxLds = 48 * 1024;
 constexpr int64_t kCUs = 256;
 
@@ -47,23 +47,27 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
   const int64_t nc = cdiv(k, kSuperK);
   if (m <= 0) return p;
   if (m <= kGemvMaxM) {
-    // Rows up to 40 super-chunks (K <= 10240): 16-row groups (a quarter of
-    // a packed block each, four lanes per row), no K split, 8 waves when a
-    // group has >= 16 super-chunks.  Longer rows: 64-row groups, split over
-    // up to 4 workgroups when the row blocks alone cannot fill the chip
-    // (one atomic combine per output), each keeping >= 2 super-chunks; 8
-    // waves when a group has >= 6 super-chunks, two in flight per wave once
-    // a wave streams >= 4.  Each group's x~ slice must fit LDS.  (Tuned on
-    // MI355X over the 2B- and 100B-class decode shapes.)
+    // Rows up to 40 super-chunks (K <= 10240) of matrices with fewer than
+    // 256 row blocks: 16-row groups (a quarter of a packed block each, four
+    // lanes per row), no K split, 8 waves when a group has >= 16
+    // super-chunks.  Otherwise 64-row groups, split over up to 4 workgroups
+    // when the row blocks alone give fewer than about one workgroup per CU
+    // at one token (two at two tokens), each keeping >= 2 super-chunks (one
+    // atomic combine per output); 4 waves per group when that leaves >= 128
+    // workgroups (at two tokens only without a split: the dot4 work doubles
+    // and one wave per SIMD no longer hides it), else 8 once a group has
+    // >= 6 super-chunks; two super-chunks in flight per wave once a wave
+    // streams >= 4.  Each group's x~ slice must fit LDS.  (Tuned on MI355X
+    // over the 2B- and 100B-class decode shapes and other long rows.)
     p.kind = 0;
     int64_t s = 1;
-    if (nc <= 40 && m * nc * 256 <= kGemvMaxLds) {
+    if (nc <= 40 && m * nc * 256 <= kGemvMaxLds && (nb < 256 || nc < 16)) {
       p.qpl = 1;
       p.variant = nc >= 16 ? 8 : 4;
       p.pf = 4;
     } else {
       if (nb < 256) {
-        s = cdiv(kGemvTargetGroups, nb);
+        s = cdiv(m == 1 ? kGemvTargetGroups : 2 * kGemvTargetGroups, nb);
         if (s > 4) s = 4;
         const int64_t smax = nc / 2 > 1 ? nc / 2 : 1;
         if (s > smax) s = smax;
@@ -71,7 +75,8 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
       while (m * cdiv(nc, s) * 256 > kGemvMaxLds) ++s;
       const int64_t per_group = nc / s;
       p.qpl = 4;
-      p.variant = per_group >= 6 ? 8 : 4;
+      const bool four = nb * s >= 128 && (m == 1 || s == 1);
+      p.variant = four || per_group < 6 ? 4 : 8;
       p.pf = per_group / p.variant >= 4 ? 2 : 1;
     }
     p.splits = (int)s;
