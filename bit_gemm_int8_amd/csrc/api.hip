@@ -161,8 +161,9 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   // T = super-chunks a workgroup should stream: the set's total over ~512
   // groups, kept within [8, 32].  Entries with up to 2T super-chunks keep
   // one group per row block; longer ones are split (atomic combine) into
-  // ~T-chunk ranges.  4 waves per group for decode-sized sets (T < 16), 8
-  // for large ones.  Rows per group: 16 (four lanes per row) when that
+  // ~T-chunk ranges.  4 waves per group (at two tokens 8 for large sets,
+  // T >= 16; at one token 4 measured 9-18% faster on the 100B-class up and
+  // down).  Rows per group: 16 (four lanes per row) when that
   // keeps the set within 512 groups, else 64 (a lane per row): small sets
   // are bound by each lane's unpack + dot4 work after the data arrive, large
   // ones by the number of groups, each of which reads and quantizes its x
@@ -190,7 +191,7 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   for (int i = 0; i < nops; ++i) units += cdiv(ops[i].n, kRowBlock) * cdiv(ops[i].k, kSuperK);
   int64_t t = cdiv(units, 512);
   t = t < 8 ? 8 : t > 32 ? 32 : t;
-  p.waves = t >= 16 ? 8 : 4;
+  p.waves = m == 1 || t < 16 ? 4 : 8;
   auto splits_of = [&](int64_t nc) {
     int64_t s = nc <= 2 * t ? 1 : cdiv(nc, t);
     if (s > 8) s = 8;
