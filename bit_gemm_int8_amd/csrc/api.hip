@@ -161,10 +161,13 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   // T = super-chunks a workgroup should stream: the set's total over ~512
   // groups, kept within [8, 32].  Entries with up to 2T super-chunks keep
   // one group per row block; longer ones are split (atomic combine) into
-  // ~T-chunk ranges.  4 waves per group (at two tokens 8 for large sets,
-  // T >= 16; at one token 4 measured 9-18% faster on the 100B-class up and
-  // down).  Rows per group: 16 (four lanes per row) when that
-  // keeps the set within 512 groups, else 64 (a lane per row): small sets
+  // ~T-chunk ranges, at two tokens in large sets (T >= 16) at most 2 (each
+  // split re-reads both activation rows for the absmax).  4 waves per group,
+  // except 8 for large two-token sets with a split entry.  (At one token 4
+  // waves measured 9-18% faster than 8 on the 100B-class up and down; at two
+  // tokens, up 4 waves -14%, down 2 splits x 8 waves -23%.)  Rows per group:
+  // 16 (four lanes per row) when that keeps the set within 512 groups, else
+  // 64 (a lane per row): small sets
   // are bound by each lane's unpack + dot4 work after the data arrive, large
   // ones by the number of groups, each of which reads and quantizes its x
   // range.  (Tuned on MI355X over the 2B- and 100B-class shapes.)
@@ -191,13 +194,16 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   for (int i = 0; i < nops; ++i) units += cdiv(ops[i].n, kRowBlock) * cdiv(ops[i].k, kSuperK);
   int64_t t = cdiv(units, 512);
   t = t < 8 ? 8 : t > 32 ? 32 : t;
-  p.waves = m == 1 || t < 16 ? 4 : 8;
+  const bool large2 = m > 1 && t >= 16;
   auto splits_of = [&](int64_t nc) {
     int64_t s = nc <= 2 * t ? 1 : cdiv(nc, t);
-    if (s > 8) s = 8;
+    if (s > (large2 ? 2 : 8)) s = large2 ? 2 : 8;
     while (m * cdiv(nc, s) * 256 > kGemvMaxLds) ++s;
     return s;
   };
+  bool any_split = false;
+  for (int i = 0; i < nops; ++i) any_split = any_split || splits_of(cdiv(ops[i].k, kSuperK)) > 1;
+  p.waves = large2 && any_split ? 8 : 4;
   int64_t groups16 = 0;                              // groups with 16 rows each
   for (int i = 0; i < nops; ++i)
     groups16 += cdiv(ops[i].n, kRowBlock) * 4 * splits_of(cdiv(ops[i].k, kSuperK));

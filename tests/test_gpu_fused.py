@@ -114,6 +114,38 @@ def test_fused_shared_inputs_and_unfused_agree(B):
     assert ws.buf is None or not host(ws.buf).any()
 
 
+@pytest.mark.parametrize("m", [1, 2])
+@pytest.mark.parametrize("shapes", [[(4096, 32768, False), (8192, 4096, True)],
+                                    [(16384, 8192, True)]])
+def test_fused_large_sets_agree_with_unfused(B, m, shapes):
+    """Sets of >= 2^27 weights take the plan's large-set rules (a split entry
+    beside an unsplit one; one unsplit entry; 4 or 8 waves, at most 2 splits
+    at two tokens): the fused step equals bitlinear_quant_act followed by
+    bitlinear_forward bit for bit, and leaves its workspace zero-filled."""
+    import torch
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    ops = []
+    for n, k, relu2 in shapes:
+        w = torch.randn((n, k), generator=gen, device="cuda") * 0.02
+        packed, gamma = B.pack_weights(w)
+        del w
+        x = torch.randn((m, k), generator=gen, device="cuda").to(torch.bfloat16)
+        ops.append(dict(x=x, packed=packed, gamma=gamma, n=n, k=k, relu2=relu2,
+                        y=torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
+                        acc_out=torch.empty((m, n), dtype=torch.int32, device="cuda")))
+    step = B.FusedStep(ops, workspace=B.Workspace())
+    assert (step.nbytes > 0) == (len(shapes) == 2)     # only the first set splits an entry
+    step()
+    for o in ops:
+        xq, s = B.quant_act(o["x"])
+        y, acc = B.forward(xq, s, o["packed"], o["gamma"], o["n"], o["k"], relu2=o["relu2"],
+                           out_dtype=torch.bfloat16, acc_out=True)
+        assert torch.equal(acc, o["acc_out"])
+        assert torch.equal(y.view(torch.int16), o["y"].view(torch.int16))
+    torch.cuda.synchronize()
+    assert step.ws.buf is None or not host(step.ws.buf).any()
+
+
 @pytest.mark.parametrize("m", [1, 8])
 def test_fused_c2_decode_set(B, m):
     """The decode set at 2B-class shapes, full size, one launch (1 token: the
