@@ -85,13 +85,15 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     // Windowed MFMA GEMV: 16, 32 or 64 token columns.  Many row blocks
     // (>= 256): wide row groups, the whole K per wave; fewer: slices of K
     // over the waves of a workgroup, more slices (8 at 16 tokens, 4 at 64)
-    // for long rows (>= 24 super-chunks) or few (<= 64) row blocks.  (Tuned on MI355X over the 2B- and
-    // 100B-class decode shapes.)
+    // for long rows (>= 24 super-chunks) or few (<= 64) row blocks.  Past
+    // 32 tokens, few row blocks keep 32-token blocks (twice the workgroups
+    // of 64-token ones: 2560 x 6912 at 64 tokens 12.2 -> 7.3 us).  (Tuned
+    // on MI355X over the 2B- and 100B-class decode shapes.)
     p.kind = 2;
     const bool wide = nb >= 256;
     if (m <= 16) p.variant = wide ? 2 : (nb <= 64 && nc >= 24) ? 1 : 0;
     else if (m <= 32) p.variant = wide ? 4 : 3;
-    else p.variant = wide ? 6 : (nc >= 24 || nb <= 64) ? 7 : 5;
+    else p.variant = wide ? 6 : nb <= 64 ? 3 : nc >= 24 ? 7 : 5;
     p.splits = 1;
     p.slots = 0;
   } else {
@@ -99,8 +101,8 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     // rounds of tiles over the 256 CUs keep busy, weighted by how well each
     // shape runs (128 x 512 best, 64 x 512 then 64 x 256 and 96 x 256).
     // When even that leaves more than half the CUs without a tile, the
-    // windowed MFMA GEMV takes the product in token blocks of 64 (it needs
-    // no split of K).  (Tuned on MI355X over the 2048- and 512-token
+    // windowed MFMA GEMV takes the product in token blocks of 64, or of 32
+    // for few row blocks (it needs no split of K).  (Tuned on MI355X over the 2048- and 512-token
     // prefills and the 100B-class k/v products.)
     static const double kRate[4] = {1.0, 0.9, 0.85, 0.85};
     double best = -1.0;
@@ -119,7 +121,7 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     }
     if (tiles < kCUs / 2) {
       p.kind = 2;
-      p.variant = nb >= 256 ? 6 : (nc >= 24 || nb <= 64) ? 7 : 5;
+      p.variant = nb >= 256 ? 6 : nb <= 64 ? 3 : nc >= 24 ? 7 : 5;
     } else {
       p.kind = 1;
     }
