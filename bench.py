@@ -741,8 +741,8 @@ def main():
         summarize(args.summarize, args.command, args.name)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU split is designed, not built).", file=sys.stderr)
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported (the library has "
+              "no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 
     import torch
