@@ -161,6 +161,8 @@ FWD_CASES = [
     (1, 20000, 512, False, "bf16", "bf16"),
     (2, 300, 40000, True, "f32", "bf16"),        # split K
     (2, 16448, 4100, True, "bf16", "bf16"),      # >= 256 row blocks: 64-row groups, 4 waves, ragged K
+    (40, 1000, 3000, True, "f32", "bf16"),       # 33-64 tokens, <= 64 row blocks: 32-token blocks, the 2nd partial
+    (64, 4160, 6400, False, "bf16", "f32"),      # 64 tokens, 65 row blocks, long rows: 64-token blocks, 4 slices
     # windowed MFMA GEMV, 3 to 16 tokens: 2 row groups x 4 slices
     (3, 130, 520, True, "f32", "f32"),           # 3 super-chunks: an empty slice
     (4, 300, 1000, False, "f32", "bf16"),
