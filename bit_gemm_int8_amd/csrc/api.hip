@@ -235,6 +235,15 @@ namespace {
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 inline bool valid_dtype(int d) { return d == BL_F32 || d == BL_BF16; }
 inline bool valid_eps(float e) { return isfinite(e) && e >= 0.0f; }
+// Activation eps: s = 127 / max(beta, eps) must be a finite fp32 for every
+// beta >= 0, so that an all-zero token quantizes to 0 (0 * s = 0) and no
+// product x * s is NaN.  That needs eps > 0 with fp32(127 / eps) finite
+// (eps >= about 3.74e-37); 0 and smaller values are refused.
+inline bool valid_act_eps(float e) {
+  if (!(isfinite(e) && e > 0.0f)) return false;
+  const volatile float smax = 127.0f / e;
+  return isfinite((float)smax);
+}
 }  // namespace
 
 extern "C" {
@@ -308,7 +317,7 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
                                   void* workspace, size_t workspace_bytes, void* stream) {
   const bl_status st = check_fused(ops, nops, m);
   if (st != BL_OK) return st;
-  if (!valid_eps(eps)) return BL_ERR_INVALID_ARG;
+  if (!valid_act_eps(eps)) return BL_ERR_INVALID_ARG;
   if (m == 0) return BL_OK;
   const FusedPlan plan = fused_plan(ops, nops, m);
   if (plan.ws_bytes > 0) {
@@ -396,7 +405,7 @@ bl_status bitlinear_pack_weights(const void* w, int w_dtype, int64_t n, int64_t 
 
 bl_status bitlinear_quant_act(const void* x, int x_dtype, int64_t m, int64_t k, float eps,
                               int8_t* xq, float* scale, void* stream) {
-  if (!valid_dtype(x_dtype) || !valid_eps(eps)) return BL_ERR_INVALID_ARG;
+  if (!valid_dtype(x_dtype) || !valid_act_eps(eps)) return BL_ERR_INVALID_ARG;
   if (m < 0 || k < 1) return BL_ERR_INVALID_ARG;
   if (m > BL_MAX_MN || k > BL_MAX_K) return BL_ERR_UNSUPPORTED_SHAPE;
   if (m == 0) return BL_OK;

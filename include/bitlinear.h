@@ -122,7 +122,10 @@ bl_status bitlinear_pack_weights(const void* w, int w_dtype, int64_t n, int64_t 
  * Defines: "8-Bit Activation Quantization: absmax Scaling".
  *
  *   x       [m][k] fp32 or bf16 (x_dtype), 4-byte aligned (16 for speed).
- *   eps     >= 0 and finite (1e-5 on the pages).
+ *   eps     > 0 with fp32(127 / eps) finite, i.e. eps >= about 3.74e-37
+ *           (1e-5 on the pages); 0, negative, NaN/Inf and smaller values
+ *           return BL_ERR_INVALID_ARG.  Then s is finite for every token and
+ *           an all-zero token gives x~ = 0 (and y = 0).
  *   xq      out, int8 [m][padded_k(k)], 16-byte aligned.  Columns k..K_pad-1
  *           are written as 0.
  *   scale   out, fp32 [m]:  s_m = fp32(127 / max(beta_m, eps)),
@@ -213,7 +216,7 @@ bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t 
  *   ops        host array of nops (1..BL_MAX_FUSED) entries; entries may
  *              share x (e.g. the q, k and v projections).
  *   m          tokens, 0..BL_FUSED_MAX_M (0 is a no-op).
- *   eps        as in bitlinear_quant_act.
+ *   eps        as in bitlinear_quant_act (the same values are refused).
  *   workspace  bitlinear_forward_fused_workspace_bytes(ops, nops, m) bytes,
  *              with the contract of bitlinear_forward's workspace.
  * Every workgroup recomputes its entry's per-token absmax from the whole row

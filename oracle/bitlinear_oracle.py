@@ -39,6 +39,9 @@ reason, in the design notes of the repository):
   R7  the 2-bit packing layout is this library's own (the pages only say
       that weights are packed two bits each); it is specified in
       ``pack_ternary`` below and in the C header.
+  R8  the activation eps must be positive with fp32(127/eps) finite; then
+      s is finite for every token, an all-zero token quantizes to x~ = 0
+      and y = 0.  eps = 0 (or a value whose 127/eps overflows) is refused.
 
 Floating point that decides an integer (codes and int8 activations) is done
 in fp32, the precision of the pages' listing (torch's default dtype).
@@ -189,7 +192,17 @@ def quant_act(x: np.ndarray, eps=EPS_DEFAULT):
 
     beta_m = max_j |x_mj| (fp32); s_m = fp32(127 / max(beta_m, eps));
     x~ = clamp(rint(fp32(x * s_m)), -128, 127).  Returns (x~ int8 [M, K],
-    s fp32 [M])."""
+    s fp32 [M]).
+
+    eps must be positive with fp32(127 / eps) finite (R8): the page's
+    listing only ever clamps beta at a positive eps, and with eps = 0 an
+    all-zero token would give s = 127/0 = inf and x * s = 0 * inf = NaN, a
+    result no rounding rule defines.  Other values raise ValueError."""
+    e32 = np.float32(eps)
+    with np.errstate(divide="ignore", over="ignore"):
+        smax = QB / e32 if e32 > 0 else np.float32(np.inf)
+    if not (np.isfinite(e32) and e32 > 0 and np.isfinite(smax)):
+        raise ValueError(f"activation eps must be > 0 with 127/eps finite in fp32, got {eps!r}")
     x = np.asarray(x, dtype=np.float32)
     if x.ndim != 2:
         raise ValueError("x must be [M, K]")
@@ -291,11 +304,12 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 # listing's RMSNorm and bias, which the pass excludes).
 # ---------------------------------------------------------------------------
 def forward(x: np.ndarray, w: np.ndarray, eps=EPS_DEFAULT, relu2: bool = False,
-            y_dtype: str = "f32", gamma=None):
-    """Returns a dict with every intermediate of the pass."""
+            y_dtype: str = "f32", gamma=None, act_eps=None):
+    """Returns a dict with every intermediate of the pass.  ``eps`` serves
+    both quantizers unless ``act_eps`` gives the activations their own."""
     g = absmean_gamma(w) if gamma is None else np.float32(gamma)
     codes = ternary_codes(w, g, eps)
-    xq, s = quant_act(x, eps)
+    xq, s = quant_act(x, eps if act_eps is None else act_eps)
     acc = contract(xq, codes)
     y64 = dequant(acc, g, s, relu2)
     return {"gamma": g, "codes": codes, "xq": xq, "s": s, "acc": acc,

@@ -77,6 +77,33 @@ def test_quant_act_rejects(bl):
     assert q(None, 0, 0, 8, 1e-5, None, None, None) == 0            # m == 0: no-op
 
 
+def test_activation_eps_boundary_matches_oracle(bl):
+    """The library refuses exactly the activation eps values the oracle
+    refuses (0, negatives, NaN/Inf, and those whose fp32 127/eps overflows),
+    in both entry points that quantize activations; weight packing still
+    takes eps = 0."""
+    import numpy as np
+    from test_oracle_pins import EPS_MIN
+    below = float(np.nextafter(EPS_MIN, np.float32(0)))
+    q = bl.lib.bitlinear_quant_act
+    arr = (bl.BLLinear * 1)()
+    arr[0] = bl.BLLinear(None, 0, None, None, 64, 256, 0, 0, None, None, None, None)
+    f = bl.lib.bitlinear_forward_fused
+    for e, ok in ((float(EPS_MIN), True), (1e-5, True), (below, False), (0.0, False),
+                  (1e-38, False), (-1e-5, False), (float("inf"), False)):
+        x = np.zeros((1, 4), np.float32)
+        try:
+            O.quant_act(x, e)
+            assert ok, e
+        except ValueError:
+            assert not ok, e
+        assert q(None, 0, 0, 8, e, None, None, None) == (0 if ok else 1), e
+        assert f(arr, 1, 0, e, None, 0, None) == (0 if ok else 1), e
+    ws = bl.lib.bitlinear_pack_workspace_bytes(64, 256)
+    assert bl.lib.bitlinear_pack_weights(FAKE, 0, 64, 256, 0.0, None, FAKE + 256, FAKE, None,
+                                         0, None) == 4      # eps = 0 passes; no workspace
+
+
 def test_pack_rejects(bl):
     p = bl.lib.bitlinear_pack_weights
     ws = bl.lib.bitlinear_pack_workspace_bytes(64, 256)

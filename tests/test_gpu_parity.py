@@ -64,6 +64,45 @@ def test_quant_act_worked_example(B):
     np.testing.assert_array_equal(host(s), np.array(g["s"], np.float32))
 
 
+@pytest.mark.parametrize("m", [1, 2, 5, 20])
+def test_zero_tokens_at_smallest_eps(B, m):
+    """All-zero tokens with the smallest activation eps the ABI accepts:
+    s = fp32(127 / eps) is the largest finite fp32 and x~ = 0, y = 0 exactly,
+    through bitlinear_quant_act + forward and through the fused step (dot4 at
+    1-2 tokens, the matrix cores from 3)."""
+    import torch
+    from test_oracle_pins import EPS_MIN
+    n, k = 192, 1000
+    w, x = random_case(4400 + m, m, n, k, x_kind="t3")
+    x[0] = 0.0
+    if m > 2:
+        x[m // 2] = 0.0
+    xd, xo = x_device(x, "bf16")
+    packed, gamma = B.pack_weights(dev(w))
+    g = host(gamma)[0]
+    r = O.forward(xo, w, gamma=g, act_eps=EPS_MIN, y_dtype="f32")
+    assert r["s"][0] == np.float32(3.4028235e38) and not r["xq"][0].any()
+    xq, s = B.quant_act(xd, eps=float(EPS_MIN))
+    np.testing.assert_array_equal(host(s), r["s"])
+    np.testing.assert_array_equal(host(xq)[:, :k], r["xq"])
+    y, acc = B.forward(xq, s, packed, gamma, n, k, acc_out=True)
+    np.testing.assert_array_equal(host(acc), r["acc"])
+    assert_y_close(host(y), r["y"], "f32", f"zero tokens m={m}")
+    assert not host(y)[0].any()
+    ops = [dict(x=xd, packed=packed, gamma=gamma, n=n, k=k,
+                y=torch.empty((m, n), dtype=torch.float32, device="cuda"),
+                acc_out=torch.empty((m, n), dtype=torch.int32, device="cuda"),
+                xq_out=torch.full((m, O.padded_k(k)), 99, dtype=torch.int8, device="cuda"),
+                scale_out=torch.empty(m, dtype=torch.float32, device="cuda"))]
+    B.forward_fused(ops, eps=float(EPS_MIN))
+    o = ops[0]
+    np.testing.assert_array_equal(host(o["scale_out"]), r["s"])
+    np.testing.assert_array_equal(host(o["xq_out"])[:, :k], r["xq"])
+    np.testing.assert_array_equal(host(o["acc_out"]), r["acc"])
+    assert_y_close(host(o["y"]), r["y"], "f32", f"fused zero tokens m={m}")
+    assert not host(o["y"])[0].any()
+
+
 def test_quant_act_unaligned_pointer(B):
     import torch
     _, x = random_case(5, 3, 1, 100)

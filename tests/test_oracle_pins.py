@@ -148,11 +148,47 @@ def test_activation_invariants():
     np.testing.assert_array_equal(O.quant_act(-x)[0], -xq)
 
 
+def smallest_act_eps():
+    """The smallest fp32 e with fp32(127 / e) finite, by bisection over the
+    positive fp32 bit patterns (their order is the order of the values)."""
+    lo, hi = 1, int(np.float32(1.0).view(np.uint32))      # 127/lo overflows, 127/hi does not
+    with np.errstate(over="ignore", divide="ignore"):
+        while hi - lo > 1:
+            mid = (lo + hi) // 2
+            e = np.uint32(mid).view(np.float32)
+            if np.isfinite(np.float32(127.0) / e):
+                hi = mid
+            else:
+                lo = mid
+    return np.uint32(hi).view(np.float32)
+
+
+EPS_MIN = smallest_act_eps()
+
+
+def test_activation_eps_rule():
+    # 127 / eps must be a finite fp32 (the listing clamps beta at a positive
+    # eps); eps = 0 would make an all-zero token 0 * inf = NaN
+    assert EPS_MIN == np.float32(3.7321948e-37)
+    x = np.zeros((2, 5), np.float32)
+    x[1, 2] = -0.75
+    below = np.nextafter(EPS_MIN, np.float32(0))
+    for bad in (0.0, -1e-5, below, float("nan"), float("inf"), 1e-38):
+        with pytest.raises(ValueError):
+            O.quant_act(x, bad)
+    xq, s = O.quant_act(x, EPS_MIN)
+    np.testing.assert_array_equal(xq, [[0] * 5, [0, 0, -127, 0, 0]])
+    assert s[0] == np.float32(3.4028235e38) and np.isfinite(s[0])     # 127 / EPS_MIN
+    assert s[1] == np.float32(127) / np.float32(0.75)
+    xq, s = O.quant_act(x, np.float32(1e-5))
+    assert s[0] == np.float32(12700000.0) and not xq[0].any()
+
+
 def test_activation_power_of_two_scaling():
     _, x = random_case(6, 5, 4, 300)
-    xq, s = O.quant_act(x, eps=0.0)
+    xq, s = O.quant_act(x, eps=EPS_MIN)
     for j in (-4, 6):
-        xq2, s2 = O.quant_act(x * np.float32(2.0 ** j), eps=0.0)
+        xq2, s2 = O.quant_act(x * np.float32(2.0 ** j), eps=EPS_MIN)
         np.testing.assert_array_equal(xq2, xq)
         np.testing.assert_array_equal(s2, s / np.float32(2.0 ** j))
 
@@ -231,8 +267,8 @@ def test_dequant_matches_page_form():
 
 def test_dequant_scaling_law():
     w, x = random_case(13, 3, 16, 256)
-    base = O.forward(x, w, eps=0.0)["y64"]
-    sc = O.forward(x * np.float32(4.0), w * np.float32(0.125), eps=0.0)["y64"]
+    base = O.forward(x, w, eps=0.0, act_eps=EPS_MIN)["y64"]
+    sc = O.forward(x * np.float32(4.0), w * np.float32(0.125), eps=0.0, act_eps=EPS_MIN)["y64"]
     np.testing.assert_array_equal(sc, base * 0.5)
 
 
