@@ -38,7 +38,9 @@ EXPORTS = [
     "bitlinear_status_string", "bitlinear_abi_version",
     "bitlinear_forward_fused_workspace_bytes", "bitlinear_forward_fused",
     "bitlinear_forward_multi_workspace_bytes", "bitlinear_forward_multi",
+    "bitlinear_forward_noalloc",
 ]
+BL_NOALLOC_SCRATCH_BYTES = 262144
 BL_MAX_FUSED = 16
 BL_FUSED_MAX_M = 64
 BL_MAX_MULTI = 16
@@ -89,6 +91,7 @@ def _load() -> ctypes.CDLL:
         "bitlinear_forward_fused": (i32, [vp, i32, i64, f32, vp, sz, vp]),
         "bitlinear_forward_multi_workspace_bytes": (sz, [vp, i32, i64, i64]),
         "bitlinear_forward_multi": (i32, [vp, vp, i64, i64, vp, i32, vp, sz, vp]),
+        "bitlinear_forward_noalloc": (i32, [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -220,6 +223,22 @@ def forward(xq, scale, packed, gamma, n: int, k: int, relu2: bool = False,
         BL_EPI_RELU2 if relu2 else BL_EPI_NONE, _dtype_code(y.dtype), _ptr(y), _ptr(acc),
         _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return (y, acc) if acc_out else y
+
+
+def forward_noalloc(xq, scale, packed, gamma, n: int, k: int, relu2: bool = False,
+                    out_dtype=None, y=None, acc_out=None, stream=None):
+    """bitlinear_forward_noalloc: bitlinear_forward without a workspace (the
+    library's per-device scratch holds the split-K slots).  y and acc_out may
+    be given as preallocated tensors; returns y."""
+    import torch
+    m = xq.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype or torch.float32, device=xq.device)
+    _check("bitlinear_forward_noalloc", lib.bitlinear_forward_noalloc(
+        _ptr(xq), _ptr(scale), _ptr(packed), _ptr(gamma), m, n, k,
+        BL_EPI_RELU2 if relu2 else BL_EPI_NONE, _dtype_code(y.dtype), _ptr(y), _ptr(acc_out),
+        _stream(stream)))
+    return y
 
 
 class FusedStep:

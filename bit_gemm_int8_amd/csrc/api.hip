@@ -2,6 +2,8 @@
 // The entry points and their contracts are declared in include/bitlinear.h.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/bitlinear.h"
 #include "bl_device.h"
 #include "bl_internal.h"
@@ -515,10 +517,12 @@ bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t 
   return BL_OK;
 }
 
-bl_status bitlinear_forward(const int8_t* xq, const float* scale, const void* packed,
-                            const float* gamma, int64_t m, int64_t n, int64_t k, int epilogue,
-                            int y_dtype, void* y, int32_t* acc_out, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+// Argument checks of bitlinear_forward and bitlinear_forward_noalloc, all
+// but the workspace; fills in the plan.
+static bl_status check_forward(const int8_t* xq, const float* scale, const void* packed,
+                               const float* gamma, int64_t m, int64_t n, int64_t k, int epilogue,
+                               int y_dtype, const void* y, const int32_t* acc_out,
+                               FwdPlan* plan) {
   if (!valid_dtype(y_dtype)) return BL_ERR_INVALID_ARG;
   if (epilogue != BL_EPI_NONE && epilogue != BL_EPI_RELU2) return BL_ERR_INVALID_ARG;
   if (m < 0 || n < 1 || k < 1) return BL_ERR_INVALID_ARG;
@@ -529,9 +533,20 @@ bl_status bitlinear_forward(const int8_t* xq, const float* scale, const void* pa
   if (!aligned(xq, 16) || !aligned(scale, 4) || !aligned(packed, 16) || !aligned(gamma, 4) ||
       !aligned(y, y_dtype == BL_BF16 ? 2 : 4) || (acc_out != nullptr && !aligned(acc_out, 4)))
     return BL_ERR_MISALIGNED;
-  const FwdPlan plan = forward_plan(m, n, k);
-  if (plan.kind == 1 && gemm_grid(plan.variant, m, &n, 1) > INT32_MAX)
+  *plan = forward_plan(m, n, k);
+  if (plan->kind == 1 && gemm_grid(plan->variant, m, &n, 1) > INT32_MAX)
     return BL_ERR_UNSUPPORTED_SHAPE;
+  return BL_OK;
+}
+
+bl_status bitlinear_forward(const int8_t* xq, const float* scale, const void* packed,
+                            const float* gamma, int64_t m, int64_t n, int64_t k, int epilogue,
+                            int y_dtype, void* y, int32_t* acc_out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  FwdPlan plan{};
+  const bl_status st = check_forward(xq, scale, packed, gamma, m, n, k, epilogue, y_dtype, y,
+                                     acc_out, &plan);
+  if (st != BL_OK || m == 0) return st;
   if (plan.ws_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return BL_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return BL_ERR_MISALIGNED;
@@ -543,3 +558,67 @@ bl_status bitlinear_forward(const int8_t* xq, const float* scale, const void* pa
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------------
+// bitlinear_forward_noalloc: bitlinear_forward whose split-K slots live in a
+// scratch array of this library's code object instead of a caller workspace.
+// Each device holds its own copy of the array for the life of the process.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address comes from hipGetSymbolAddress, once per device with that
+// device current, and only that address is handed to kernels.
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[BL_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};     // device address of `scratch`, per device
+bool g_scratch_clean[kMaxDevices] = {};    // cleared by a call outside stream capture
+
+// The current device's scratch address, looked up on the first call on the
+// device.  When the plan uses the scratch and no call outside stream capture
+// has cleared it yet, a fill kernel clears it on `stream` first (a kernel,
+// not hipMemsetAsync, so a captured graph replays it correctly); from then
+// on every completed call leaves the slots it used zero-filled.
+bl_status noalloc_scratch(bool needed, hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BL_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return BL_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  if (needed && !g_scratch_clean[dev]) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return BL_ERR_HIP;
+    if (launch_fill_zero(reinterpret_cast<uint32_t*>(g_scratch_ptr[dev]),
+                         BL_NOALLOC_SCRATCH_BYTES / 4, stream) != hipSuccess)
+      return BL_ERR_HIP;
+    if (cs == hipStreamCaptureStatusNone) g_scratch_clean[dev] = true;
+  }
+  *out = g_scratch_ptr[dev];
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" bl_status bitlinear_forward_noalloc(const int8_t* xq, const float* scale,
+                                               const void* packed, const float* gamma, int64_t m,
+                                               int64_t n, int64_t k, int epilogue, int y_dtype,
+                                               void* y, int32_t* acc_out, void* stream) {
+  FwdPlan plan{};
+  const bl_status st = check_forward(xq, scale, packed, gamma, m, n, k, epilogue, y_dtype, y,
+                                     acc_out, &plan);
+  if (st != BL_OK || m == 0) return st;
+  if (plan.ws_bytes > BL_NOALLOC_SCRATCH_BYTES) return BL_ERR_WORKSPACE;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  const bl_status sst = noalloc_scratch(plan.ws_bytes > 0, hs, &ws);
+  if (sst != BL_OK) return sst;
+  hipError_t e = launch_forward(plan, xq, scale, reinterpret_cast<const uint32_t*>(packed), gamma,
+                                m, n, k, epilogue == BL_EPI_RELU2, y_dtype == BL_BF16, y, acc_out,
+                                ws, hs);
+  return e == hipSuccess ? BL_OK : BL_ERR_HIP;
+}

@@ -245,6 +245,32 @@ size_t bitlinear_forward_fused_workspace_bytes(const bl_linear* ops, int nops, i
 bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, float eps,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * bitlinear_forward_noalloc -- bitlinear_forward for callers that cannot
+ * allocate device memory or own a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * checks, kernels and results as bitlinear_forward, without the workspace:
+ * the split-K slots live in a scratch array of BL_NOALLOC_SCRATCH_BYTES
+ * that the library's code object holds on each device until the process
+ * ends.  Nothing is allocated or freed.
+ *
+ *   - Products whose plan needs more than BL_NOALLOC_SCRATCH_BYTES of
+ *     split-K slots return BL_ERR_WORKSPACE before any launch (every split
+ *     plan of a matrix with fewer than 16384 rows fits).
+ *   - The first call on a device that needs the scratch, and every such call
+ *     made under stream capture until one outside capture has run, first
+ *     enqueues a small zero-fill kernel on `stream`; every completed call
+ *     leaves the scratch zero-filled again.
+ *   - All calls on one device share its scratch: calls that overlap in time
+ *     on one device (different streams without ordering) race and may return
+ *     wrong results.  Order them on one stream or with events.
+ * ---------------------------------------------------------------------- */
+#define BL_NOALLOC_SCRATCH_BYTES 262144
+bl_status bitlinear_forward_noalloc(const int8_t* xq, const float* scale, const void* packed,
+                                    const float* gamma, int64_t m, int64_t n, int64_t k,
+                                    int epilogue, int y_dtype, void* y, int32_t* acc_out,
+                                    void* stream);
+
 /* Zero-fill a forward workspace with a device kernel (no hipMemset, so it can
  * be captured in a HIP graph).  bytes must be a multiple of 4. */
 bl_status bitlinear_workspace_init(void* workspace, size_t bytes, void* stream);

@@ -152,6 +152,26 @@ def test_forward_rejects(bl):
     assert call(m=bl.BL_MAX_MN, n=bl.BL_MAX_MN, k=256) == 2
 
 
+def test_forward_noalloc_rejects(bl):
+    """The entry point without a workspace checks like bitlinear_forward and
+    refuses, before touching the device, a plan whose split-K slots exceed
+    its scratch."""
+    f = bl.lib.bitlinear_forward_noalloc
+
+    def call(xq=FAKE, s=FAKE, pk=FAKE, g=FAKE, m=4, n=64, k=256, epi=0, yd=0, y=FAKE, acc=None):
+        return f(xq, s, pk, g, m, n, k, epi, yd, y, acc, None)
+
+    assert call(n=0) == 1
+    assert call(epi=3) == 1
+    assert call(pk=None) == 1
+    assert call(k=bl.BL_MAX_K + 1) == 2
+    assert call(xq=FAKE + 4) == 3
+    assert call(m=0, xq=None, y=None) == 0
+    assert bl.forward_workspace_bytes(2, 16448, 65536) > bl.BL_NOALLOC_SCRATCH_BYTES
+    assert call(m=2, n=16448, k=65536) == 4
+    assert call(m=bl.BL_MAX_MN, n=bl.BL_MAX_MN, k=256) == 2
+
+
 def test_forward_multi_rejects(bl):
     f = bl.lib.bitlinear_forward_multi
 
