@@ -32,6 +32,8 @@ constexpr int64_t kMfmaGemvMaxM = 64;      // windowed MFMA GEMV up to here (4 t
 constexpr int64_t kGemvTargetGroups = 256;  // one token: about one workgroup per CU
 constexpr int64_t kGemvMaxLds = 48 * 1024;
 constexpr int64_t kCUs = 256;
+constexpr int64_t kStreamMinSubs = 64;      // stream GEMV from 1024 rows
+constexpr size_t kStreamMaxLds = 64 * 1024;
 
 }  // namespace
 
@@ -83,6 +85,21 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     }
     p.splits = (int)s;
     p.slots = s > 1 ? (size_t)(nb * m * 64) : 0;
+    // The streaming matrix-core GEMV for matrices of >= 1024 rows whose x~
+    // (every token, all of K) fits a workgroup's LDS: no K split, about one
+    // workgroup per CU.  Rows of at least 12 super-chunks at one token, 8 at
+    // two (shorter rows leave its waves too little to stream; measured on
+    // MI355X against the plans above, bit for bit).
+    const int64_t subs = nb * 4;
+    if (subs >= kStreamMinSubs && nc >= (m == 1 ? 12 : 8)) {
+      const int64_t grid = subs < kCUs ? subs : kCUs;
+      if (stream_lds_bytes((int)m, nc, (int)cdiv(subs, grid)) <= kStreamMaxLds) {
+        p.kind = 3;
+        p.qpl = (int)grid;
+        p.splits = 1;
+        p.slots = 0;
+      }
+    }
   } else if (m <= kMfmaGemvMaxM) {
     // Windowed MFMA GEMV: 16, 32 or 64 token columns.  Many row blocks
     // (>= 256): wide row groups, the whole K per wave; fewer: slices of K
@@ -142,6 +159,9 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
   if (plan.kind == 0)
     return launch_gemv((int)m, plan.variant, plan.pf, plan.qpl, xq, scale, packed, gamma, n, k,
                        plan.splits, relu2, bf16, y, acc_out, slots, stream);
+  if (plan.kind == 3)
+    return launch_gemv_stream((int)m, xq, scale, packed, gamma, n, k, plan.qpl, relu2, bf16, y,
+                              acc_out, stream);
   if (plan.kind == 2)
     return launch_gemv_mfma(plan.variant, xq, scale, packed, gamma, m, n, k, relu2, bf16, y,
                             acc_out, stream);
@@ -150,6 +170,10 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
 }
 
 struct FusedPlan {
+  bool stream = false;                  // 1..2 tokens: the streaming matrix-core kernel
+  int xr = 0;                           // its activation units per thread and token
+  int nsub_alloc = 0;                   // its sub-blocks per workgroup, at most
+  int64_t nc_max = 0;
   bool mfma = false;                    // 3..64 tokens: the fused MFMA kernel
   int variant = 0;                      // its wave layout
   int waves = 8;
@@ -160,6 +184,67 @@ struct FusedPlan {
   int splits[kMaxFused] = {};
   size_t slot_off[kMaxFused] = {};      // bytes
 };
+
+// The fused step on the streaming kernel: every entry's rows whole aligned
+// 16-byte units of one activation dtype, every entry's x~ within the LDS, the
+// activation rows within 8 units per thread and token, and some entry with
+// rows of at least 8 super-chunks.  Workgroups are
+// shared out in proportion to each entry's packed bytes, about one per CU in
+// all, each entry at least one and at most one per 16-row sub-block.
+static bool stream_fused_plan(const bl_linear* ops, int nops, int64_t m, FusedPlan* p) {
+  const int xdt = ops[0].x_dtype;
+  int64_t units = 0, nc_max = 0, nu_max = 0;
+  for (int i = 0; i < nops; ++i) {
+    const int64_t esize = ops[i].x_dtype == BL_BF16 ? 2 : 4;
+    if (ops[i].x_dtype != xdt || (ops[i].k * esize) % 16 != 0 || ((uintptr_t)ops[i].x % 16) != 0)
+      return false;
+    const int64_t nc = cdiv(ops[i].k, kSuperK);
+    units += cdiv(ops[i].n, kRowBlock) * 4 * nc;
+    if (nc > nc_max) nc_max = nc;
+    const int64_t nu = ops[i].k * esize / 16;
+    if (nu > nu_max) nu_max = nu;
+  }
+  if (nc_max < 8) return false;
+  int waves, depth;
+  stream_shape((int)m, nc_max, &waves, &depth);
+  const int64_t xr = cdiv(nu_max, 64 * waves);
+  if (m * xr > 8) return false;
+  // one workgroup per CU at most: a 16-wave workgroup fills a CU, so a
+  // workgroup past the 256th would wait for a whole round
+  int64_t gs[kMaxFused], total = 0;
+  for (int i = 0; i < nops; ++i) {
+    const int64_t subs = cdiv(ops[i].n, kRowBlock) * 4;
+    const int64_t w = subs * cdiv(ops[i].k, kSuperK);
+    int64_t gi = (kCUs * w + units / 2) / units;
+    gs[i] = gi < 1 ? 1 : gi > subs ? subs : gi;
+    total += gs[i];
+  }
+  while (total > kCUs) {
+    int big = 0;
+    for (int i = 1; i < nops; ++i) big = gs[i] > gs[big] ? i : big;
+    if (gs[big] <= 1) break;
+    --gs[big];
+    --total;
+  }
+  int groups = 0, nsub_alloc = 1;
+  for (int i = 0; i < nops; ++i) {
+    const int64_t subs = cdiv(ops[i].n, kRowBlock) * 4;
+    p->splits[i] = (int)gs[i];
+    groups += (int)gs[i];
+    const int spw = (int)cdiv(subs, gs[i]);
+    if (spw > nsub_alloc) nsub_alloc = spw;
+  }
+  const size_t lds = stream_lds_bytes((int)m, nc_max, nsub_alloc);
+  if (lds > kStreamMaxLds) return false;
+  p->stream = true;
+  p->xr = (int)xr;
+  p->nsub_alloc = nsub_alloc;
+  p->nc_max = nc_max;
+  p->groups = groups;
+  p->lds = lds;
+  p->ws_bytes = 0;
+  return true;
+}
 
 FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   // T = super-chunks a workgroup should stream: the set's total over ~512
@@ -176,6 +261,7 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   // ones by the number of groups, each of which reads and quantizes its x
   // range.  (Tuned on MI355X over the 2B- and 100B-class shapes.)
   FusedPlan p;
+  if (m <= 2 && stream_fused_plan(ops, nops, m, &p)) return p;
   if (m >= 3) {
     // Matrix cores: two 16-row groups x 4 K-slices per workgroup, or for
     // sets with >= 256 row blocks in an entry four 32-row groups with the
@@ -348,10 +434,18 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
     sg.flags = (o.epilogue == BL_EPI_RELU2 ? 1 : 0) | (o.y_dtype == BL_BF16 ? 2 : 0) |
                (o.x_dtype == BL_BF16 ? 4 : 0);
     args.wg_begin[i] = begin;
-    if (sg.splits > 1)
+    if (sg.splits > 1 && !plan.stream)
       sg.slots = reinterpret_cast<int64_t*>(reinterpret_cast<char*>(workspace) + plan.slot_off[i]);
-    begin += plan.mfma ? (int)cdiv(cdiv(o.n, kRowBlock) * 4, plan.variant == 0 ? 2 : 8)
-                       : (int)(cdiv(o.n, kRowBlock) * (4 / plan.qpl) * sg.splits);
+    begin += plan.stream ? sg.splits
+             : plan.mfma ? (int)cdiv(cdiv(o.n, kRowBlock) * 4, plan.variant == 0 ? 2 : 8)
+                         : (int)(cdiv(o.n, kRowBlock) * (4 / plan.qpl) * sg.splits);
+  }
+  if (plan.stream) {
+    args.nsub_alloc = plan.nsub_alloc;
+    const hipError_t e = launch_gemv_stream_fused(args, (int)m, plan.nc_max,
+                                                  ops[0].x_dtype == BL_BF16, plan.xr, begin,
+                                                  plan.lds, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BL_OK : BL_ERR_HIP;
   }
   if (plan.mfma) {
     bool all_bf16 = true, all_fast = true;

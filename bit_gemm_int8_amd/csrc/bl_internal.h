@@ -26,10 +26,11 @@ hipError_t launch_pack(const void* w, bool bf16, int64_t n, int64_t k, float eps
 
 // Forward: dispatch plan shared by the workspace query and the launch.
 struct FwdPlan {
-  int kind;            // 0 = dot4 GEMV, 1 = MFMA GEMM, 2 = MFMA GEMV
+  int kind;            // 0 = dot4 GEMV, 1 = MFMA GEMM, 2 = MFMA GEMV, 3 = stream GEMV
   int variant;         // dot4 GEMV: waves per workgroup; otherwise the kernel variant
   int pf;              // GEMV: super-chunks in flight per wave
-  int qpl;             // GEMV: 16-byte q-parts per lane (4: 64 rows per group, 1: 16 rows)
+  int qpl;             // GEMV: 16-byte q-parts per lane (4: 64 rows per group, 1: 16 rows);
+                       // stream GEMV: workgroups
   int splits;          // split-K factor
   size_t slots;        // 64-bit split-K slots in the workspace (splits > 1)
   size_t ws_bytes;     // total workspace bytes
@@ -84,6 +85,7 @@ struct FusedArgs {
   int wg_begin[kMaxFused];
   int nseg;
   float eps;
+  int nsub_alloc;         // stream kernel: 16-row sub-blocks per workgroup, at most
   FusedSeg seg[kMaxFused];
 };
 static_assert(kMaxFused * sizeof(int) == 64, "entry starts in one line");
@@ -96,6 +98,17 @@ hipError_t launch_gemv_mfma_fused(const FusedArgs& args, int m, int variant, boo
                                   bool all_fast, int groups, hipStream_t stream);
 hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, int qpl, bool long_rows,
                              int groups, size_t lds, hipStream_t stream);
+
+// Streaming one/two-token GEMV on the matrix cores (whole 16-row sub-blocks
+// per workgroup, x~ of every token in LDS).
+size_t stream_lds_bytes(int m, int64_t nc, int nsub_alloc);
+void stream_shape(int m, int64_t nc, int* waves, int* depth);
+hipError_t launch_gemv_stream(int m, const int8_t* xq, const float* scale,
+                              const uint32_t* packed, const float* gamma, int64_t n, int64_t k,
+                              int grid, bool relu2, bool bf16, void* y, int32_t* acc_out,
+                              hipStream_t stream);
+hipError_t launch_gemv_stream_fused(const FusedArgs& args, int m, int64_t nc_max, bool x_bf16,
+                                    int xr, int groups, size_t lds, hipStream_t stream);
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t padded_n(int64_t n) { return 64 * cdiv(n, 64); }

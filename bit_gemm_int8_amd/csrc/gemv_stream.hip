@@ -1,0 +1,491 @@
+// One- and two-token ternary GEMV on the int8 matrix cores, streaming whole
+// 16-row sub-blocks, with the fused dequant; and the same kernel with the
+// activation quantization in its prologue (the fused decode step).
+//
+// "BitNet b1.58 2B4T Guide: Scaling Native 1-Bit LLMs", section "Matrix
+// Multiplication as Pure Integer Addition": acc = x~ W~^T in an integer
+// accumulator, y = acc * gamma / s; section "8-Bit Activation Quantization:
+// absmax Scaling" for x~ and s.
+//
+// At one or two tokens the product reads every packed weight once, so the
+// kernel is bound by HBM.  What limits it on MI355X is keeping enough bytes
+// in flight per CU while the lanes unpack and multiply, so the work is laid
+// out for the memory system and the VALU load is kept low:
+//   - a workgroup (8 or 16 waves, about one per CU) owns whole 16-row
+//     sub-blocks of one product, all of K, so no K split crosses workgroups:
+//     no workspace and no atomics in memory;
+//   - the workgroup's 1 KiB units (sub-block t, super-chunk c) are taken in
+//     memory order and cut into one contiguous run per wave; each wave keeps
+//     D units (one 16-byte non-temporal load per lane each) in flight, issuing
+//     the load of unit v + D right after it consumes unit v;
+//   - lane (r, g) holds row r, inputs 64j + 16g .. + 15 of word j: exactly the
+//     first operand of v_mfma_i32_16x16x64_i8 after the shift-and-mask unpack,
+//     so one MFMA per packed word does what four v_dot4 did (the matrix core
+//     is idle otherwise; the VALU keeps only the unpack);
+//   - the second operand is x~ of token r for lanes r < M (from LDS) and zero
+//     for the other lanes, so result column r is token r: lanes r < M hold
+//     rows 4g .. 4g + 3 of their token;
+//   - a wave adds its sums into LDS (per sub-block, row and token) each time
+//     it leaves a sub-block; after one barrier the workgroup writes its rows.
+// x~ (all of K, every token) sits in LDS: the plain kernel copies it there
+// (loads issued before the weights), the fused kernel computes it there from
+// the activations (see gemv_stream_fused_kernel).
+#include <climits>
+
+#include "bl_device.h"
+#include "bl_internal.h"
+
+namespace bl {
+namespace {
+
+// Load cursor over a wave's units: unit v is sub-block tl, super-chunk cl;
+// it stops at the wave's last unit, so loads past the run repeat that unit
+// (no branch around the loads, which keeps them in flight).
+struct Cursor {
+  const uint4* base;      // the lane's record in super-chunk 0 of sub-block tl
+  int vl, tl, cl, ulast;
+};
+
+__device__ __forceinline__ const uint4* sub_base(const uint4* packed, int nc, int t, int g,
+                                                 int r) {
+  return packed + ((int64_t)(t >> 2) * nc * 4 + g) * 64 + (t & 3) * 16 + r;
+}
+
+__device__ __forceinline__ Cursor cursor_at(const uint4* packed, int nc, int t0, int u0, int u1,
+                                            int g, int r) {
+  Cursor c;
+  c.ulast = u1 > 0 ? u1 - 1 : 0;
+  c.vl = min(u0, c.ulast);
+  c.tl = t0 + c.vl / nc;
+  c.cl = c.vl - (c.vl / nc) * nc;
+  c.base = sub_base(packed, nc, c.tl, g, r);
+  return c;
+}
+
+__device__ __forceinline__ void cursor_next(Cursor& c, const uint4* packed, int nc, int g,
+                                            int r) {
+  if (c.vl < c.ulast) {
+    ++c.vl;
+    if (++c.cl == nc) {
+      c.cl = 0;
+      ++c.tl;
+      c.base = sub_base(packed, nc, c.tl, g, r);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void prefetch_units(uint4 (&buf)[D], Cursor& cur, const uint4* packed,
+                                               int nc, int g, int r) {
+  static_for<D>([&](auto P) {
+    buf[(int)P] = load_stream16(cur.base + (int64_t)cur.cl * kBlockU4);
+    cursor_next(cur, packed, nc, g, r);
+  });
+}
+
+// Stream units [u0, u1) of this workgroup (sub-blocks from t0, nc
+// super-chunks each; the first D already in buf) and add each sub-block's
+// sums into sums[sub - t0][token][row].  x~ of token m, super-chunk c,
+// inputs 64j + 16g .. +15 is LDS uint4 m * kp16 + 16c + 4j + g; zero_idx
+// holds 16 zero uint4.
+template <int M, int D>
+__device__ __forceinline__ void stream_units(uint4 (&buf)[D], Cursor& cur, const uint4* packed,
+                                             int nc, int t0, int u0, int u1, int g, int r,
+                                             const uint4* xs, int kp16, int zero_idx, int* sums) {
+  bl_v4i acc = {0, 0, 0, 0};
+  int tc = t0 + u0 / nc, cc = u0 - (u0 / nc) * nc;   // unit being consumed
+  auto flush = [&]() __attribute__((always_inline)) {
+    if (r < M) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) atomicAdd(&sums[((tc - t0) * M + r) * 16 + 4 * g + i], acc[i]);
+    }
+    acc = bl_v4i{0, 0, 0, 0};
+  };
+  auto consume = [&](const uint4& w) __attribute__((always_inline)) {
+    const int xa = r < M ? r * kp16 + cc * 16 + g : zero_idx + g;
+    const uint32_t wj[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 x4 = xs[xa + 4 * j];
+      const bl_v4i xv = {(int)x4.x, (int)x4.y, (int)x4.z, (int)x4.w};
+      const bl_v4i a = {(int)unpack_x64(wj[j], 0), (int)unpack_x64(wj[j], 1),
+                        (int)unpack_x64(wj[j], 2), (int)unpack_x64(wj[j], 3)};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xv, acc, 0, 0, 0);
+    }
+    if (++cc == nc) {
+      flush();
+      cc = 0;
+      ++tc;
+    }
+  };
+  int v = u0;
+  for (; v + D <= u1; v += D) {
+    static_for<D>([&](auto P) {
+      constexpr int p = decltype(P)::value;
+      consume(buf[p]);
+      buf[p] = load_stream16(cur.base + (int64_t)cur.cl * kBlockU4);
+      cursor_next(cur, packed, nc, g, r);
+    });
+  }
+  static_for<D>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    if (v + p < u1) consume(buf[p]);
+  });
+  if (u1 > u0 && cc != 0) flush();
+}
+
+// Rows t0*16 .. t1*16-1 of every token from the LDS sums (64 * acc, exact).
+template <int M>
+__device__ __forceinline__ void stream_epilogue(const int* sums, int t0, int nsub, int n,
+                                                const float (&fac)[M], bool relu2, bool ybf16,
+                                                void* y, int32_t* acc_out, int nt) {
+  const int rows = nsub * 16;
+  for (int i = threadIdx.x; i < rows * M; i += nt) {
+    const int m = i / rows, rr = i - m * rows;
+    const int row = t0 * 16 + rr;
+    if (row >= n) continue;
+    const int a = sums[((rr >> 4) * M + m) * 16 + (rr & 15)] >> 6;
+    if (acc_out != nullptr) acc_out[(int64_t)m * n + row] = a;
+    store_out(y, (int64_t)m * n + row, a, fac[m], relu2, ybf16);
+  }
+}
+
+// LDS of a workgroup: x~ [M][kp16] uint4, sums [nsub_alloc][M][16] int,
+// 16 zero uint4.
+__host__ __device__ constexpr int stream_zero_idx(int m, int kp16, int nsub_alloc) {
+  return m * kp16 + nsub_alloc * m * 4;
+}
+
+// ------------------------------------------------------------ plain GEMV --
+// x~ and s given.  Workgroup w owns sub-blocks [S w / G, S (w + 1) / G).
+template <int M, int WAVES, int D, int XR>
+__global__ __launch_bounds__(64 * WAVES) void gemv_stream_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ scale,
+    const uint4* __restrict__ packed, const float* __restrict__ gamma, int n, int nc, int S,
+    int G, int nsub_alloc, int relu2, int ybf16, void* __restrict__ y,
+    int32_t* __restrict__ acc_out) {
+  constexpr int NT = 64 * WAVES;
+  extern __shared__ uint4 lds[];
+  const int wg = blockIdx.x;
+  const int t0 = (int)((int64_t)S * wg / G), t1 = (int)((int64_t)S * (wg + 1) / G);
+  const int nsub = t1 - t0, units = nsub * nc;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int kp16 = nc * 16;
+  const int u0 = (int)((int64_t)units * wave / WAVES);
+  const int u1 = (int)((int64_t)units * (wave + 1) / WAVES);
+  int* sums = reinterpret_cast<int*>(lds + M * kp16);
+  const int zero_idx = stream_zero_idx(M, kp16, nsub_alloc);
+
+  // x~ first (loads retire in issue order, so staging it then waits for it
+  // alone), clamped so that no load sits behind a branch
+  const int xu = M * kp16;
+  const uint4* xg = reinterpret_cast<const uint4*>(xq);
+  uint4 xr[XR];
+#pragma unroll
+  for (int j = 0; j < XR; ++j) xr[j] = xg[min((int)threadIdx.x + NT * j, xu - 1)];
+  uint4 buf[D];
+  Cursor cur = cursor_at(packed, nc, t0, u0, u1, g, r);
+  prefetch_units<D>(buf, cur, packed, nc, g, r);
+  const float gm = *gamma;
+  float fac[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) fac[m] = scale[m];
+
+#pragma unroll
+  for (int j = 0; j < XR; ++j) {
+    const int i = (int)threadIdx.x + NT * j;
+    if (i < xu) lds[i] = xr[j];
+  }
+  for (int i = (int)threadIdx.x + NT * XR; i < xu; i += NT) lds[i] = xg[i];
+  for (int i = threadIdx.x; i < nsub * M * 16; i += NT) sums[i] = 0;
+  if (threadIdx.x < 16) lds[zero_idx + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+
+  stream_units<M, D>(buf, cur, packed, nc, t0, u0, u1, g, r, lds, kp16, zero_idx, sums);
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < M; ++m) fac[m] = gamma_over_s(gm, fac[m]);
+  stream_epilogue<M>(sums, t0, nsub, n, fac, relu2 != 0, ybf16 != 0, y, acc_out, NT);
+}
+
+// ----------------------------------------------------- fused decode step --
+// A table of products sharing the token count (the entries of FusedArgs;
+// `splits` of an entry holds its workgroup count here).  Each workgroup
+// quantizes its entry's whole activation rows into LDS before streaming:
+//   1. the activations are loaded first (XR 16-byte units per thread and
+//      token, clamped: the units past the row repeat the last one, which the
+//      max ignores), then the first D weight units;
+//   2. beta = max|x| per token (sign-cleared fp32 bits, DPP in the wave, LDS
+//      across waves) and s = fp32(127 / max(beta, eps)) exactly as
+//      bitlinear_quant_act computes it;
+//   3. x~ = clamp(rint(fp32(x * s))) of every held unit into LDS (the
+//      1.5 * 2^23 rounding of quant4_magic, checked against rintf), zero past
+//      K; every workgroup of an entry computes the same s and x~ bit for bit.
+// Rows must be whole 16-byte units at 16-byte alignment (checked on the host).
+template <bool BF16>
+__device__ __forceinline__ uint32_t unit_absmax_bits(const uint4& u) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  uint32_t mx = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (BF16) {
+      mx = max(mx, (w[e] << 16) & 0x7FFFFFFFu);
+      mx = max(mx, w[e] & 0x7FFF0000u);
+    } else {
+      mx = max(mx, w[e] & 0x7FFFFFFFu);
+    }
+  }
+  return mx;
+}
+
+__device__ __forceinline__ uint32_t quant4_of(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                              float s) {
+  uint32_t q[4] = {a, b, c, d};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float p = __fmul_rn(__uint_as_float(q[i]), s);     // one fp32 multiply
+    p = fminf(fmaxf(p, -128.0f), 127.0f);
+    q[i] = __float_as_uint(p + 12582912.0f);          // rint, half to even, in the low bits
+  }
+  const uint32_t lo = __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+template <int M, int WAVES, int D, int XR, bool BF16>
+__global__ __launch_bounds__(64 * WAVES) void gemv_stream_fused_kernel(
+    int nseg, int wb1, int wb2, int wb3, int wb4, int wb5, int wb6, int wb7, int wb8, int wb9,
+    int wb10, int wb11, int wb12, int wb13, FusedArgs args) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int EPU = BF16 ? 8 : 4;                  // activations per 16-byte unit
+  extern __shared__ uint4 lds[];
+  __shared__ uint32_t red[WAVES][M];
+  __shared__ float s_lds[M];
+  const int bid = (int)blockIdx.x;
+  const int wb[13] = {wb1, wb2, wb3, wb4, wb5, wb6, wb7, wb8, wb9, wb10, wb11, wb12, wb13};
+  int si = 0;
+#pragma unroll
+  for (int i = 0; i < 13; ++i) si = bid >= wb[i] ? i + 1 : si;
+  if (nseg > 14) {
+#pragma unroll
+    for (int i = 14; i < kMaxFused; ++i)
+      if (i < nseg && bid >= args.wg_begin[i]) si = i;
+  }
+  const FusedSeg& sg = args.seg[si];
+  const int local = bid - sg.wg_begin;
+  const int G = sg.splits;
+  const int nc = sg.nc, n = sg.n, k = sg.k;
+  const int S = ((n + kRowBlock - 1) / kRowBlock) * 4;
+  const int t0 = (int)((int64_t)S * local / G), t1 = (int)((int64_t)S * (local + 1) / G);
+  const int nsub = t1 - t0, units = nsub * nc;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int kp16 = nc * 16;
+  const int u0 = (int)((int64_t)units * wave / WAVES);
+  const int u1 = (int)((int64_t)units * (wave + 1) / WAVES);
+  const int nsub_alloc = args.nsub_alloc;
+  int* sums = reinterpret_cast<int*>(lds + M * kp16);
+  const int zero_idx = stream_zero_idx(M, kp16, nsub_alloc);
+  const uint4* packed = reinterpret_cast<const uint4*>(sg.packed);
+
+  // 1. activations, then weights
+  const int nu = k / EPU;                             // units per row (whole units)
+  uint4 xr[M][XR];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint4* row = reinterpret_cast<const uint4*>(sg.x) + (int64_t)m * nu;
+#pragma unroll
+    for (int j = 0; j < XR; ++j) xr[m][j] = row[min((int)threadIdx.x + NT * j, nu - 1)];
+  }
+  uint4 buf[D];
+  Cursor cur = cursor_at(packed, nc, t0, u0, u1, g, r);
+  prefetch_units<D>(buf, cur, packed, nc, g, r);
+  const float gm = *sg.gamma;
+
+  // 2. beta and s per token
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int j = 0; j < XR; ++j) mx = max(mx, unit_absmax_bits<BF16>(xr[m][j]));
+    mx = wave_max_u32(mx);
+    if (lane == 0) red[wave][m] = mx;
+  }
+  for (int i = threadIdx.x; i < nsub * M * 16; i += NT) sums[i] = 0;
+  if (threadIdx.x < 16) lds[zero_idx + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  float sv[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    uint32_t b = red[0][m];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) b = max(b, red[w][m]);
+    sv[m] = (float)(127.0 / (double)fmaxf(__uint_as_float(b), args.eps));
+  }
+
+  // 3. x~ into LDS (bytes EPU*u .. of token m), zero from K to K_pad
+  uint32_t* xw = reinterpret_cast<uint32_t*>(lds);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+#pragma unroll
+    for (int j = 0; j < XR; ++j) {
+      const int u = (int)threadIdx.x + NT * j;
+      if (u < nu) {
+        const uint4 x = xr[m][j];
+        if (BF16) {
+          const uint32_t d0 = quant4_of(x.x << 16, x.x & 0xFFFF0000u, x.y << 16,
+                                        x.y & 0xFFFF0000u, sv[m]);
+          const uint32_t d1 = quant4_of(x.z << 16, x.z & 0xFFFF0000u, x.w << 16,
+                                        x.w & 0xFFFF0000u, sv[m]);
+          reinterpret_cast<uint2*>(xw + m * kp16 * 4)[u] = make_uint2(d0, d1);
+        } else {
+          xw[m * kp16 * 4 + u] = quant4_of(x.x, x.y, x.z, x.w, sv[m]);
+        }
+      }
+    }
+    for (int d = k / 4 + (int)threadIdx.x; d < kp16 * 4; d += NT) xw[m * kp16 * 4 + d] = 0u;
+  }
+  __syncthreads();
+  if (local == 0) {                                   // optional copies of x~ and s
+    if (sg.xq_out != nullptr)
+      for (int m = 0; m < M; ++m)
+        for (int i = threadIdx.x; i < kp16; i += NT)
+          reinterpret_cast<uint4*>(sg.xq_out + (int64_t)m * kp16 * 16)[i] = lds[m * kp16 + i];
+    if (sg.scale_out != nullptr && threadIdx.x < M) sg.scale_out[threadIdx.x] = sv[threadIdx.x];
+  }
+
+  stream_units<M, D>(buf, cur, packed, nc, t0, u0, u1, g, r, lds, kp16, zero_idx, sums);
+  __syncthreads();
+  float fac[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) fac[m] = gamma_over_s(gm, sv[m]);
+  stream_epilogue<M>(sums, t0, nsub, n, fac, sg.relu2(), sg.y_bf16(), sg.y, sg.acc_out, NT);
+}
+
+template <int M, int WAVES, int D, int XR>
+void run_stream(const int8_t* xq, const float* scale, const uint32_t* packed,
+                const float* gamma, int n, int nc, int S, int G, int nsub_alloc, bool relu2,
+                bool bf16, void* y, int32_t* acc_out, size_t lds, hipStream_t stream) {
+  gemv_stream_kernel<M, WAVES, D, XR><<<G, 64 * WAVES, lds, stream>>>(
+      xq, scale, reinterpret_cast<const uint4*>(packed), gamma, n, nc, S, G, nsub_alloc,
+      relu2, bf16, y, acc_out);
+}
+
+template <int M, int WAVES, int D>
+void run_stream_xr(int xr, const int8_t* xq, const float* scale, const uint32_t* packed,
+                   const float* gamma, int n, int nc, int S, int G, int nsub_alloc, bool relu2,
+                   bool bf16, void* y, int32_t* acc_out, size_t lds, hipStream_t stream) {
+  if (xr <= 1)
+    run_stream<M, WAVES, D, 1>(xq, scale, packed, gamma, n, nc, S, G, nsub_alloc, relu2, bf16, y,
+                               acc_out, lds, stream);
+  else if (xr <= 2)
+    run_stream<M, WAVES, D, 2>(xq, scale, packed, gamma, n, nc, S, G, nsub_alloc, relu2, bf16, y,
+                               acc_out, lds, stream);
+  else if (xr <= 4)
+    run_stream<M, WAVES, D, 4>(xq, scale, packed, gamma, n, nc, S, G, nsub_alloc, relu2, bf16, y,
+                               acc_out, lds, stream);
+  else
+    run_stream<M, WAVES, D, 8>(xq, scale, packed, gamma, n, nc, S, G, nsub_alloc, relu2, bf16, y,
+                               acc_out, lds, stream);
+}
+
+template <int M, int WAVES, int D, int XR>
+void run_stream_fused(const FusedArgs& args, const int (&wb)[14], int groups, size_t lds,
+                      bool bf16, hipStream_t stream) {
+#define BL_SF(B)                                                                             \
+  gemv_stream_fused_kernel<M, WAVES, D, XR, B><<<groups, 64 * WAVES, lds, stream>>>(         \
+      args.nseg, wb[1], wb[2], wb[3], wb[4], wb[5], wb[6], wb[7], wb[8], wb[9], wb[10],      \
+      wb[11], wb[12], wb[13], args)
+  if (bf16)
+    BL_SF(true);
+  else
+    BL_SF(false);
+#undef BL_SF
+}
+
+template <int M, int WAVES, int D>
+void run_stream_fused_xr(int xr, const FusedArgs& args, const int (&wb)[14], int groups,
+                         size_t lds, bool bf16, hipStream_t stream) {
+  // the plan keeps M * xr <= 8 (the activation registers)
+  if (xr <= 2) {
+    run_stream_fused<M, WAVES, D, 2>(args, wb, groups, lds, bf16, stream);
+  } else if constexpr (M > 1) {
+    run_stream_fused<M, WAVES, D, 4>(args, wb, groups, lds, bf16, stream);
+  } else {
+    if (xr <= 4)
+      run_stream_fused<M, WAVES, D, 4>(args, wb, groups, lds, bf16, stream);
+    else
+      run_stream_fused<M, WAVES, D, 8>(args, wb, groups, lds, bf16, stream);
+  }
+}
+
+}  // namespace
+
+size_t stream_lds_bytes(int m, int64_t nc, int nsub_alloc) {
+  return (size_t)stream_zero_idx(m, (int)(nc * 16), nsub_alloc) * 16 + 16 * 16;
+}
+
+// Waves per workgroup and units in flight per wave: 8 x 4 at one token on
+// rows of fewer than 64 super-chunks, else 16 x 3.  (Swept on MI355X over
+// the 100B-class shapes at one and two tokens: 8 x 4, 16 x 2/3/4, 8 x 6.)
+void stream_shape(int m, int64_t nc, int* waves, int* depth) {
+  if (m == 1 && nc < 64) {
+    *waves = 8;
+    *depth = 4;
+  } else {
+    *waves = 16;
+    *depth = 3;
+  }
+}
+
+hipError_t launch_gemv_stream(int m, const int8_t* xq, const float* scale,
+                              const uint32_t* packed, const float* gamma, int64_t n, int64_t k,
+                              int grid, bool relu2, bool bf16, void* y, int32_t* acc_out,
+                              hipStream_t stream) {
+  const int nc = (int)cdiv(k, kSuperK);
+  const int S = (int)(cdiv(n, kRowBlock) * 4);
+  const int G = grid < S ? grid : S;
+  const int nsub_alloc = (int)cdiv(S, G);
+  const size_t lds = stream_lds_bytes(m, nc, nsub_alloc);
+  int waves, depth;
+  stream_shape(m, nc, &waves, &depth);
+  const int xr = (int)cdiv((int64_t)m * nc * 16, 64 * waves);
+  if (m == 1) {
+    if (waves == 8)
+      run_stream_xr<1, 8, 4>(xr, xq, scale, packed, gamma, (int)n, nc, S, G, nsub_alloc, relu2,
+                             bf16, y, acc_out, lds, stream);
+    else
+      run_stream_xr<1, 16, 3>(xr, xq, scale, packed, gamma, (int)n, nc, S, G, nsub_alloc, relu2,
+                              bf16, y, acc_out, lds, stream);
+  } else if (m == 2) {
+    run_stream_xr<2, 16, 3>(xr, xq, scale, packed, gamma, (int)n, nc, S, G, nsub_alloc, relu2,
+                            bf16, y, acc_out, lds, stream);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_stream_fused(const FusedArgs& args, int m, int64_t nc_max, bool x_bf16,
+                                    int xr, int groups, size_t lds, hipStream_t stream) {
+  int wb[14];
+  for (int i = 1; i < 14; ++i) wb[i] = i < args.nseg ? args.wg_begin[i] : INT_MAX;
+  int waves, depth;
+  stream_shape(m, nc_max, &waves, &depth);
+  if (m == 1) {
+    if (waves == 8)
+      run_stream_fused_xr<1, 8, 4>(xr, args, wb, groups, lds, x_bf16, stream);
+    else
+      run_stream_fused_xr<1, 16, 3>(xr, args, wb, groups, lds, x_bf16, stream);
+  } else if (m == 2) {
+    run_stream_fused_xr<2, 16, 3>(xr, args, wb, groups, lds, x_bf16, stream);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bl

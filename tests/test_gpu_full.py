@@ -196,15 +196,23 @@ def test_c3_stack_launches(B, c3, m):
 
 
 # ------------------------------------------------- fused plan, large sets --
-@pytest.mark.parametrize("m", [1, 2])
-@pytest.mark.parametrize("shapes", [[(4096, 32768, False), (8192, 4096, True)],
-                                    [(16384, 8192, True)]])
-def test_fused_large_sets_vs_oracle(B, m, shapes):
-    """Sets of >= 2^27 weights take the fused plan's large-set rules: at one
-    token up to 8 splits and 4 waves, at two tokens at most 2 splits and 8
-    waves when an entry splits (the first set splits its 32768-input entry,
-    the second splits nothing).  Every x~, s, acc and y against the oracle,
-    and the workspace is left zero-filled."""
+# (tokens, entries (n, k, relu2), whether the plan splits K over workgroups)
+LARGE_SETS = [
+    # the streaming matrix-core kernel (x~ of every token within the LDS)
+    (1, [(4096, 32768, False), (8192, 4096, True)], False),
+    (1, [(16384, 8192, True)], False),
+    (2, [(16384, 8192, True)], False),
+    # rows too long for it: the dot4 kernel's large-set rules (at one token
+    # up to 8 splits and 4 waves, at two at most 2 splits and 8 waves)
+    (1, [(2048, 65536, False), (8192, 4096, True)], True),
+    (2, [(4096, 32768, False), (8192, 4096, True)], True),
+]
+
+
+@pytest.mark.parametrize("m,shapes,splits", LARGE_SETS)
+def test_fused_large_sets_vs_oracle(B, m, shapes, splits):
+    """Sets of >= 2^27 weights in one fused launch: every x~, s, acc and y
+    against the oracle, and a split plan leaves its workspace zero-filled."""
     import torch
     mats, xs = [], {}
     for i, (n, k, relu2) in enumerate(shapes):
@@ -227,7 +235,7 @@ def test_fused_large_sets_vs_oracle(B, m, shapes):
                 xq_out=torch.full((m, O.padded_k(p.k)), 99, dtype=torch.int8, device="cuda"),
                 scale_out=torch.empty(m, dtype=torch.float32, device="cuda")) for p in mats]
     step = B.FusedStep(ops, workspace=B.Workspace())
-    assert (step.nbytes > 0) == (len(shapes) == 2)     # only the first set splits an entry
+    assert (step.nbytes > 0) == splits
     log(f"fused large set m={m} {shapes}")
     step()
     for p, o in zip(mats, ops):

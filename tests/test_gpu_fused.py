@@ -72,6 +72,12 @@ FUSED_CASES = [
     (1, [(100, 20000, True, "bf16", "bf16")]),                                     # long row, split K, 16-row groups
     (1, [(2560, 2560, False, "bf16", "bf16"), (6912, 2560, True, "bf16", "bf16"),
          (2560, 6912, False, "bf16", "bf16")]),                                     # 64-row groups
+    # the streaming matrix-core kernel: fp32 activations, ragged N, entries of
+    # one workgroup, two tokens
+    (1, [(1000, 4096, False, "f32", "f32"), (70, 2048, True, "bf16", "f32")]),
+    (2, [(2000, 3000, True, "bf16", "f32"), (1040, 8192, False, "f32", "f32")]),
+    (2, [(8192, 8192, False, "bf16", "bf16"), (1024, 8192, False, "bf16", "bf16"),
+         (1024, 8192, False, "bf16", "bf16")]),
     # 3 to 16 tokens: int8 matrix cores
     (8, [(2560, 2560, False, "bf16", "bf16"), (640, 2560, False, "bf16", "bf16"),
          (6912, 2560, True, "bf16", "bf16")]),                                        # all bf16

@@ -202,6 +202,13 @@ FWD_CASES = [
     (2, 16448, 4100, True, "bf16", "bf16"),      # >= 256 row blocks: 64-row groups, 4 waves, ragged K
     (40, 1000, 3000, True, "f32", "bf16"),       # 33-64 tokens, <= 64 row blocks: 32-token blocks, the 2nd partial
     (64, 4160, 6400, False, "bf16", "f32"),      # 64 tokens, 65 row blocks, long rows: 64-token blocks, 4 slices
+    # streaming matrix-core GEMV (1-2 tokens, >= 1024 rows, x~ within the LDS)
+    (1, 1024, 3072, False, "bf16", "bf16"),      # 64 sub-blocks, one per workgroup
+    (1, 5000, 12345, True, "f32", "bf16"),       # ragged N and K
+    (2, 1030, 2056, False, "bf16", "f32"),       # ragged, 9 super-chunks at two tokens
+    (1, 16448, 4100, True, "bf16", "bf16"),      # 1028 sub-blocks over 256 workgroups
+    (2, 1088, 32000, False, "f32", "bf16"),      # x~ of two tokens fills the LDS
+    (1, 3000, 28672, False, "bf16", "bf16"),     # 16 waves x 3 units in flight
     # windowed MFMA GEMV, 3 to 16 tokens: 2 row groups x 4 slices
     (3, 130, 520, True, "f32", "f32"),           # 3 super-chunks: an empty slice
     (4, 300, 1000, False, "f32", "bf16"),
@@ -310,13 +317,14 @@ def test_forward_extreme_accumulator(B):
 
 def test_forward_deterministic_and_workspace_clean(B):
     import torch
-    # long rows (64 super-chunks): the dot4 GEMV splits K over workgroups
-    w, x = random_case(9, 2, 2560, 16384)
+    # rows too long for the streaming kernel's LDS (157 super-chunks at two
+    # tokens): the dot4 GEMV splits K over workgroups
+    w, x = random_case(9, 2, 2560, 40000)
     packed, gamma = B.pack_weights(dev(w))
     xq, s = B.quant_act(dev(x))
     ws = B.Workspace()
-    outs = [host(B.forward(xq, s, packed, gamma, 2560, 16384, workspace=ws)) for _ in range(3)]
-    assert B.forward_workspace_bytes(2, 2560, 16384) > 0
+    outs = [host(B.forward(xq, s, packed, gamma, 2560, 40000, workspace=ws)) for _ in range(3)]
+    assert B.forward_workspace_bytes(2, 2560, 40000) > 0
     np.testing.assert_array_equal(outs[0], outs[1])
     np.testing.assert_array_equal(outs[0], outs[2])
     torch.cuda.synchronize()
