@@ -281,10 +281,10 @@ def run_headline(B, torch, W, args):
     achieved = b_f / (t_f * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
-            "kernel": "gemv_fused_kernel at one token on the 100B-class up (28672x8192, ReLU^2) "
-                      "and down (8192x28672) products: activation quant + GEMV + dequant",
+            "kernel": "gemv_stream_fused_kernel at one token on the 100B-class up (28672x8192, "
+                      "ReLU^2) and down (8192x28672) products: activation quant + GEMV + dequant",
             "bytes_per_launch_pair": b_f, "us_per_launch_pair": round(t_f, 3), "legs": legs}
-    plain = {"kernel": "gemv_kernel (bitlinear_forward, x~ given) on the same two products",
+    plain = {"kernel": "gemv_stream_kernel (bitlinear_forward, x~ given) on the same two products",
              "achieved": round(b_p / (t_p * 1e-6) / 1e9, 1), "unit": "GB/s",
              "frac": round(b_p / (t_p * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
              "bytes_per_launch_pair": b_p, "us_per_launch_pair": round(t_p, 3)}
@@ -544,7 +544,8 @@ def environment(torch):
 
 
 # ---------------------------------------------------------- profiling aids --
-KERNEL_SOURCES = ["bit_gemm_int8_amd/csrc/gemv.hip", "bit_gemm_int8_amd/csrc/bl_device.h"]
+KERNEL_SOURCES = ["bit_gemm_int8_amd/csrc/gemv_stream.hip", "bit_gemm_int8_amd/csrc/bl_device.h",
+                  "bit_gemm_int8_amd/csrc/bl_internal.h"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_fused_c5_updown_traffic.md")
 COPY_BYTES = 256 << 20
 
@@ -677,7 +678,7 @@ def summarize(directory, command, name):
         kib = COPY_BYTES / 1024
         ff = kib / copy_f if copy_f else None
         fw = kib / copy_w if copy_w else None
-        kernels = sorted({k for (k, c) in vals if "gemv_fused_kernel" in k})
+        kernels = sorted({k for (k, c) in vals if "gemv_stream_fused_kernel" in k})
         lines = ["# HBM traffic of the fused one-token GEMV on the 100B-class up and down "
                  "products (rocprofv3 --pmc)", "",
                  f"Commands: `{command}` (one run with FETCH_SIZE, one with WRITE_SIZE)", "",
