@@ -7,4 +7,5 @@ from .bitlinear_oracle import (absmean_gamma, ternary_codes, pack_ternary,  # no
                                unpack_ternary, packed_word_index, quant_act,
                                contract, contract_addsub, dequant, round_output,
                                f32_to_bf16_bits, bf16_bits_to_f32, forward,
-                               padded_k, padded_n, packed_bytes, EPS_DEFAULT)
+                               padded_k, padded_n, packed_bytes, EPS_DEFAULT,
+                               rmsnorm, mean_square, NORM_EPS_DEFAULT)

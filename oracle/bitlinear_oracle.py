@@ -42,6 +42,13 @@ reason, in the design notes of the repository):
   R8  the activation eps must be positive with fp32(127/eps) finite; then
       s is finite for every token, an all-zero token quantizes to x~ = 0
       and y = 0.  eps = 0 (or a value whose 127/eps overflows) is refused.
+  R9  the RMSNorm ahead of the activation quant (the listing's
+      nn.RMSNorm(in_features), with torch's defaults: eps = fp32 machine
+      epsilon 2^-23, a weight vector initialised to ones, out =
+      x * rsqrt(mean(x^2) + eps) * weight): mean(x^2) is the exact sum of the
+      squares (fp64, correctly rounded) over K, rounded to fp32; r =
+      fp32(1 / sqrt(fp32(ms + eps))) evaluated in fp64; y = fp32(fp32(x * r)
+      * w).  The norm eps must be positive and finite.
 
 Floating point that decides an integer (codes and int8 activations) is done
 in fp32, the precision of the pages' listing (torch's default dtype).
@@ -218,6 +225,49 @@ def quant_act(x: np.ndarray, eps=EPS_DEFAULT):
 
 
 # ---------------------------------------------------------------------------
+# RMSNorm ahead of the activation quant [P1 listing, BitLinear.forward step 1:
+# self.rms_norm = nn.RMSNorm(in_features) applied to x; P2 "Under the Hood":
+# subln normalization; P3 "Mathematical Foundations": the five-step flow
+# begins by normalizing the input activations] (R9).
+# ---------------------------------------------------------------------------
+NORM_EPS_DEFAULT = np.float32(2.0 ** -23)      # fp32 machine epsilon
+
+
+def mean_square(x_row) -> np.float32:
+    """fp32(fp64(sum of x_j^2) / K): the squares of fp32 values are exact in
+    fp64 and math.fsum returns their exact sum correctly rounded to fp64."""
+    import math
+    r = np.asarray(x_row, dtype=np.float32).astype(np.float64)
+    s = math.fsum((r * r).tolist())
+    return np.float32(s / np.float64(r.size))
+
+
+def rmsnorm(x: np.ndarray, weight=None, eps=NORM_EPS_DEFAULT, ms=None) -> np.ndarray:
+    """y = x * r * w per token with r = 1/sqrt(mean(x^2) + eps) (R9).
+
+    Returns fp32 [M, K].  ``weight`` is the fp32 [K] gain (None: ones, the
+    listing's initial value).  ``ms`` may give the per-token fp32 mean
+    squares (for a caller that checks a neighbouring rounding); by default
+    they come from mean_square."""
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim != 2:
+        raise ValueError("x must be [M, K]")
+    e = np.float32(eps)
+    if not (np.isfinite(e) and e > 0):
+        raise ValueError(f"norm eps must be positive and finite, got {eps!r}")
+    m, k = x.shape
+    w = np.ones(k, np.float32) if weight is None else np.asarray(weight, dtype=np.float32)
+    if w.shape != (k,):
+        raise ValueError("weight must be [K]")
+    ms = np.array([mean_square(x[i]) for i in range(m)], np.float32) if ms is None \
+        else np.asarray(ms, np.float32)
+    v = (ms + e).astype(np.float32)                               # fp32 add
+    r = (1.0 / np.sqrt(v.astype(np.float64))).astype(np.float32)  # fp64, rounded once
+    xr = (x * r[:, None]).astype(np.float32)                      # fp32 multiply
+    return (xr * w[None, :]).astype(np.float32)                   # fp32 multiply
+
+
+# ---------------------------------------------------------------------------
 # Step 4: integer contraction  [P1 "Matrix Multiplication as Pure Integer
 # Addition"]:  acc[i, k] = sum_j x~[i, j] * W~[k, j]
 # ---------------------------------------------------------------------------
@@ -304,12 +354,15 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 # listing's RMSNorm and bias, which the pass excludes).
 # ---------------------------------------------------------------------------
 def forward(x: np.ndarray, w: np.ndarray, eps=EPS_DEFAULT, relu2: bool = False,
-            y_dtype: str = "f32", gamma=None, act_eps=None):
+            y_dtype: str = "f32", gamma=None, act_eps=None, norm=False, norm_weight=None,
+            norm_eps=NORM_EPS_DEFAULT, norm_ms=None):
     """Returns a dict with every intermediate of the pass.  ``eps`` serves
-    both quantizers unless ``act_eps`` gives the activations their own."""
+    both quantizers unless ``act_eps`` gives the activations their own; with
+    ``norm`` the activations go through rmsnorm first (the listing's order)."""
     g = absmean_gamma(w) if gamma is None else np.float32(gamma)
     codes = ternary_codes(w, g, eps)
-    xq, s = quant_act(x, eps if act_eps is None else act_eps)
+    xn = rmsnorm(x, norm_weight, norm_eps, norm_ms) if norm else x
+    xq, s = quant_act(xn, eps if act_eps is None else act_eps)
     acc = contract(xq, codes)
     y64 = dequant(acc, g, s, relu2)
     return {"gamma": g, "codes": codes, "xq": xq, "s": s, "acc": acc,

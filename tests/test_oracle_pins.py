@@ -338,3 +338,116 @@ def test_pack_roundtrip(shape):
 def test_pack_rejects_non_ternary():
     with pytest.raises(ValueError):
         O.pack_ternary(np.array([[2]], np.int8))
+
+
+# ----------------------------------------------------------------- RMSNorm --
+def _f32_nearest(fr):
+    """The fp32 nearest to the rational fr, ties to even, by exact comparison
+    with the midpoints of the fp32 neighbours (no float rounding involved)."""
+    from fractions import Fraction
+    c = np.float32(float(fr))
+    lo = c if Fraction(float(c)) <= fr else np.nextafter(c, np.float32(-np.inf))
+    hi = np.nextafter(lo, np.float32(np.inf))
+    mid = (Fraction(float(lo)) + Fraction(float(hi))) / 2
+    if fr < mid:
+        return lo
+    if fr > mid:
+        return hi
+    return lo if (int(np.asarray(lo).view(np.uint32)) & 1) == 0 else hi
+
+
+def test_rmsnorm_worked_example():
+    # x = [3, 4]: mean of squares 12.5; with eps = 2^-23 (below half an ulp
+    # of 12.5) v = 12.5, r = 1/sqrt(12.5) = sqrt(2)/5, y = (3 r, 4 r) * w
+    from decimal import Decimal, getcontext
+    from fractions import Fraction
+    getcontext().prec = 60
+    r_exact = Fraction(Decimal(2).sqrt() / Decimal(5))
+    r32 = _f32_nearest(r_exact)
+    x = f32([[3.0, 4.0]])
+    w = f32([2.0, 0.5])
+    y = O.rmsnorm(x, w)
+    assert O.mean_square(x[0]) == np.float32(12.5)
+    exp = [_f32_nearest(Fraction(float(_f32_nearest(3 * Fraction(float(r32))))) * 2),
+           _f32_nearest(Fraction(float(_f32_nearest(4 * Fraction(float(r32))))) / 2)]
+    np.testing.assert_array_equal(y[0], f32(exp))
+
+
+def test_rmsnorm_mean_square_is_exact():
+    # squares spanning 120 binades: the correctly rounded sum, then / K
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    for k in (1, 7, 1000):
+        row = (rng.standard_normal(k) * 2.0 ** rng.integers(-60, 60, k)).astype(np.float32)
+        exact = sum(Fraction(float(v)) ** 2 for v in row)
+        assert O.mean_square(row) == np.float32(float(exact) / k)
+
+
+def test_rmsnorm_against_torch():
+    # torch's nn.RMSNorm (CPU, fp32) computes the same formula with its own
+    # reduction order and rsqrt: agreement to a few ulp pins the formula
+    # (mean rather than sum, eps inside the root, the gain, no bias)
+    import torch
+    _, x = random_case(31, 6, 1, 3000, x_kind="t3")
+    x[2] *= 1e-3
+    x[3, :17] *= 100.0
+    w = (np.random.default_rng(3).standard_normal(3000) * 0.3 + 1.0).astype(np.float32)
+    for eps in (2.0 ** -23, 1e-5, 1e-2):
+        norm = torch.nn.RMSNorm(3000, eps=eps)
+        with torch.no_grad():
+            norm.weight.copy_(torch.from_numpy(w))
+            yt = norm(torch.from_numpy(x)).numpy()
+        yo = O.rmsnorm(x, w, np.float32(eps))
+        np.testing.assert_allclose(yo, yt, rtol=4e-6, atol=0)
+
+
+def test_rmsnorm_closed_forms():
+    k = 64
+    # zero row -> 0; constant row c -> sign(c) * w; one nonzero x_j -> sqrt(K) sign(x_j) w_j
+    w = (np.arange(k, dtype=np.float32) / 16 + 0.5).astype(np.float32)
+    x = np.zeros((4, k), np.float32)
+    x[1] = 3.0
+    x[2] = -0.125
+    x[3, 9] = -7.0
+    y = O.rmsnorm(x, w, np.float32(1e-30))
+    assert not y[0].any()
+    np.testing.assert_allclose(y[1], w, rtol=2.5e-7)
+    np.testing.assert_allclose(y[2], -w, rtol=2.5e-7)
+    assert not np.delete(y[3], 9).any()
+    np.testing.assert_allclose(y[3, 9], -8.0 * w[9], rtol=2.5e-7)   # sqrt(64) = 8
+    # K = 1: x / |x|
+    np.testing.assert_array_equal(O.rmsnorm(f32([[-5.0], [0.25]]), None, np.float32(1e-30)),
+                                  f32([[-1.0], [1.0]]))
+
+
+def test_rmsnorm_power_of_two_scaling():
+    # eps far below the mean square: scaling x by 2^j leaves y unchanged bit for bit
+    _, x = random_case(32, 5, 1, 700, x_kind="t3")
+    w = np.linspace(0.5, 2.0, 700, dtype=np.float32)
+    y = O.rmsnorm(x, w, np.float32(1e-30))
+    for j in (-6, 9):
+        np.testing.assert_array_equal(O.rmsnorm(x * np.float32(2.0 ** j), w, np.float32(1e-30)), y)
+
+
+def test_rmsnorm_then_quant():
+    # every nonzero token reaches |x~| = 127 at the largest |y|; the listing's
+    # order (norm, then quant) inside forward
+    _, x = random_case(33, 4, 1, 500, x_kind="t3")
+    x[1] = 0.0
+    w = np.linspace(0.1, 3.0, 500, dtype=np.float32)
+    yn = O.rmsnorm(x, w)
+    xq, s = O.quant_act(yn)
+    for m in (0, 2, 3):
+        assert np.abs(xq[m]).max() == 127
+        assert int(np.argmax(np.abs(yn[m]))) in np.flatnonzero(np.abs(xq[m]) == 127)
+    assert not xq[1].any()
+    wt, _ = random_case(34, 1, 8, 500)
+    r = O.forward(x, wt, norm=True, norm_weight=w)
+    np.testing.assert_array_equal(r["xq"], xq)
+    np.testing.assert_array_equal(r["s"], s)
+
+
+def test_rmsnorm_rejects_bad_eps():
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        with pytest.raises(ValueError):
+            O.rmsnorm(np.ones((1, 4), np.float32), None, bad)
