@@ -38,8 +38,9 @@ EXPORTS = [
     "bitlinear_status_string", "bitlinear_abi_version",
     "bitlinear_forward_fused_workspace_bytes", "bitlinear_forward_fused",
     "bitlinear_forward_multi_workspace_bytes", "bitlinear_forward_multi",
-    "bitlinear_forward_noalloc",
+    "bitlinear_forward_noalloc", "bitlinear_rmsnorm_quant_act",
 ]
+NORM_EPS_DEFAULT = 2.0 ** -23       # fp32 machine epsilon, nn.RMSNorm's default
 BL_NOALLOC_SCRATCH_BYTES = 262144
 BL_MAX_FUSED = 16
 BL_FUSED_MAX_M = 64
@@ -52,7 +53,8 @@ class BLLinear(ctypes.Structure):
                 ("gamma", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
                 ("epilogue", ctypes.c_int), ("y_dtype", ctypes.c_int), ("y", ctypes.c_void_p),
                 ("acc_out", ctypes.c_void_p), ("xq_out", ctypes.c_void_p),
-                ("scale_out", ctypes.c_void_p)]
+                ("scale_out", ctypes.c_void_p), ("rmsnorm", ctypes.c_int),
+                ("norm_eps", ctypes.c_float), ("norm_weight", ctypes.c_void_p)]
 
 
 class BLProduct(ctypes.Structure):
@@ -92,6 +94,7 @@ def _load() -> ctypes.CDLL:
         "bitlinear_forward_multi_workspace_bytes": (sz, [vp, i32, i64, i64]),
         "bitlinear_forward_multi": (i32, [vp, vp, i64, i64, vp, i32, vp, sz, vp]),
         "bitlinear_forward_noalloc": (i32, [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]),
+        "bitlinear_rmsnorm_quant_act": (i32, [vp, i32, i64, i64, vp, f32, f32, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -206,6 +209,24 @@ def quant_act(x, eps: float = EPS_DEFAULT, stream=None) -> Tuple:
     return xq, scale
 
 
+def rmsnorm_quant_act(x, weight=None, norm_eps: float = NORM_EPS_DEFAULT,
+                      eps: float = EPS_DEFAULT, stream=None) -> Tuple:
+    """bitlinear_rmsnorm_quant_act: RMSNorm of x [M, K] (gain `weight` fp32
+    [K], or ones) then absmax int8 -> (xq int8 [M, K_pad], scale fp32 [M])."""
+    import torch
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M, K] tensor")
+    m, k = x.shape
+    if weight is not None and (weight.dtype != torch.float32 or weight.shape != (k,)):
+        raise ValueError("weight must be fp32 [K]")
+    xq = torch.empty((m, padded_k(k)), dtype=torch.int8, device=x.device)
+    scale = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check("bitlinear_rmsnorm_quant_act", lib.bitlinear_rmsnorm_quant_act(
+        _ptr(x), _dtype_code(x.dtype), m, k, _ptr(weight), float(norm_eps), float(eps), _ptr(xq),
+        _ptr(scale), _stream(stream)))
+    return xq, scale
+
+
 def forward(xq, scale, packed, gamma, n: int, k: int, relu2: bool = False,
             out_dtype=None, acc_out: bool = False, y=None, workspace: Optional[Workspace] = None,
             stream=None):
@@ -246,7 +267,8 @@ class FusedStep:
     sharing the token count m, each quantizing its own activations.
 
     ops: list of dicts with keys x, packed, gamma, n, k, y and optional
-    relu2, acc_out, xq_out, scale_out (tensors on the device)."""
+    relu2, acc_out, xq_out, scale_out (tensors on the device), rmsnorm (bool),
+    norm_weight (fp32 [k] tensor or None), norm_eps."""
 
     def __init__(self, ops, eps: float = EPS_DEFAULT, workspace: Optional[Workspace] = None):
         if not 1 <= len(ops) <= BL_MAX_FUSED:
@@ -263,7 +285,10 @@ class FusedStep:
                               int(o["n"]), int(o["k"]),
                               BL_EPI_RELU2 if o.get("relu2") else BL_EPI_NONE,
                               _dtype_code(y.dtype), _ptr(y), _ptr(o.get("acc_out")),
-                              _ptr(o.get("xq_out")), _ptr(o.get("scale_out")))
+                              _ptr(o.get("xq_out")), _ptr(o.get("scale_out")),
+                              1 if o.get("rmsnorm") else 0,
+                              float(o.get("norm_eps", NORM_EPS_DEFAULT)),
+                              _ptr(o.get("norm_weight")))
         self.arr = arr
         self.nbytes = int(lib.bitlinear_forward_fused_workspace_bytes(arr, len(ops), self.m))
         self.ws = workspace or Workspace(ops[0]["x"].device)

@@ -170,6 +170,8 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
 }
 
 struct FusedPlan {
+  bool unsupported = false;             // no kernel takes this table
+  bool norm = false;                    // some entry has RMSNorm
   bool stream = false;                  // 1..2 tokens: the streaming matrix-core kernel
   int xr = 0;                           // its activation units per thread and token
   int nsub_alloc = 0;                   // its sub-blocks per workgroup, at most
@@ -191,7 +193,8 @@ struct FusedPlan {
 // rows of at least 8 super-chunks.  Workgroups are
 // shared out in proportion to each entry's packed bytes, about one per CU in
 // all, each entry at least one and at most one per 16-row sub-block.
-static bool stream_fused_plan(const bl_linear* ops, int nops, int64_t m, FusedPlan* p) {
+static bool stream_fused_plan(const bl_linear* ops, int nops, int64_t m, bool norm,
+                              FusedPlan* p) {
   const int xdt = ops[0].x_dtype;
   int64_t units = 0, nc_max = 0, nu_max = 0;
   for (int i = 0; i < nops; ++i) {
@@ -204,11 +207,11 @@ static bool stream_fused_plan(const bl_linear* ops, int nops, int64_t m, FusedPl
     const int64_t nu = ops[i].k * esize / 16;
     if (nu > nu_max) nu_max = nu;
   }
-  if (nc_max < 8) return false;
+  if (nc_max < 8 && !norm) return false;
   int waves, depth;
   stream_shape((int)m, nc_max, &waves, &depth);
   const int64_t xr = cdiv(nu_max, 64 * waves);
-  if (m * xr > 8) return false;
+  if (m * xr > 8 || (norm && m * xr > 4)) return false;
   // one workgroup per CU at most: a 16-wave workgroup fills a CU, so a
   // workgroup past the 256th would wait for a whole round
   int64_t gs[kMaxFused], total = 0;
@@ -237,6 +240,7 @@ static bool stream_fused_plan(const bl_linear* ops, int nops, int64_t m, FusedPl
   const size_t lds = stream_lds_bytes((int)m, nc_max, nsub_alloc);
   if (lds > kStreamMaxLds) return false;
   p->stream = true;
+  p->norm = norm;
   p->xr = (int)xr;
   p->nsub_alloc = nsub_alloc;
   p->nc_max = nc_max;
@@ -261,8 +265,13 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   // ones by the number of groups, each of which reads and quantizes its x
   // range.  (Tuned on MI355X over the 2B- and 100B-class shapes.)
   FusedPlan p;
-  if (m <= 2 && stream_fused_plan(ops, nops, m, &p)) return p;
-  if (m >= 3) {
+  bool norm = false;
+  for (int i = 0; i < nops; ++i) norm = norm || ops[i].rmsnorm != 0;
+  if (m <= 2 && stream_fused_plan(ops, nops, m, norm, &p)) return p;
+  // RMSNorm tables the streaming kernel does not take run on the matrix-core
+  // fused kernel at any token count
+  p.norm = norm;
+  if (m >= 3 || norm) {
     // Matrix cores: two 16-row groups x 4 K-slices per workgroup, or for
     // sets with >= 256 row blocks in an entry four 32-row groups with the
     // whole K per wave; no K split over workgroups, no workspace.
@@ -332,6 +341,7 @@ inline bool valid_act_eps(float e) {
   const volatile float smax = 127.0f / e;
   return isfinite((float)smax);
 }
+inline bool valid_norm_eps(float e) { return isfinite(e) && e > 0.0f; }
 }  // namespace
 
 extern "C" {
@@ -383,9 +393,12 @@ static bl_status check_fused(const bl_linear* ops, int nops, int64_t m) {
     if (o.epilogue != BL_EPI_NONE && o.epilogue != BL_EPI_RELU2) return BL_ERR_INVALID_ARG;
     if (o.n < 1 || o.k < 1) return BL_ERR_INVALID_ARG;
     if (o.n > BL_MAX_MN || o.k > BL_MAX_K) return BL_ERR_UNSUPPORTED_SHAPE;
+    if (o.rmsnorm && !valid_norm_eps(o.norm_eps)) return BL_ERR_INVALID_ARG;
     if (m == 0) continue;
     if (o.x == nullptr || o.packed == nullptr || o.gamma == nullptr || o.y == nullptr)
       return BL_ERR_INVALID_ARG;
+    if (o.rmsnorm && o.norm_weight != nullptr && !aligned(o.norm_weight, 16))
+      return BL_ERR_MISALIGNED;
     if (!aligned(o.x, o.x_dtype == BL_BF16 ? 2 : 4) || !aligned(o.packed, 16) ||
         !aligned(o.gamma, 4) || !aligned(o.y, o.y_dtype == BL_BF16 ? 2 : 4) ||
         (o.acc_out != nullptr && !aligned(o.acc_out, 4)) ||
@@ -408,6 +421,7 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
   if (!valid_act_eps(eps)) return BL_ERR_INVALID_ARG;
   if (m == 0) return BL_OK;
   const FusedPlan plan = fused_plan(ops, nops, m);
+  if (plan.unsupported) return BL_ERR_UNSUPPORTED_SHAPE;
   if (plan.ws_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return BL_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return BL_ERR_MISALIGNED;
@@ -432,7 +446,9 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
     sg.splits = plan.splits[i];
     sg.wg_begin = begin;
     sg.flags = (o.epilogue == BL_EPI_RELU2 ? 1 : 0) | (o.y_dtype == BL_BF16 ? 2 : 0) |
-               (o.x_dtype == BL_BF16 ? 4 : 0);
+               (o.x_dtype == BL_BF16 ? 4 : 0) | (o.rmsnorm ? 8 : 0);
+    sg.norm_weight = o.norm_weight;
+    sg.norm_eps = o.norm_eps;
     args.wg_begin[i] = begin;
     if (sg.splits > 1 && !plan.stream)
       sg.slots = reinterpret_cast<int64_t*>(reinterpret_cast<char*>(workspace) + plan.slot_off[i]);
@@ -443,8 +459,9 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
   if (plan.stream) {
     args.nsub_alloc = plan.nsub_alloc;
     const hipError_t e = launch_gemv_stream_fused(args, (int)m, plan.nc_max,
-                                                  ops[0].x_dtype == BL_BF16, plan.xr, begin,
-                                                  plan.lds, reinterpret_cast<hipStream_t>(stream));
+                                                  ops[0].x_dtype == BL_BF16, plan.norm, plan.xr,
+                                                  begin, plan.lds,
+                                                  reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? BL_OK : BL_ERR_HIP;
   }
   if (plan.mfma) {
@@ -455,7 +472,8 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
       all_fast = all_fast && ops[i].k * esize % 16 == 0 && aligned(ops[i].x, 16);
     }
     const hipError_t e = launch_gemv_mfma_fused(args, (int)m, plan.variant, all_bf16, all_fast,
-                                                begin, reinterpret_cast<hipStream_t>(stream));
+                                                plan.norm, begin,
+                                                reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? BL_OK : BL_ERR_HIP;
   }
   bool long_rows = false;                            // a row of more than 1024 16-byte units
@@ -510,6 +528,24 @@ bl_status bitlinear_quant_act(const void* x, int x_dtype, int64_t m, int64_t k, 
     return BL_ERR_MISALIGNED;
   hipError_t e = launch_quant_act(x, x_dtype == BL_BF16, m, k, padded_k(k), eps, xq, scale,
                                   reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? BL_OK : BL_ERR_HIP;
+}
+
+bl_status bitlinear_rmsnorm_quant_act(const void* x, int x_dtype, int64_t m, int64_t k,
+                                      const float* norm_weight, float norm_eps, float eps,
+                                      int8_t* xq, float* scale, void* stream) {
+  if (!valid_dtype(x_dtype) || !valid_act_eps(eps) || !valid_norm_eps(norm_eps))
+    return BL_ERR_INVALID_ARG;
+  if (m < 0 || k < 1) return BL_ERR_INVALID_ARG;
+  if (m > BL_MAX_MN || k > BL_MAX_K) return BL_ERR_UNSUPPORTED_SHAPE;
+  if (m == 0) return BL_OK;
+  if (x == nullptr || xq == nullptr || scale == nullptr) return BL_ERR_INVALID_ARG;
+  if (!aligned(x, x_dtype == BL_BF16 ? 2 : 4) || !aligned(xq, 16) || !aligned(scale, 4) ||
+      (norm_weight != nullptr && !aligned(norm_weight, 4)))
+    return BL_ERR_MISALIGNED;
+  hipError_t e = launch_rmsnorm_quant(x, x_dtype == BL_BF16, m, k, padded_k(k), norm_weight,
+                                      norm_eps, eps, xq, scale,
+                                      reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? BL_OK : BL_ERR_HIP;
 }
 

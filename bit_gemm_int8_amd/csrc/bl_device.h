@@ -98,6 +98,28 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return a > c ? a : c;
 }
 
+// Sum over the wave in fp64 in a fixed order (xor butterfly): every lane
+// ends with the same value, the same for every run.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// RMSNorm factor from the fp64 sum of squares of a row of k activations:
+// ms = fp32(sum / k), v = fp32(ms + eps), r = fp32(1 / sqrt(v)) evaluated in
+// fp64 (division and square root correctly rounded there) and rounded once.
+__device__ __forceinline__ float rms_factor(double sumsq, int k, float norm_eps) {
+  const float ms = (float)(sumsq / (double)k);
+  const float v = __fadd_rn(ms, norm_eps);
+  return (float)(1.0 / sqrt((double)v));
+}
+
+// y = fp32(fp32(x * r) * w): two separately rounded multiplies.
+__device__ __forceinline__ float rms_apply(float x, float r, float w) {
+  return __fmul_rn(__fmul_rn(x, r), w);
+}
+
 // Rescale factor gamma / s as the correctly rounded fp32 quotient (the fp64
 // quotient of two fp32 values rounds to the same fp32 as the exact one).
 __device__ __forceinline__ float gamma_over_s(float gamma, float s) {

@@ -12,6 +12,11 @@ namespace bl {
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t m, int64_t k, int64_t kpad,
                             float eps, int8_t* xq, float* scale, hipStream_t stream);
 
+// RMSNorm + activation quantization: one workgroup per token.
+hipError_t launch_rmsnorm_quant(const void* x, bool bf16, int64_t m, int64_t k, int64_t kpad,
+                                const float* norm_weight, float norm_eps, float eps, int8_t* xq,
+                                float* scale, hipStream_t stream);
+
 // Weight absmean partial sums + ternarize/pack.
 struct PackPlan {
   int64_t total;       // n * k
@@ -71,11 +76,14 @@ struct alignas(64) FusedSeg {
   void* y;                // [m][n]
   int64_t* slots;         // split-K slots, [row block][m][64] (splits > 1)
   int n, k, nc, splits, wg_begin;
-  int flags;              // bit 0: ReLU^2, bit 1: y bf16, bit 2: x bf16
+  int flags;              // bit 0: ReLU^2, bit 1: y bf16, bit 2: x bf16, bit 3: RMSNorm
   int32_t* acc_out;       // nullable
   int8_t* xq_out;         // nullable, [m][padded_k(k)]
   float* scale_out;       // nullable, [m]
+  const float* norm_weight;  // RMSNorm gain (nullable: ones), with flags bit 3
+  float norm_eps;
   __host__ __device__ bool relu2() const { return (flags & 1) != 0; }
+  __host__ __device__ bool rmsnorm() const { return (flags & 8) != 0; }
   __host__ __device__ bool y_bf16() const { return (flags & 2) != 0; }
   __host__ __device__ bool x_bf16() const { return (flags & 4) != 0; }
 };
@@ -95,7 +103,7 @@ hipError_t launch_gemv_mfma(int variant, const int8_t* xq, const float* scale,
                             int64_t k, bool relu2, bool bf16, void* y, int32_t* acc_out,
                             hipStream_t stream);
 hipError_t launch_gemv_mfma_fused(const FusedArgs& args, int m, int variant, bool all_bf16,
-                                  bool all_fast, int groups, hipStream_t stream);
+                                  bool all_fast, bool norm, int groups, hipStream_t stream);
 hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, int qpl, bool long_rows,
                              int groups, size_t lds, hipStream_t stream);
 
@@ -108,7 +116,8 @@ hipError_t launch_gemv_stream(int m, const int8_t* xq, const float* scale,
                               int grid, bool relu2, bool bf16, void* y, int32_t* acc_out,
                               hipStream_t stream);
 hipError_t launch_gemv_stream_fused(const FusedArgs& args, int m, int64_t nc_max, bool x_bf16,
-                                    int xr, int groups, size_t lds, hipStream_t stream);
+                                    bool norm, int xr, int groups, size_t lds,
+                                    hipStream_t stream);
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t padded_n(int64_t n) { return 64 * cdiv(n, 64); }

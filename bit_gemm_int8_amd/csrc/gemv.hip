@@ -580,7 +580,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_fused_kernel(
 //      workgroup).
 // Workgroup g of an entry owns WR row groups of SB 16-row sub-blocks; its
 // WK waves per group split the super-chunks and meet in LDS at the end.
-template <int WR, int WK, int SB, int PF, int RPU, int MT, bool FAST>
+// With NORM, entries flagged for RMSNorm normalize each token first (the
+// BitLinear listing of "End-to-End Implementation: Building a Native BitLinear
+// Layer" applies nn.RMSNorm before quantize_activations_int8): the token's
+// wave sums x^2 over the row in fp64 (lanes, then the xor butterfly),
+// r = rms_factor(sum, K, eps), and y = fp32(fp32(x * r) * w) replaces x in
+// the absmax and in the staging.
+template <int WR, int WK, int SB, int PF, int RPU, int MT, bool FAST, bool NORM>
 // Leading scalar arguments (preloadable into SGPRs, as in gemv_fused_kernel):
 // the token count, the entry count and the first workgroup of entries 1..12
 // (INT_MAX past nseg).
@@ -603,6 +609,7 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(
   __shared__ uint32_t bmax[MT];
   __shared__ float s_lds[16];
   __shared__ float fac_lds[16];
+  __shared__ float rn_lds[NORM ? MT : 1];
   // token block blockIdx.y: tokens t0 .. t0 + m - 1 (16 per block)
   const int t0 = 16 * (int)blockIdx.y;
   const int m = min(m_all - t0, MT);
@@ -652,8 +659,30 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(
   //    last unit: the max is idempotent)
   const XRow xrow = x_row_info(sg);
   const bool xbf = sg.x_bf16();
+  const bool nrm = NORM && sg.rmsnorm();
+  const float* gain = sg.norm_weight;
+  // RMSNorm gain of input i (ones when absent; i past K clamped, where x is 0)
+  auto gain_at = [&](int i) __attribute__((always_inline)) {
+    return gain != nullptr ? gain[min(i, sg.k - 1)] : 1.0f;
+  };
   for (int t = wave; t < m; t += WAVES) {
     const char* row = x_row(sg, t0 + t);
+    float rn = 1.0f;
+    if (NORM && nrm) {                               // sum of squares (fp64), this wave
+      double ss = 0.0;
+      for (int u = lane; u < xrow.nu; u += 64) {
+        uint32_t e[8];
+        expand_unit(xbf, FAST ? reinterpret_cast<const uint4*>(row)[u]
+                              : load_unit(sg, xrow, row, u), e);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double d = (double)__uint_as_float(e[i]);
+          ss += d * d;
+        }
+      }
+      rn = rms_factor(wave_sum_f64(ss), sg.k, sg.norm_eps);
+      if (lane == 0) rn_lds[t] = rn;
+    }
     uint32_t mx = 0;
     for (int ub = 0; ub < xrow.nu; ub += 64 * 8) {
       uint4 v[8];
@@ -662,8 +691,23 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(
         const int u = min(ub + lane + 64 * j, xrow.nu - 1);
         v[j] = FAST ? reinterpret_cast<const uint4*>(row)[u] : load_unit(sg, xrow, row, u);
       }
+      if (NORM && nrm) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mx = max(mx, absmax_unit(xbf, v[j]));
+        for (int j = 0; j < 8; ++j) {
+          const int u = min(ub + lane + 64 * j, xrow.nu - 1);
+          uint32_t e[8];
+          expand_unit(xbf, v[j], e);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if (i >= xrow.epu) break;
+            const float y = rms_apply(__uint_as_float(e[i]), rn, gain_at(u * xrow.epu + i));
+            mx = max(mx, __float_as_uint(y) & 0x7FFFFFFFu);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mx = max(mx, absmax_unit(xbf, v[j]));
+      }
     }
     mx = wave_max_u32(mx);
     if (lane == 0) bmax[t] = mx;
@@ -685,7 +729,7 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(
   const int epu = xrow.epu;                         // activations per 16-byte unit: 8 or 4
   const char* xsrc[XU];
   int xdst[XU], xtok[XU], xq16[XU];
-  float xsc[XU];
+  float xsc[XU], xrn[XU];
 #pragma unroll
   for (int i = 0; i < XU; ++i) {
     const int q = wr * 64 + lane + NTS * i;
@@ -695,7 +739,19 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(
     xsrc[i] = x_row(sg, t0 + min(t, m - 1));
     xdst[i] = t * 16 + (u ^ (t & 15));
     xsc[i] = s_lds[t];
+    xrn[i] = NORM && nrm ? rn_lds[min(t, m - 1)] : 1.0f;
   }
+  // gains of a step's units (16 inputs each), RMSNorm entries only
+  float xg[NORM ? PF : 1][NORM ? XU : 1][16];
+  auto load_g = [&](auto P, int c) __attribute__((always_inline)) {
+    if (NORM && nrm) {
+      constexpr int p = decltype(P)::value;
+#pragma unroll
+      for (int i = 0; i < XU; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xg[p][i][e] = gain_at(c * 256 + xq16[i] * 16 + e);
+    }
+  };
   // raw activations of a step's units: RPU 16-byte units each (bf16 uses
   // the first two of four)
   uint4 xr[PF][XU][RPU];
@@ -710,12 +766,37 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(
                            : load_unit(sg, xrow, xsrc[i], min(u, xrow.nu - 1));
       }
   };
-  // x~ of one unit from its raw activations (zero past the row)
-  auto quant_unit = [&](const uint4 (&raw)[RPU], float sc, int c, int q16)
-      __attribute__((always_inline)) {
+  // x~ of one unit from its raw activations (zero past the row); with
+  // RMSNorm, of y = (x r) w
+  auto quant_unit = [&](const uint4 (&raw)[RPU], float sc, int c, int q16, float rnv,
+                        const float* gv) __attribute__((always_inline)) {
     const int k0 = c * 256 + q16 * 16;
     uint32_t d[4];
-    if (xbf) {
+    if (NORM && nrm) {
+      uint32_t v[16];
+      if (xbf) {
+        uint32_t e0[8], e1[8];
+        expand_unit(true, raw[0], e0);
+        expand_unit(true, raw[1 < RPU ? 1 : 0], e1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[i] = e0[i];
+          v[8 + i] = e1[i];
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          uint32_t e[8];
+          expand_unit(false, raw[h < RPU ? h : 0], e);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[4 * h + i] = e[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = __float_as_uint(rms_apply(__uint_as_float(v[i]), rnv, gv[i]));
+#pragma unroll
+      for (int h = 0; h < 4; ++h) d[h] = quant4_magic(v + 4 * h, sc);
+    } else if (xbf) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         uint32_t e[8];
@@ -744,7 +825,10 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(
     }
     return out;
   };
-  static_for<PF>([&](auto P) { load_x(P, min(c0 + (int)P, clast)); });
+  static_for<PF>([&](auto P) {
+    load_x(P, min(c0 + (int)P, clast));
+    load_g(P, min(c0 + (int)P, clast));
+  });
 
   bl_v4i acc[SB];
 #pragma unroll
@@ -756,7 +840,7 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(
     bl_v4i* win = xs[wk][p & 1];
 #pragma unroll
     for (int i = 0; i < XU; ++i) {
-      const bl_v4i qv = quant_unit(xr[p][i], xsc[i], c, xq16[i]);
+      const bl_v4i qv = quant_unit(xr[p][i], xsc[i], c, xq16[i], xrn[i], xg[NORM ? p : 0][NORM ? i : 0]);
       win[xdst[i]] = qv;
       if (write_xq && c < c1 && xtok[i] < m)
         *reinterpret_cast<bl_v4i*>(sg.xq_out + (int64_t)(t0 + xtok[i]) * kpad + c * 256 + xq16[i] * 16) =
@@ -765,6 +849,7 @@ __global__ __launch_bounds__(64 * WR * WK) void gemv_mfma_fused_kernel(
     __syncthreads();
     const int cn = min(c + PF, clast);
     load_x(P, cn);
+    load_g(P, cn);
     __builtin_amdgcn_sched_barrier(0);
     if (c < c1) {
 #pragma unroll
@@ -865,16 +950,21 @@ hipError_t launch_gemv(int m, int waves, int pf, int qpl, const int8_t* xq, cons
 // all_bf16: every entry's x is bf16 (two 16-byte loads per x~ unit, not
 // four); all_fast: every entry's rows are whole, aligned 16-byte units.
 hipError_t launch_gemv_mfma_fused(const FusedArgs& args, int m, int variant, bool all_bf16,
-                                  bool all_fast, int groups, hipStream_t stream) {
+                                  bool all_fast, bool norm, int groups, hipStream_t stream) {
   if (m < 1 || m > 64) return hipErrorInvalidValue;
   const dim3 grid((unsigned)groups, (unsigned)((m + 15) / 16));   // token blocks of 16
   int wb[13];
   for (int i = 1; i < 13; ++i) wb[i] = i < args.nseg ? args.wg_begin[i] : INT_MAX;
-#define BL_MF(WR, WK, SB, PF, RPU, MT, FAST)                                         \
-  gemv_mfma_fused_kernel<WR, WK, SB, PF, RPU, MT, FAST>                              \
+#define BL_MF1(WR, WK, SB, PF, RPU, MT, FAST, NORM)                                   \
+  gemv_mfma_fused_kernel<WR, WK, SB, PF, RPU, MT, FAST, NORM>                        \
       <<<grid, 64 * WR * WK, 0, stream>>>(m, args.nseg, wb[1], wb[2], wb[3], wb[4], wb[5],  \
                                           wb[6], wb[7], wb[8], wb[9], wb[10], wb[11], wb[12],  \
                                           args)
+#define BL_MF(WR, WK, SB, PF, RPU, MT, FAST)                  \
+  do {                                                        \
+    if (norm) BL_MF1(WR, WK, SB, PF, RPU, MT, FAST, true);    \
+    else BL_MF1(WR, WK, SB, PF, RPU, MT, FAST, false);        \
+  } while (0)
 #define BL_MF_X(WR, WK, SB, PF, MT)               \
   if (all_fast && all_bf16) BL_MF(WR, WK, SB, PF, 2, MT, true); \
   else if (all_fast) BL_MF(WR, WK, SB, PF, 4, MT, true);       \
@@ -890,6 +980,7 @@ hipError_t launch_gemv_mfma_fused(const FusedArgs& args, int m, int variant, boo
   }
 #undef BL_MF_X
 #undef BL_MF
+#undef BL_MF1
   return hipGetLastError();
 }
 

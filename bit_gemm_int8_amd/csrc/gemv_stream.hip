@@ -254,15 +254,22 @@ __device__ __forceinline__ uint32_t quant4_of(uint32_t a, uint32_t b, uint32_t c
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-template <int M, int WAVES, int D, int XR, bool BF16>
+// With NORM, entries flagged for RMSNorm first normalize each token (the
+// BitLinear listing of "End-to-End Implementation: Building a Native
+// BitLinear Layer" applies nn.RMSNorm before quantize_activations_int8):
+// the fp64 sum of squares of the held units, reduced in a fixed order (xor
+// butterfly in the wave, waves in order), r = rms_factor(sum, K, eps), and
+// y = fp32(fp32(x * r) * w) replaces x in steps 2 and 3.
+template <int M, int WAVES, int D, int XR, bool BF16, bool NORM>
 __global__ __launch_bounds__(64 * WAVES) void gemv_stream_fused_kernel(
     int nseg, int wb1, int wb2, int wb3, int wb4, int wb5, int wb6, int wb7, int wb8, int wb9,
     int wb10, int wb11, int wb12, int wb13, FusedArgs args) {
   constexpr int NT = 64 * WAVES;
   constexpr int EPU = BF16 ? 8 : 4;                  // activations per 16-byte unit
+  constexpr int WPU = EPU / 4;                       // 16-byte gain units per activation unit
   extern __shared__ uint4 lds[];
   __shared__ uint32_t red[WAVES][M];
-  __shared__ float s_lds[M];
+  __shared__ double red64[NORM ? WAVES : 1][M];
   const int bid = (int)blockIdx.x;
   const int wb[13] = {wb1, wb2, wb3, wb4, wb5, wb6, wb7, wb8, wb9, wb10, wb11, wb12, wb13};
   int si = 0;
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_fused_kernel(
   const int zero_idx = stream_zero_idx(M, kp16, nsub_alloc);
   const uint4* packed = reinterpret_cast<const uint4*>(sg.packed);
 
-  // 1. activations, then weights
+  // 1. activations (and the RMSNorm gain), then weights
   const int nu = k / EPU;                             // units per row (whole units)
   uint4 xr[M][XR];
 #pragma unroll
@@ -300,22 +307,96 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_fused_kernel(
 #pragma unroll
     for (int j = 0; j < XR; ++j) xr[m][j] = row[min((int)threadIdx.x + NT * j, nu - 1)];
   }
+  const bool nrm = NORM && sg.rmsnorm();
+  const bool have_w = nrm && sg.norm_weight != nullptr;
+  uint4 wr[NORM ? XR : 1][WPU];
+  if (NORM) {
+    // without a gain the loads read the packed weights instead (at least as
+    // long as the gain would be), which are never used: no load behind a branch
+    const uint4* wsrc = have_w ? reinterpret_cast<const uint4*>(sg.norm_weight) : packed;
+#pragma unroll
+    for (int j = 0; j < XR; ++j)
+#pragma unroll
+      for (int h = 0; h < WPU; ++h)
+        wr[j][h] = wsrc[min((int)threadIdx.x + NT * j, nu - 1) * WPU + h];
+  }
   uint4 buf[D];
   Cursor cur = cursor_at(packed, nc, t0, u0, u1, g, r);
   prefetch_units<D>(buf, cur, packed, nc, g, r);
   const float gm = *sg.gamma;
+  for (int i = threadIdx.x; i < nsub * M * 16; i += NT) sums[i] = 0;
+  if (threadIdx.x < 16) lds[zero_idx + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+
+  // the EPU activations of held unit j of token m as fp32 bit patterns
+  auto raw_vals = [&](int m, int j, uint32_t (&v)[8]) __attribute__((always_inline)) {
+    const uint4 x = xr[m][j];
+    if (BF16) {
+      v[0] = x.x << 16; v[1] = x.x & 0xFFFF0000u; v[2] = x.y << 16; v[3] = x.y & 0xFFFF0000u;
+      v[4] = x.z << 16; v[5] = x.z & 0xFFFF0000u; v[6] = x.w << 16; v[7] = x.w & 0xFFFF0000u;
+    } else {
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    }
+  };
+  float rn[M];                                        // RMSNorm factors
+#pragma unroll
+  for (int m = 0; m < M; ++m) rn[m] = 1.0f;
+  if (nrm) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      double ss = 0.0;
+#pragma unroll
+      for (int j = 0; j < XR; ++j) {
+        if ((int)threadIdx.x + NT * j < nu) {
+          uint32_t v[8];
+          raw_vals(m, j, v);
+#pragma unroll
+          for (int e = 0; e < EPU; ++e) {
+            const double d = (double)__uint_as_float(v[e]);
+            ss += d * d;
+          }
+        }
+      }
+      ss = wave_sum_f64(ss);
+      if (lane == 0) red64[wave][m] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      double t = red64[0][m];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) t += red64[w][m];
+      rn[m] = rms_factor(t, k, sg.norm_eps);
+    }
+  }
+  // the values the quantization sees: x, or y = (x r) w
+  auto vals = [&](int m, int j, uint32_t (&v)[8]) __attribute__((always_inline)) {
+    raw_vals(m, j, v);
+    if (NORM && nrm) {
+      const uint32_t wv[8] = {wr[j][0].x, wr[j][0].y, wr[j][0].z, wr[j][0].w,
+                              wr[j][WPU - 1].x, wr[j][WPU - 1].y, wr[j][WPU - 1].z,
+                              wr[j][WPU - 1].w};
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) {
+        const float w = have_w ? __uint_as_float(wv[e]) : 1.0f;
+        v[e] = __float_as_uint(rms_apply(__uint_as_float(v[e]), rn[m], w));
+      }
+    }
+  };
 
   // 2. beta and s per token
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     uint32_t mx = 0;
 #pragma unroll
-    for (int j = 0; j < XR; ++j) mx = max(mx, unit_absmax_bits<BF16>(xr[m][j]));
+    for (int j = 0; j < XR; ++j) {
+      uint32_t v[8];
+      vals(m, j, v);
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) mx = max(mx, v[e] & 0x7FFFFFFFu);
+    }
     mx = wave_max_u32(mx);
     if (lane == 0) red[wave][m] = mx;
   }
-  for (int i = threadIdx.x; i < nsub * M * 16; i += NT) sums[i] = 0;
-  if (threadIdx.x < 16) lds[zero_idx + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   float sv[M];
 #pragma unroll
@@ -334,15 +415,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_fused_kernel(
     for (int j = 0; j < XR; ++j) {
       const int u = (int)threadIdx.x + NT * j;
       if (u < nu) {
-        const uint4 x = xr[m][j];
+        uint32_t v[8];
+        vals(m, j, v);
         if (BF16) {
-          const uint32_t d0 = quant4_of(x.x << 16, x.x & 0xFFFF0000u, x.y << 16,
-                                        x.y & 0xFFFF0000u, sv[m]);
-          const uint32_t d1 = quant4_of(x.z << 16, x.z & 0xFFFF0000u, x.w << 16,
-                                        x.w & 0xFFFF0000u, sv[m]);
+          const uint32_t d0 = quant4_of(v[0], v[1], v[2], v[3], sv[m]);
+          const uint32_t d1 = quant4_of(v[4], v[5], v[6], v[7], sv[m]);
           reinterpret_cast<uint2*>(xw + m * kp16 * 4)[u] = make_uint2(d0, d1);
         } else {
-          xw[m * kp16 * 4 + u] = quant4_of(x.x, x.y, x.z, x.w, sv[m]);
+          xw[m * kp16 * 4 + u] = quant4_of(v[0], v[1], v[2], v[3], sv[m]);
         }
       }
     }
@@ -392,11 +472,11 @@ void run_stream_xr(int xr, const int8_t* xq, const float* scale, const uint32_t*
                                acc_out, lds, stream);
 }
 
-template <int M, int WAVES, int D, int XR>
+template <int M, int WAVES, int D, int XR, bool NORM>
 void run_stream_fused(const FusedArgs& args, const int (&wb)[14], int groups, size_t lds,
                       bool bf16, hipStream_t stream) {
 #define BL_SF(B)                                                                             \
-  gemv_stream_fused_kernel<M, WAVES, D, XR, B><<<groups, 64 * WAVES, lds, stream>>>(         \
+  gemv_stream_fused_kernel<M, WAVES, D, XR, B, NORM><<<groups, 64 * WAVES, lds, stream>>>(   \
       args.nseg, wb[1], wb[2], wb[3], wb[4], wb[5], wb[6], wb[7], wb[8], wb[9], wb[10],      \
       wb[11], wb[12], wb[13], args)
   if (bf16)
@@ -406,20 +486,33 @@ void run_stream_fused(const FusedArgs& args, const int (&wb)[14], int groups, si
 #undef BL_SF
 }
 
-template <int M, int WAVES, int D>
+template <int M, int WAVES, int D, bool NORM>
 void run_stream_fused_xr(int xr, const FusedArgs& args, const int (&wb)[14], int groups,
                          size_t lds, bool bf16, hipStream_t stream) {
-  // the plan keeps M * xr <= 8 (the activation registers)
+  // the plan keeps M * xr <= 8 (the activation registers), and xr <= 4 with
+  // RMSNorm (the gain registers)
   if (xr <= 2) {
-    run_stream_fused<M, WAVES, D, 2>(args, wb, groups, lds, bf16, stream);
-  } else if constexpr (M > 1) {
-    run_stream_fused<M, WAVES, D, 4>(args, wb, groups, lds, bf16, stream);
+    run_stream_fused<M, WAVES, D, 2, NORM>(args, wb, groups, lds, bf16, stream);
+  } else if constexpr (M > 1 && NORM) {
+    // unreachable: the plan keeps M * xr <= 4 with RMSNorm
+    run_stream_fused<M, WAVES, D, 2, NORM>(args, wb, groups, lds, bf16, stream);
+  } else if constexpr (M > 1 || NORM) {
+    run_stream_fused<M, WAVES, D, 4, NORM>(args, wb, groups, lds, bf16, stream);
   } else {
     if (xr <= 4)
-      run_stream_fused<M, WAVES, D, 4>(args, wb, groups, lds, bf16, stream);
+      run_stream_fused<M, WAVES, D, 4, NORM>(args, wb, groups, lds, bf16, stream);
     else
-      run_stream_fused<M, WAVES, D, 8>(args, wb, groups, lds, bf16, stream);
+      run_stream_fused<M, WAVES, D, 8, NORM>(args, wb, groups, lds, bf16, stream);
   }
+}
+
+template <int M, int WAVES, int D>
+void run_stream_fused_n(bool norm, int xr, const FusedArgs& args, const int (&wb)[14],
+                        int groups, size_t lds, bool bf16, hipStream_t stream) {
+  if (norm)
+    run_stream_fused_xr<M, WAVES, D, true>(xr, args, wb, groups, lds, bf16, stream);
+  else
+    run_stream_fused_xr<M, WAVES, D, false>(xr, args, wb, groups, lds, bf16, stream);
 }
 
 }  // namespace
@@ -470,18 +563,19 @@ hipError_t launch_gemv_stream(int m, const int8_t* xq, const float* scale,
 }
 
 hipError_t launch_gemv_stream_fused(const FusedArgs& args, int m, int64_t nc_max, bool x_bf16,
-                                    int xr, int groups, size_t lds, hipStream_t stream) {
+                                    bool norm, int xr, int groups, size_t lds,
+                                    hipStream_t stream) {
   int wb[14];
   for (int i = 1; i < 14; ++i) wb[i] = i < args.nseg ? args.wg_begin[i] : INT_MAX;
   int waves, depth;
   stream_shape(m, nc_max, &waves, &depth);
   if (m == 1) {
     if (waves == 8)
-      run_stream_fused_xr<1, 8, 4>(xr, args, wb, groups, lds, x_bf16, stream);
+      run_stream_fused_n<1, 8, 4>(norm, xr, args, wb, groups, lds, x_bf16, stream);
     else
-      run_stream_fused_xr<1, 16, 3>(xr, args, wb, groups, lds, x_bf16, stream);
+      run_stream_fused_n<1, 16, 3>(norm, xr, args, wb, groups, lds, x_bf16, stream);
   } else if (m == 2) {
-    run_stream_fused_xr<2, 16, 3>(xr, args, wb, groups, lds, x_bf16, stream);
+    run_stream_fused_n<2, 16, 3>(norm, xr, args, wb, groups, lds, x_bf16, stream);
   } else {
     return hipErrorInvalidValue;
   }

@@ -170,7 +170,95 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
   for (int64_t i = k + tid; i < kpad; i += kThreads) qrow[i] = 0;
 }
 
+// ---------------------------------------------------------------- RMSNorm --
+// x -> y = x * r * w with r = 1 / sqrt(mean(x^2) + norm_eps) per token, then
+// the absmax quantization of y.  "BitNet b1.58 2B4T Guide", the BitLinear
+// listing in "End-to-End Implementation: Building a Native BitLinear Layer"
+// normalises x with RMSNorm before quantize_activations_int8.  One workgroup
+// per token, three passes over the row (the second and third from cache):
+// the fp64 sum of squares, max|y|, and x~ = clamp(rint(fp32(y * s))).
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+  const int tid = threadIdx.x;
+  v = wave_sum_f64(v);
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  double t = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) t += red[w];
+  return t;
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void rmsnorm_quant_kernel(
+    const void* __restrict__ x, int64_t k, int64_t kpad, const float* __restrict__ nw,
+    float neps, float eps, int8_t* __restrict__ xq, float* __restrict__ scale) {
+  constexpr int V = Row<BF16, VEC>::kVec;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const char* xrow = reinterpret_cast<const char*>(x) + row * k * (BF16 ? 2 : 4);
+  int8_t* qrow = xq + row * kpad;
+  __shared__ double red64[kThreads / 64];
+  __shared__ uint32_t red[kThreads / 64];
+  auto xval = [&](int64_t i) __attribute__((always_inline)) { return load_elem(xrow, i, BF16); };
+  auto wval = [&](int64_t i) __attribute__((always_inline)) { return nw ? nw[i] : 1.0f; };
+
+  // ---- pass 1: sum of squares (fp64) ----
+  double ss = 0.0;
+  for (int64_t i = (int64_t)tid * V; i < k; i += (int64_t)kThreads * V) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const double v = (double)xval(i + e);
+      ss += v * v;
+    }
+  }
+  const float r = rms_factor(block_sum_f64(ss, red64), (int)k, neps);
+
+  // ---- pass 2: max |y| ----
+  uint32_t mx = 0;
+  for (int64_t i = (int64_t)tid * V; i < k; i += (int64_t)kThreads * V) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const uint32_t b = __float_as_uint(rms_apply(xval(i + e), r, wval(i + e))) & 0x7FFFFFFFu;
+      mx = mx > b ? mx : b;
+    }
+  }
+  const float s = row_scale(mx, eps, red);
+  if (tid == 0) scale[row] = s;
+
+  // ---- pass 3: quantize y ----
+  for (int64_t i = (int64_t)tid * V; i < k; i += (int64_t)kThreads * V) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) qrow[i + e] = quantize(rms_apply(xval(i + e), r, wval(i + e)), s);
+  }
+  for (int64_t i = k + tid; i < kpad; i += kThreads) qrow[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_rmsnorm_quant(const void* x, bool bf16, int64_t m, int64_t k, int64_t kpad,
+                                const float* norm_weight, float norm_eps, float eps, int8_t* xq,
+                                float* scale, hipStream_t stream) {
+  if (m == 0) return hipSuccess;
+  dim3 grid((unsigned)m), block(kThreads);
+  // V elements per thread and step when a row splits into whole groups of V
+  const bool vec = (k % (bf16 ? 8 : 4)) == 0;
+  if (bf16) {
+    if (vec)
+      rmsnorm_quant_kernel<true, true><<<grid, block, 0, stream>>>(x, k, kpad, norm_weight,
+                                                                   norm_eps, eps, xq, scale);
+    else
+      rmsnorm_quant_kernel<true, false><<<grid, block, 0, stream>>>(x, k, kpad, norm_weight,
+                                                                    norm_eps, eps, xq, scale);
+  } else {
+    if (vec)
+      rmsnorm_quant_kernel<false, true><<<grid, block, 0, stream>>>(x, k, kpad, norm_weight,
+                                                                    norm_eps, eps, xq, scale);
+    else
+      rmsnorm_quant_kernel<false, false><<<grid, block, 0, stream>>>(x, k, kpad, norm_weight,
+                                                                     norm_eps, eps, xq, scale);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t m, int64_t k, int64_t kpad,
                             float eps, int8_t* xq, float* scale, hipStream_t stream) {

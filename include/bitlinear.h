@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 1
+#define BITLINEAR_ABI_VERSION 2
 
 /* Largest K: the kernels accumulate 64 * x~ * W~ in int32, so
  * 64 * 127 * K must stay below 2^31. */
@@ -137,6 +137,31 @@ bl_status bitlinear_quant_act(const void* x, int x_dtype, int64_t m, int64_t k,
                               float eps, int8_t* xq, float* scale, void* stream);
 
 /* ------------------------------------------------------------------------
+ * bitlinear_rmsnorm_quant_act -- RMSNorm of each token, then the per-token
+ * absmax int8 quantization of the normalized activations.  Defines: the
+ * BitLinear listing of "End-to-End Implementation: Building a Native
+ * BitLinear Layer" (nn.RMSNorm(in_features) applied to x before
+ * quantize_activations_int8); "8-Bit Activation Quantization: absmax
+ * Scaling" for the quantization.
+ *
+ *   x            [m][k] fp32 or bf16 (x_dtype), 4-byte aligned.
+ *   norm_weight  NULL (a gain of ones, the listing's initial value) or fp32
+ *                [k] on the device, 4-byte aligned.
+ *   norm_eps     > 0 and finite (nn.RMSNorm's default: fp32 machine epsilon,
+ *                2^-23).
+ *   eps, xq, scale  as in bitlinear_quant_act, for the normalized y.
+ * Per token: ms = fp32(sum_j x_j^2 / k) with the sum accumulated in fp64 in a
+ * fixed order (deterministic; equal to the exactly rounded mean unless that
+ * lies within fp64 rounding of an fp32 rounding boundary); r = fp32(1 /
+ * sqrt(fp32(ms + norm_eps))) evaluated in fp64; y_j = fp32(fp32(x_j * r) *
+ * w_j); then s and x~ from y exactly as bitlinear_quant_act.  m == 0 is a
+ * no-op.
+ * ---------------------------------------------------------------------- */
+bl_status bitlinear_rmsnorm_quant_act(const void* x, int x_dtype, int64_t m, int64_t k,
+                                      const float* norm_weight, float norm_eps, float eps,
+                                      int8_t* xq, float* scale, void* stream);
+
+/* ------------------------------------------------------------------------
  * bitlinear_forward -- y = (x~ W~^T) * gamma / s, with an optional fused
  * ReLU^2.  Defines: "Matrix Multiplication as Pure Integer Addition"
  * (integer accumulator; rescale by beta*gamma/127).
@@ -225,6 +250,12 @@ bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t 
  * one block of up to 16 tokens per workgroup) per workgroup; meant for
  * decode-sized batches.  From 3 tokens no workspace is needed (the size
  * query returns 0).
+ * Entries with rmsnorm set normalize x first (same numbers as
+ * bitlinear_rmsnorm_quant_act followed by bitlinear_forward).  At 1-2
+ * tokens a table with such an entry needs, for every entry, rows of whole
+ * 16-byte units at 16-byte alignment, one activation dtype, and x~ of
+ * every token within 64 KiB (2 * padded_k <= 65536 at two tokens);
+ * otherwise BL_ERR_UNSUPPORTED_SHAPE.
  * ---------------------------------------------------------------------- */
 #define BL_MAX_FUSED 16
 #define BL_FUSED_MAX_M 64
@@ -240,6 +271,9 @@ typedef struct {
   int32_t* acc_out;     /* nullable: int32 [m][n] accumulator */
   int8_t* xq_out;       /* nullable: int8 [m][padded_k(k)], 16-byte aligned */
   float* scale_out;     /* nullable: fp32 [m] */
+  int rmsnorm;          /* nonzero: RMSNorm of x first, as bitlinear_rmsnorm_quant_act */
+  float norm_eps;       /* with rmsnorm: > 0 and finite */
+  const float* norm_weight;  /* with rmsnorm: NULL (ones) or fp32 [k], 16-byte aligned */
 } bl_linear;
 size_t bitlinear_forward_fused_workspace_bytes(const bl_linear* ops, int nops, int64_t m);
 bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, float eps,

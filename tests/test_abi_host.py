@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(bl):
     raw = ctypes.CDLL(bl.LIB_PATH)
     for name in _declared_functions():
         assert hasattr(raw, name), name
-    assert bl.lib.bitlinear_abi_version() == 1
+    assert bl.lib.bitlinear_abi_version() == 2
 
 
 @pytest.mark.parametrize("n,k", [(1, 1), (64, 256), (65, 257), (2560, 6912), (28672, 8192), (130, 520)])
@@ -87,7 +87,7 @@ def test_activation_eps_boundary_matches_oracle(bl):
     below = float(np.nextafter(EPS_MIN, np.float32(0)))
     q = bl.lib.bitlinear_quant_act
     arr = (bl.BLLinear * 1)()
-    arr[0] = bl.BLLinear(None, 0, None, None, 64, 256, 0, 0, None, None, None, None)
+    arr[0] = bl.BLLinear(None, 0, None, None, 64, 256, 0, 0, None, None, None, None, 0, 1e-6, None)
     f = bl.lib.bitlinear_forward_fused
     for e, ok in ((float(EPS_MIN), True), (1e-5, True), (below, False), (0.0, False),
                   (1e-38, False), (-1e-5, False), (float("inf"), False)):
@@ -102,6 +102,28 @@ def test_activation_eps_boundary_matches_oracle(bl):
     ws = bl.lib.bitlinear_pack_workspace_bytes(64, 256)
     assert bl.lib.bitlinear_pack_weights(FAKE, 0, 64, 256, 0.0, None, FAKE + 256, FAKE, None,
                                          0, None) == 4      # eps = 0 passes; no workspace
+
+
+def test_rmsnorm_quant_act_rejects(bl):
+    q = bl.lib.bitlinear_rmsnorm_quant_act
+    assert q(FAKE, 0, 4, 8, None, 0.0, 1e-5, FAKE, FAKE, None) == 1       # norm eps 0
+    assert q(FAKE, 0, 4, 8, None, -1.0, 1e-5, FAKE, FAKE, None) == 1
+    assert q(FAKE, 0, 4, 8, None, float("inf"), 1e-5, FAKE, FAKE, None) == 1
+    assert q(FAKE, 0, 4, 8, None, 1e-6, 0.0, FAKE, FAKE, None) == 1       # activation eps 0
+    assert q(FAKE, 9, 4, 8, None, 1e-6, 1e-5, FAKE, FAKE, None) == 1      # dtype
+    assert q(FAKE, 0, 4, 0, None, 1e-6, 1e-5, FAKE, FAKE, None) == 1      # k < 1
+    assert q(FAKE, 0, 4, bl.BL_MAX_K + 1, None, 1e-6, 1e-5, FAKE, FAKE, None) == 2
+    assert q(FAKE, 0, 4, 8, FAKE + 2, 1e-6, 1e-5, FAKE, FAKE, None) == 3  # gain at 2 bytes
+    assert q(FAKE, 0, 4, 8, None, 1e-6, 1e-5, FAKE + 8, FAKE, None) == 3  # xq at 8 bytes
+    assert q(None, 0, 0, 8, None, 1e-6, 1e-5, None, None, None) == 0     # m == 0: no-op
+    # the fused step checks an entry's norm eps and gain alignment
+    f = bl.lib.bitlinear_forward_fused
+    arr = (bl.BLLinear * 1)()
+    arr[0] = bl.BLLinear(FAKE, 1, FAKE, FAKE, 64, 256, 0, 0, FAKE, None, None, None, 1, 0.0, None)
+    assert f(arr, 1, 1, 1e-5, None, 0, None) == 1
+    arr[0] = bl.BLLinear(FAKE, 1, FAKE, FAKE, 64, 256, 0, 0, FAKE, None, None, None, 1, 1e-6,
+                         FAKE + 4)
+    assert f(arr, 1, 1, 1e-5, None, 0, None) == 3
 
 
 def test_pack_rejects(bl):
