@@ -171,8 +171,10 @@ class Workspace:
 _default_ws = {}
 
 
-def _workspace_for(device) -> Workspace:
-    key = str(device)
+def _workspace_for(device, stream=None) -> Workspace:
+    """The default workspace of a (device, stream) pair: calls that share a
+    workspace must be ordered, and calls on one stream are."""
+    key = (str(device), _stream(stream))
     if key not in _default_ws:
         _default_ws[key] = Workspace(device)
     return _default_ws[key]
@@ -238,7 +240,7 @@ def forward(xq, scale, packed, gamma, n: int, k: int, relu2: bool = False,
         y = torch.empty((m, n), dtype=out_dtype, device=xq.device)
     acc = torch.empty((m, n), dtype=torch.int32, device=xq.device) if acc_out else None
     nbytes = forward_workspace_bytes(m, n, k)
-    ws = (workspace or _workspace_for(xq.device)).get(nbytes, stream)
+    ws = (workspace or _workspace_for(xq.device, stream)).get(nbytes, stream)
     _check("bitlinear_forward", lib.bitlinear_forward(
         _ptr(xq), _ptr(scale), _ptr(packed), _ptr(gamma), m, n, k,
         BL_EPI_RELU2 if relu2 else BL_EPI_NONE, _dtype_code(y.dtype), _ptr(y), _ptr(acc),
@@ -317,7 +319,7 @@ def forward_multi(xq, scale, k: int, ops, workspace: Optional[Workspace] = None,
         e.y_dtype, e.y = _dtype_code(o["y"].dtype), _ptr(o["y"])
         e.acc_out = _ptr(o.get("acc_out"))
     nbytes = int(lib.bitlinear_forward_multi_workspace_bytes(arr, len(ops), m, int(k)))
-    ws = (workspace or _workspace_for(xq.device)).get(nbytes, stream)
+    ws = (workspace or _workspace_for(xq.device, stream)).get(nbytes, stream)
     _check("bitlinear_forward_multi", lib.bitlinear_forward_multi(
         _ptr(xq), _ptr(scale), m, int(k), arr, len(ops), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
@@ -327,3 +329,66 @@ def forward_fused(ops, eps: float = EPS_DEFAULT, workspace: Optional[Workspace] 
                   stream=None) -> None:
     """bitlinear_forward_fused over a list of entries (see FusedStep)."""
     FusedStep(ops, eps, workspace)(stream)
+
+
+class BitLinearW158A8:
+    """Inference-only BitLinear layer (ternary weights, int8 activations) on
+    the library's kernels: the page's BitLinear(in_features, out_features,
+    bias=False) without its training state ("BitNet b1.58 2B4T Guide",
+    section "End-to-End Implementation: Building a Native BitLinear Layer").
+    The weights are packed once (bitlinear_pack_weights); a call runs the
+    RMSNorm (the listing's self.rms_norm, gain initialised to ones; off with
+    rmsnorm=False), the per-token absmax quantization, the ternary x int8
+    product and the rescale -- one fused launch up to BL_FUSED_MAX_M tokens,
+    else the quantization and bitlinear_forward.  x: [..., in_features] fp32
+    or bf16 on the device; returns [..., out_features] (out_dtype, default
+    the dtype of x).  Argument marshalling only."""
+
+    def __init__(self, in_features: int, out_features: int, bias: bool = False,
+                 rmsnorm: bool = True, relu2: bool = False, eps: float = EPS_DEFAULT,
+                 norm_eps: float = NORM_EPS_DEFAULT, out_dtype=None, device="cuda"):
+        import torch
+        if bias:
+            raise ValueError("BitLinear W1.58A8 has no bias terms")
+        self.in_features, self.out_features = int(in_features), int(out_features)
+        self.rmsnorm, self.relu2 = bool(rmsnorm), bool(relu2)
+        self.eps, self.norm_eps = float(eps), float(norm_eps)
+        self.out_dtype, self.device = out_dtype, device
+        self.norm_weight = torch.ones(self.in_features, dtype=torch.float32, device=device)
+        self.packed = self.gamma = None
+        self.workspace = Workspace(device)
+
+    def load_weight(self, weight, eps: Optional[float] = None):
+        """Pack W [out_features, in_features] (fp32 or bf16, on the device)."""
+        if tuple(weight.shape) != (self.out_features, self.in_features):
+            raise ValueError(f"weight must be [{self.out_features}, {self.in_features}]")
+        self.packed, self.gamma = pack_weights(weight.contiguous(),
+                                               self.eps if eps is None else eps)
+        return self
+
+    def __call__(self, x):
+        import torch
+        if self.packed is None:
+            raise RuntimeError("no weights: call load_weight first")
+        if x.shape[-1] != self.in_features:
+            raise ValueError(f"x must end in {self.in_features}")
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, self.in_features).contiguous()
+        m = x2.shape[0]
+        ydt = self.out_dtype or x.dtype
+        y = torch.empty((m, self.out_features), dtype=ydt, device=x.device)
+        if m == 0:
+            return y.reshape(*lead, self.out_features)
+        if m <= BL_FUSED_MAX_M:
+            FusedStep([dict(x=x2, packed=self.packed, gamma=self.gamma, n=self.out_features,
+                            k=self.in_features, y=y, relu2=self.relu2, rmsnorm=self.rmsnorm,
+                            norm_weight=self.norm_weight, norm_eps=self.norm_eps)],
+                      eps=self.eps, workspace=self.workspace)()
+        else:
+            if self.rmsnorm:
+                xq, s = rmsnorm_quant_act(x2, self.norm_weight, self.norm_eps, self.eps)
+            else:
+                xq, s = quant_act(x2, self.eps)
+            forward(xq, s, self.packed, self.gamma, self.out_features, self.in_features,
+                    relu2=self.relu2, y=y, workspace=self.workspace)
+        return y.reshape(*lead, self.out_features)

@@ -182,3 +182,38 @@ def test_rmsnorm_fused_equals_two_step(B):
                              acc_out=True)
         assert torch.equal(acc, acc2), m
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), m
+
+
+@pytest.mark.parametrize("rmsnorm", [True, False])
+def test_bitlinear_module_page_harness_shapes(B, rmsnorm):
+    """BitLinearW158A8(128, 256) on x [4, 16, 128] -> [4, 16, 256], the shapes
+    of the page's validation harness ("Functional Validation Harness"): 64
+    tokens through one fused launch, and 130 tokens through the quant +
+    forward path, every output against the oracle."""
+    import torch
+    w, _ = random_case(8200, 1, 256, 128)
+    layer = B.BitLinearW158A8(128, 256, rmsnorm=rmsnorm).load_weight(dev(w))
+    g = host(layer.gamma)[0]
+    assert gamma_agrees(g, w)
+    codes = O.ternary_codes(w, g)
+    for shape in ((4, 16, 128), (2, 65, 128)):
+        _, x = random_case(8201 + shape[1], int(np.prod(shape[:-1])), 1, 128, x_kind="t3")
+        xd = dev(x.reshape(shape))
+        y = layer(xd)
+        assert tuple(y.shape) == shape[:-1] + (256,) and y.dtype == torch.float32
+        yg = host(y).reshape(-1, 256)
+
+        def ref_of(ms):
+            xn = O.rmsnorm(x, None, np.float32(B.NORM_EPS_DEFAULT), ms) if rmsnorm else x
+            oq, os_ = O.quant_act(xn)
+            return O.round_output(O.dequant(O.contract(oq, codes), g, os_), "f32")
+        ms, other = ms_candidates(x)
+        ref = ref_of(ms)
+        for i, alt in enumerate(other):            # either rounding of an ambiguous mean square
+            if rmsnorm and alt is not None:
+                ms2 = ms.copy()
+                ms2[i] = alt
+                r2 = ref_of(ms2)
+                if np.all(np.abs(yg[i] - r2[i]) <= 1e-5 * np.abs(r2[i])):
+                    ref[i] = r2[i]
+        assert_y_close(yg, ref, "f32", f"module {shape}")

@@ -451,3 +451,51 @@ def test_rmsnorm_rejects_bad_eps():
     for bad in (0.0, -1.0, float("nan"), float("inf")):
         with pytest.raises(ValueError):
             O.rmsnorm(np.ones((1, 4), np.float32), None, bad)
+
+
+# ------------------------------------------------------ page-code cross-check --
+def _listing_weight_quant(w):
+    """What the page's WeightQuantFunction.forward computes, in CPU torch
+    (fp32): gamma = mean|W| clamped below at 1e-5, codes = clamp(round(W /
+    gamma), -1, 1).  Returns (codes, gamma)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(w, np.float32))
+    g = t.abs().mean().clamp(min=1e-5)
+    return torch.clamp(torch.round(t / g), -1, 1).to(torch.int8).numpy(), np.float32(g.item())
+
+
+def _listing_act_quant(x):
+    """What the page's quantize_activations_int8 computes, in CPU torch
+    (fp32): beta = max|x| over the last dimension clamped below at 1e-5,
+    x~ = clamp(round(x * (127 / beta)), -128, 127)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32))
+    beta = t.abs().amax(dim=-1, keepdim=True).clamp(min=1e-5)
+    q = torch.clamp(torch.round(t * (127.0 / beta)), -128, 127)
+    return q.to(torch.int8).numpy(), beta[:, 0].numpy()
+
+
+def test_page_code_cross_check():
+    """The page's listing, run with CPU torch, against the oracle in its
+    max(gamma, eps) divisor mode: codes identical given the same gamma (the
+    only freedom is torch.mean's fp32 reduction order, which moves gamma by
+    a few ulp); x~ identical, and 127/beta equal to the oracle's s."""
+    for seed, (n, k) in enumerate([(64, 256), (256, 2560), (640, 2560), (70, 1001)]):
+        w, x = random_case(900 + seed, 6, n, k, x_kind="t3")
+        x[2] = 0.0
+        codes_t, g_t = _listing_weight_quant(w)
+        g_o = O.absmean_gamma(w)
+        assert abs(float(g_t) - float(g_o)) <= 4 * float(np.spacing(g_o))
+        np.testing.assert_array_equal(codes_t, O.ternary_codes(w, g_t, divisor="max"))
+        # the readings part only on weights within a hair of a 0.5 boundary
+        diff = O.ternary_codes(w, g_o) != codes_t
+        assert diff.mean() < 1e-3
+        xq_t, beta_t = _listing_act_quant(x)
+        xq_o, s_o = O.quant_act(x)
+        np.testing.assert_array_equal(xq_t, xq_o)
+        np.testing.assert_array_equal((np.float32(127.0) / beta_t).astype(np.float32), s_o)
+        # the listing's rescale beta*gamma/127 against the oracle's gamma/s
+        acc = O.contract(xq_o, codes_t)
+        y_t = acc.astype(np.float32) * ((beta_t * g_t) / np.float32(127.0))[:, None]
+        y_o = O.dequant(acc, g_t, s_o)
+        np.testing.assert_allclose(y_t, y_o, rtol=1e-6, atol=0)
