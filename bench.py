@@ -596,6 +596,26 @@ def pmc_driver(B, torch, args):
             torch.cuda.synchronize()
         print(json.dumps({"pmc_driver": "prefill", "steps": args.steps}))
         return
+    if args.pmc_driver == "c3":
+        # stack passes at args.m tokens, eager, in the launch configuration
+        # of run_stack_c3
+        wl = datagen.WORKLOADS["c3"]
+        W = Weights(B, torch, wl, copies=wl.layers)
+        X = Inputs(B, torch, W, args.m)
+        ws = B.Workspace()
+        for _ in range(args.steps):
+            for l in range(wl.layers):
+                for grp in LAYER_GROUPS:
+                    if args.m <= 2 or (args.m <= B.BL_FUSED_MAX_M and len(grp) > 1):
+                        fused_call(B, W, X, grp, l, ws)()
+                    else:
+                        g = W.mats[grp[0]]["group"]
+                        X.xq[g], X.s[g] = B.quant_act(X.x[g])
+                        for nm in grp:
+                            forward_call(B, W, X, nm, l, ws)()
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_driver": "c3", "steps": args.steps, "m": args.m}))
+        return
     if args.pmc_driver == "mfma":
         for wlname, m, names in (("c2", 64, ("q", "up", "down")), ("c5", 512, ("k",))):
             W = Weights(B, torch, datagen.WORKLOADS[wlname], names=names)
@@ -759,8 +779,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip every leg after the headline")
     ap.add_argument("--pmc-driver", nargs="?", const="c5gemv",
-                    choices=["c5gemv", "step", "prefill", "mfma"],
+                    choices=["c5gemv", "step", "prefill", "mfma", "c3"],
                     help="only launch what counters or traces are read from")
+    ap.add_argument("--m", type=int, default=64, help="tokens for --pmc-driver c3")
     ap.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSVs")
     ap.add_argument("--name", default="gemv_fused_c5_updown",
                     help="kernel and workload the summaries are named for")
