@@ -38,7 +38,8 @@ Also on the same line:
   c2            batch-1 decode at 2B-class shapes: the six products in one
                 fused launch, and each product's plain GEMV;
   stack_c3      the 2B-class set as a 30-layer stack (388 MB packed, two
-                stack copies alternating), us per pass at 1/8/32/64 tokens;
+                stack copies alternating), one fused launch per input group,
+                us per pass at 1/8/32/64 tokens;
   cpu_baseline  the CPU oracle on the same decode step, on one core and on
                 every core the process may use.
 Per-launch times are median and minimum over >= 20 replays.
@@ -422,10 +423,8 @@ def run_stack_c3(B, torch):
     """The c3 stack: the 2B-class set as 30 layers, each with its own copy of
     the packed weights, and a second copy of the whole stack (776 MB in all),
     the two passes alternating.  One pass = every layer in order: q/k/v (one
-    shared input), o, up (ReLU^2), down, at 1, 8, 32 and 64 tokens.  Each
-    group is one fused decode launch at 1-2 tokens, and at 3-64 tokens when
-    it holds several products; otherwise one activation quant plus one
-    forward per product."""
+    shared input), o, up (ReLU^2), down, at 1, 8, 32 and 64 tokens, each
+    group one fused decode launch (activation quant in the prologue)."""
     import datagen
     wl = datagen.WORKLOADS["c3"]
     W = Weights(B, torch, wl, copies=2 * wl.layers)
@@ -439,18 +438,9 @@ def run_stack_c3(B, torch):
             for l in range(wl.layers):
                 cp = half * wl.layers + l
                 for grp in LAYER_GROUPS:
-                    if m <= 2 or (m <= B.BL_FUSED_MAX_M and len(grp) > 1):
-                        fc = fused_call(B, W, X, grp, cp, ws)
-                        ws.get(fc.nbytes)
-                        calls[half].append(fc)
-                    else:
-                        g = W.mats[grp[0]]["group"]
-                        x = X.x[g]
-                        calls[half].append(lambda x=x, g=g: B._check("quant", B.lib.bitlinear_quant_act(
-                            x.data_ptr(), B.BL_BF16, m, x.shape[1], B.EPS_DEFAULT,
-                            X.xq[g].data_ptr(), X.s[g].data_ptr(), B._stream())))
-                        for nm in grp:
-                            calls[half].append(forward_call(B, W, X, nm, cp, ws))
+                    fc = fused_call(B, W, X, grp, cp, ws)
+                    ws.get(fc.nbytes)
+                    calls[half].append(fc)
         g = capture(torch, lambda: [c() for h in (0, 1) for c in calls[h]])
         ts = replay_times(torch, g, 2, reps=REPS)
         t = stats(ts)
@@ -606,13 +596,7 @@ def pmc_driver(B, torch, args):
         for _ in range(args.steps):
             for l in range(wl.layers):
                 for grp in LAYER_GROUPS:
-                    if args.m <= 2 or (args.m <= B.BL_FUSED_MAX_M and len(grp) > 1):
-                        fused_call(B, W, X, grp, l, ws)()
-                    else:
-                        g = W.mats[grp[0]]["group"]
-                        X.xq[g], X.s[g] = B.quant_act(X.x[g])
-                        for nm in grp:
-                            forward_call(B, W, X, nm, l, ws)()
+                    fused_call(B, W, X, grp, l, ws)()
         torch.cuda.synchronize()
         print(json.dumps({"pmc_driver": "c3", "steps": args.steps, "m": args.m}))
         return
@@ -764,6 +748,22 @@ def summarize(directory, command, name):
                                                "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS",
                                                "SQ_WAIT_INST_ANY", "SQ_BUSY_CYCLES")) + " |")
         out.append((f"{name}_lds_counters.md", "\n".join(lines) + "\n"))
+    if ctrs and not out:
+        # any other counter set: one row per kernel, medians per dispatch
+        cols = sorted(ctrs)
+        kernels = sorted({k for (k, c) in vals})
+        lines = ["# Counters per dispatch (rocprofv3 --pmc)", "",
+                 f"Command: `{command}`", "",
+                 "Medians over the dispatches of each kernel instance.", "",
+                 "| kernel | dispatches | us | " + " | ".join(cols) + " |",
+                 "|---|---|---|" + "---|" * len(cols)]
+        for k in kernels:
+            us = statistics.median(durs[k]) if durs.get(k) else None
+            nd = max(len(xs) for (kk, c), xs in vals.items() if kk == k)
+            lines.append(f"| {k} | {nd} | {f(us, '.2f')} | " +
+                         " | ".join(f(statistics.median(vals[(k, c)]) if (k, c) in vals else None,
+                                      ".6g") for c in cols) + " |")
+        out.append((f"{name}_counters.md", "\n".join(lines) + "\n"))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for fname, text in out:
         with open(os.path.join(ROOT, "profiles", fname), "w") as fh:

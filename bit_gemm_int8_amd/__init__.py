@@ -21,6 +21,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbitlinear.so")
 
 BL_OK = 0
+BL_ERR_INVALID_ARG, BL_ERR_UNSUPPORTED_SHAPE, BL_ERR_MISALIGNED = 1, 2, 3
+BL_ERR_WORKSPACE, BL_ERR_HIP = 4, 5
 BL_F32, BL_BF16 = 0, 1
 BL_EPI_NONE, BL_EPI_RELU2 = 0, 1
 BL_MAX_K = 262144
@@ -39,12 +41,15 @@ EXPORTS = [
     "bitlinear_forward_fused_workspace_bytes", "bitlinear_forward_fused",
     "bitlinear_forward_multi_workspace_bytes", "bitlinear_forward_multi",
     "bitlinear_forward_noalloc", "bitlinear_rmsnorm_quant_act",
+    "bitlinear_forward_kernel", "bitlinear_forward_fused_kernel",
 ]
 NORM_EPS_DEFAULT = 2.0 ** -23       # fp32 machine epsilon, nn.RMSNorm's default
 BL_NOALLOC_SCRATCH_BYTES = 262144
 BL_MAX_FUSED = 16
 BL_FUSED_MAX_M = 64
 BL_MAX_MULTI = 16
+# kernels a call can run (bitlinear_forward_kernel / _fused_kernel)
+KERNEL_NAMES = {0: "dot4_gemv", 1: "gemm", 2: "mfma_gemv", 3: "stream_gemv", 4: "stream_mt"}
 
 
 class BLLinear(ctypes.Structure):
@@ -95,6 +100,8 @@ def _load() -> ctypes.CDLL:
         "bitlinear_forward_multi": (i32, [vp, vp, i64, i64, vp, i32, vp, sz, vp]),
         "bitlinear_forward_noalloc": (i32, [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]),
         "bitlinear_rmsnorm_quant_act": (i32, [vp, i32, i64, i64, vp, f32, f32, vp, vp, vp]),
+        "bitlinear_forward_kernel": (i32, [i64, i64, i64]),
+        "bitlinear_forward_fused_kernel": (i32, [vp, i32, i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -141,6 +148,14 @@ def padded_n(n: int) -> int:
 
 def packed_bytes(n: int, k: int) -> int:
     return int(lib.bitlinear_packed_bytes(n, k))
+
+
+def forward_kernel(m: int, n: int, k: int) -> str:
+    """Name of the kernel bitlinear_forward runs for (m, n, k) (KERNEL_NAMES)."""
+    r = int(lib.bitlinear_forward_kernel(int(m), int(n), int(k)))
+    if r < 0:
+        _check("bitlinear_forward_kernel", -r)
+    return KERNEL_NAMES[r]
 
 
 def forward_workspace_bytes(m: int, n: int, k: int) -> int:
@@ -295,6 +310,13 @@ class FusedStep:
         self.nbytes = int(lib.bitlinear_forward_fused_workspace_bytes(arr, len(ops), self.m))
         self.ws = workspace or Workspace(ops[0]["x"].device)
         self.ws.get(self.nbytes)
+
+    def kernel(self) -> str:
+        """Name of the kernel this step launches (KERNEL_NAMES)."""
+        r = int(lib.bitlinear_forward_fused_kernel(self.arr, len(self.ops), self.m))
+        if r < 0:
+            _check("bitlinear_forward_fused_kernel", -r)
+        return KERNEL_NAMES[r]
 
     def __call__(self, stream=None):
         ws = self.ws.get(self.nbytes, stream)

@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "libbitlinear.so")
-SOURCES = ["api.hip", "quant_act.hip", "pack.hip", "gemv.hip", "gemv_stream.hip", "gemv_mfma.hip",
+SOURCES = ["api.hip", "quant_act.hip", "pack.hip", "gemv.hip", "gemv_stream.hip", "gemv_stream_mt.hip",
+           "gemv_mfma.hip",
            "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -34,6 +34,7 @@ constexpr int64_t kGemvMaxLds = 48 * 1024;
 constexpr int64_t kCUs = 256;
 constexpr int64_t kStreamMinSubs = 64;      // stream GEMV from 1024 rows
 constexpr size_t kStreamMaxLds = 64 * 1024;
+constexpr size_t kMtMaxLds = 160 * 1024;     // a workgroup's LDS on gfx950
 
 }  // namespace
 
@@ -43,6 +44,39 @@ hipError_t launch_fill_zero(uint32_t* p, size_t words, hipStream_t stream) {
   if (blocks > 4096) blocks = 4096;
   fill_zero_kernel<<<(unsigned)blocks, 256, 0, stream>>>(p, words);
   return hipGetLastError();
+}
+
+// Row ranges of the multi-token streaming GEMV: about one workgroup per CU
+// over the ceil(m / 16) token blocks, a multiple of 8 when there are several
+// blocks (so a row range's blocks share an XCD), at most one per sub-block.
+static int64_t mt_row_ranges(int64_t m, int64_t subs) {
+  const int64_t tb = cdiv(m, 16);
+  int64_t p = kCUs / tb;
+  if (p < 1) p = 1;
+  if (tb > 1 && p >= 8) p -= p % 8;
+  return p < subs ? p : subs;
+}
+
+// The multi-token streaming GEMV for long rows (>= 32 super-chunks) of
+// matrices with few row blocks: past 32 tokens up to 128 row blocks, past 16
+// tokens up to 16, when x~ of a 16-token block and the sums of a row range
+// fit a workgroup's LDS.  Elsewhere the windowed MFMA GEMV measured faster:
+// the streaming kernel stages all of its block's x~ before the first MFMA,
+// which only pays when every row is long and there are few row ranges to
+// feed (MI355X, 100B- and 2B-class shapes at 8 to 64 tokens: 100B q at 64
+// tokens 14.8 -> 12.9 us, k/v at 32-64 tokens 7.6 -> 6.7 us).
+static bool mt_plan(int64_t m, int64_t n, int64_t k, FwdPlan* p) {
+  const int64_t nb = cdiv(n, kRowBlock);
+  const int64_t subs = nb * 4;
+  const int64_t nc = cdiv(k, kSuperK);
+  if (nc < 32 || !((m > 32 && nb <= 128) || (m > 16 && nb <= 16))) return false;
+  const int64_t P = mt_row_ranges(m, subs);
+  if (stream_mt_lds_bytes(m, nc, (int)cdiv(subs, P)) > kMtMaxLds) return false;
+  p->kind = 4;
+  p->qpl = (int)P;
+  p->splits = 1;
+  p->slots = 0;
+  return true;
 }
 
 FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
@@ -100,6 +134,8 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
         p.slots = 0;
       }
     }
+  } else if (m <= kMfmaGemvMaxM && mt_plan(m, n, k, &p)) {
+    // multi-token streaming GEMV (below)
   } else if (m <= kMfmaGemvMaxM) {
     // Windowed MFMA GEMV: 16, 32 or 64 token columns.  Many row blocks
     // (>= 256): wide row groups, the whole K per wave; fewer: slices of K
@@ -162,6 +198,9 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
   if (plan.kind == 3)
     return launch_gemv_stream((int)m, xq, scale, packed, gamma, n, k, plan.qpl, relu2, bf16, y,
                               acc_out, stream);
+  if (plan.kind == 4)
+    return launch_gemv_stream_mt(xq, scale, packed, gamma, m, n, k, plan.qpl, relu2, bf16, y,
+                                 acc_out, stream);
   if (plan.kind == 2)
     return launch_gemv_mfma(plan.variant, xq, scale, packed, gamma, m, n, k, relu2, bf16, y,
                             acc_out, stream);
@@ -176,6 +215,7 @@ struct FusedPlan {
   int xr = 0;                           // its activation units per thread and token
   int nsub_alloc = 0;                   // its sub-blocks per workgroup, at most
   int64_t nc_max = 0;
+  bool mt = false;                      // the multi-token streaming kernel
   bool mfma = false;                    // 3..64 tokens: the fused MFMA kernel
   int variant = 0;                      // its wave layout
   int waves = 8;
@@ -250,6 +290,72 @@ static bool stream_fused_plan(const bl_linear* ops, int nops, int64_t m, bool no
   return true;
 }
 
+// The fused step on the multi-token streaming kernel (faster than the fused
+// windowed kernel on every 2B- and 100B-class shape measured at 8 to 64
+// tokens on MI355X, e.g. 100B q/k/v at 64 tokens 49.9 -> 21.8 us, 2B q/k/v
+// 11.6 -> 8.9 us): every entry's rows
+// whole aligned 16-byte units of one activation dtype, a token's row within
+// 16 units per lane (bf16 K <= 8192, fp32 K <= 4096), and x~ of a 16-token
+// block plus the sums within the LDS.  Row ranges are shared out in
+// proportion to each entry's packed bytes, about one workgroup per CU over
+// the token blocks, each entry at least one and at most one per sub-block,
+// multiples of 8 when there are several token blocks.
+static bool mt_fused_plan(const bl_linear* ops, int nops, int64_t m, bool norm, FusedPlan* p) {
+  const int xdt = ops[0].x_dtype;
+  int64_t units = 0, nc_max = 0, nu_max = 0;
+  for (int i = 0; i < nops; ++i) {
+    const int64_t esize = ops[i].x_dtype == BL_BF16 ? 2 : 4;
+    if (ops[i].x_dtype != xdt || (ops[i].k * esize) % 16 != 0 || ((uintptr_t)ops[i].x % 16) != 0)
+      return false;
+    const int64_t nc = cdiv(ops[i].k, kSuperK);
+    units += cdiv(ops[i].n, kRowBlock) * 4 * nc;
+    if (nc > nc_max) nc_max = nc;
+    const int64_t nu = ops[i].k * esize / 16;
+    if (nu > nu_max) nu_max = nu;
+  }
+  const int64_t xr = cdiv(nu_max, 64);
+  if (xr > 16) return false;
+  const int64_t tb = cdiv(m, 16);
+  const int64_t budget = (kCUs / tb) < 1 ? 1 : kCUs / tb;
+  const int64_t step = tb > 1 ? 8 : 1;
+  int64_t ps[kMaxFused], total = 0;
+  for (int i = 0; i < nops; ++i) {
+    const int64_t subs = cdiv(ops[i].n, kRowBlock) * 4;
+    const int64_t w = subs * cdiv(ops[i].k, kSuperK);
+    int64_t pi = (budget * w + units / 2) / units;
+    if (pi >= step) pi -= pi % step;
+    ps[i] = pi < 1 ? 1 : pi > subs ? subs : pi;
+    total += ps[i];
+  }
+  while (total > budget) {
+    int big = 0;
+    for (int i = 1; i < nops; ++i) big = ps[i] > ps[big] ? i : big;
+    const int64_t dec = ps[big] > step ? step : ps[big] - 1;
+    if (dec <= 0) break;
+    ps[big] -= dec;
+    total -= dec;
+  }
+  int groups = 0, nsub_alloc = 1;
+  for (int i = 0; i < nops; ++i) {
+    const int64_t subs = cdiv(ops[i].n, kRowBlock) * 4;
+    p->splits[i] = (int)(ps[i] * tb);
+    groups += p->splits[i];
+    const int spw = (int)cdiv(subs, ps[i]);
+    if (spw > nsub_alloc) nsub_alloc = spw;
+  }
+  const size_t lds = stream_mt_lds_bytes(m, nc_max, nsub_alloc);
+  if (lds > kMtMaxLds) return false;
+  p->mt = true;
+  p->norm = norm;
+  p->xr = (int)xr;
+  p->nsub_alloc = nsub_alloc;
+  p->nc_max = nc_max;
+  p->groups = groups;
+  p->lds = lds;
+  p->ws_bytes = 0;
+  return true;
+}
+
 FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   // T = super-chunks a workgroup should stream: the set's total over ~512
   // groups, kept within [8, 32].  Entries with up to 2T super-chunks keep
@@ -268,6 +374,7 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   bool norm = false;
   for (int i = 0; i < nops; ++i) norm = norm || ops[i].rmsnorm != 0;
   if (m <= 2 && stream_fused_plan(ops, nops, m, norm, &p)) return p;
+  if ((m >= 3 || norm) && m <= BL_FUSED_MAX_M && mt_fused_plan(ops, nops, m, norm, &p)) return p;
   // RMSNorm tables the streaming kernel does not take run on the matrix-core
   // fused kernel at any token count
   p.norm = norm;
@@ -450,9 +557,9 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
     sg.norm_weight = o.norm_weight;
     sg.norm_eps = o.norm_eps;
     args.wg_begin[i] = begin;
-    if (sg.splits > 1 && !plan.stream)
+    if (sg.splits > 1 && !plan.stream && !plan.mt)
       sg.slots = reinterpret_cast<int64_t*>(reinterpret_cast<char*>(workspace) + plan.slot_off[i]);
-    begin += plan.stream ? sg.splits
+    begin += plan.stream || plan.mt ? sg.splits
              : plan.mfma ? (int)cdiv(cdiv(o.n, kRowBlock) * 4, plan.variant == 0 ? 2 : 8)
                          : (int)(cdiv(o.n, kRowBlock) * (4 / plan.qpl) * sg.splits);
   }
@@ -462,6 +569,13 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
                                                   ops[0].x_dtype == BL_BF16, plan.norm, plan.xr,
                                                   begin, plan.lds,
                                                   reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? BL_OK : BL_ERR_HIP;
+  }
+  if (plan.mt) {
+    args.nsub_alloc = plan.nsub_alloc;
+    const hipError_t e = launch_gemv_stream_mt_fused(args, (int)m, ops[0].x_dtype == BL_BF16,
+                                                     plan.norm, plan.xr, begin, plan.lds,
+                                                     reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? BL_OK : BL_ERR_HIP;
   }
   if (plan.mfma) {
@@ -483,6 +597,31 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
                                          plan.groups, plan.lds,
                                          reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? BL_OK : BL_ERR_HIP;
+}
+
+int bitlinear_forward_kernel(int64_t m, int64_t n, int64_t k) {
+  if (m < 1 || n < 1 || k < 1) return -BL_ERR_INVALID_ARG;
+  if (m > BL_MAX_MN || n > BL_MAX_MN || k > BL_MAX_K) return -BL_ERR_UNSUPPORTED_SHAPE;
+  const FwdPlan p = forward_plan(m, n, k);
+  switch (p.kind) {
+    case 0: return BL_KERNEL_DOT4_GEMV;
+    case 1: return BL_KERNEL_GEMM;
+    case 2: return BL_KERNEL_MFMA_GEMV;
+    case 3: return BL_KERNEL_STREAM_GEMV;
+    default: return BL_KERNEL_STREAM_MT;
+  }
+}
+
+int bitlinear_forward_fused_kernel(const bl_linear* ops, int nops, int64_t m) {
+  const bl_status st = check_fused(ops, nops, m);
+  if (st != BL_OK) return -(int)st;
+  if (m < 1) return -BL_ERR_INVALID_ARG;
+  const FusedPlan p = fused_plan(ops, nops, m);
+  if (p.unsupported) return -BL_ERR_UNSUPPORTED_SHAPE;
+  if (p.stream) return BL_KERNEL_STREAM_GEMV;
+  if (p.mt) return BL_KERNEL_STREAM_MT;
+  if (p.mfma) return BL_KERNEL_MFMA_GEMV;
+  return BL_KERNEL_DOT4_GEMV;
 }
 
 bl_status bitlinear_workspace_init(void* workspace, size_t bytes, void* stream) {

@@ -31,11 +31,12 @@ hipError_t launch_pack(const void* w, bool bf16, int64_t n, int64_t k, float eps
 
 // Forward: dispatch plan shared by the workspace query and the launch.
 struct FwdPlan {
-  int kind;            // 0 = dot4 GEMV, 1 = MFMA GEMM, 2 = MFMA GEMV, 3 = stream GEMV
+  int kind;            // 0 = dot4 GEMV, 1 = MFMA GEMM, 2 = MFMA GEMV, 3 = stream GEMV,
+                       // 4 = multi-token stream GEMV
   int variant;         // dot4 GEMV: waves per workgroup; otherwise the kernel variant
   int pf;              // GEMV: super-chunks in flight per wave
   int qpl;             // GEMV: 16-byte q-parts per lane (4: 64 rows per group, 1: 16 rows);
-                       // stream GEMV: workgroups
+                       // stream GEMV: workgroups; multi-token stream GEMV: row ranges
   int splits;          // split-K factor
   size_t slots;        // 64-bit split-K slots in the workspace (splits > 1)
   size_t ws_bytes;     // total workspace bytes
@@ -118,6 +119,17 @@ hipError_t launch_gemv_stream(int m, const int8_t* xq, const float* scale,
 hipError_t launch_gemv_stream_fused(const FusedArgs& args, int m, int64_t nc_max, bool x_bf16,
                                     bool norm, int xr, int groups, size_t lds,
                                     hipStream_t stream);
+
+// Multi-token streaming GEMV on the matrix cores (x~ of a block of up to 16
+// tokens in LDS, whole 16-row sub-blocks per row range, P row ranges x
+// ceil(m / 16) token blocks of workgroups).
+size_t stream_mt_lds_bytes(int64_t m, int64_t nc, int nsub_alloc);
+hipError_t launch_gemv_stream_mt(const int8_t* xq, const float* scale, const uint32_t* packed,
+                                 const float* gamma, int64_t m, int64_t n, int64_t k, int P,
+                                 bool relu2, bool bf16, void* y, int32_t* acc_out,
+                                 hipStream_t stream);
+hipError_t launch_gemv_stream_mt_fused(const FusedArgs& args, int m, bool x_bf16, bool norm,
+                                       int xr, int groups, size_t lds, hipStream_t stream);
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t padded_n(int64_t n) { return 64 * cdiv(n, 64); }

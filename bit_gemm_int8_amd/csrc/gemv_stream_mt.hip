@@ -1,0 +1,600 @@
+// Decode products for 3 to 64 tokens (and larger batches whose outputs are
+// few) on the int8 matrix cores: the streaming GEMV of whole 16-row
+// sub-blocks, with x~ of a block of up to 16 tokens in LDS; plain (x~ and s
+// given) and fused (the activation quantization in the prologue, for a
+// table of products).
+//
+// "BitNet b1.58 2B4T Guide: Scaling Native 1-Bit LLMs", section "Matrix
+// Multiplication as Pure Integer Addition": acc = x~ W~^T in an integer
+// accumulator, y = acc * gamma / s; section "8-Bit Activation Quantization:
+// absmax Scaling" for x~ and s.
+//
+// v_mfma_i32_16x16x64_i8 has 16 result columns, so one instruction per
+// packed word serves 16 tokens as easily as one: the weight stream of the
+// one/two-token kernel carries over and the second operand becomes x~ of 16
+// real tokens.  The work of a product is cut into (row range, token block):
+//   - token block b holds tokens 16 b .. 16 b + 15 (fewer in the last); its
+//     x~ (all of K) sits in LDS, 16-byte unit q of token t's row at
+//     q ^ (t % 16), so the 16 tokens of one operand read fall on 16
+//     different bank groups;
+//   - a row range is whole 16-row sub-blocks over all of K (no K split: no
+//     workspace, no atomics in memory), its 1 KiB units cut into one
+//     contiguous run per wave, D units in flight per wave;
+//   - the token blocks of one row range run on one XCD (workgroup w of a
+//     launch runs on XCD w % 8), so after one block has read a weight from
+//     HBM the others find it in that XCD's L2.
+// Every workgroup reads its block's whole x~ (fused: its activations), so
+// more row ranges fill the chip better and re-read more; the plans take
+// about one workgroup per CU.
+#include <climits>
+
+#include "bl_device.h"
+#include "bl_internal.h"
+
+namespace bl {
+namespace {
+
+constexpr int kTokBlock = 16;
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+// Word 3 of a raw buffer resource on gfx9 (untyped 32-bit data; loads past
+// num_records return zero).
+constexpr int kBufferDword3 = 0x00020000;
+
+// (row range, token block) of workgroup w of a product with P row ranges and
+// TB token blocks.  With P a multiple of 8, the TB workgroups of a row range
+// are w = 8 TB a + 8 b + (p % 8), all on XCD p % 8.
+struct MtWork {
+  int p, tb;
+};
+__device__ __forceinline__ MtWork mt_work(int w, int P, int TB) {
+  if (TB == 1) return {w, 0};
+  if ((P & 7) == 0) return {(w / (8 * TB)) * 8 + (w & 7), (w >> 3) % TB};
+  return {w % P, w / P};
+}
+
+// Wave cursor over 1 KiB units: unit v is sub-block tl, super-chunk cl;
+// loads past the wave's last unit repeat it (no branch around the loads).
+struct MtCursor {
+  const uint4* base;
+  int vl, tl, cl, ulast;
+};
+
+__device__ __forceinline__ const uint4* mt_sub_base(const uint4* packed, int nc, int t, int g,
+                                                    int r) {
+  return packed + ((int64_t)(t >> 2) * nc * 4 + g) * 64 + (t & 3) * 16 + r;
+}
+
+__device__ __forceinline__ MtCursor mt_cursor(const uint4* packed, int nc, int t0, int u0, int u1,
+                                              int g, int r) {
+  MtCursor c;
+  c.ulast = u1 > 0 ? u1 - 1 : 0;
+  c.vl = min(u0, c.ulast);
+  c.tl = t0 + c.vl / nc;
+  c.cl = c.vl - (c.vl / nc) * nc;
+  c.base = mt_sub_base(packed, nc, c.tl, g, r);
+  return c;
+}
+
+__device__ __forceinline__ void mt_next(MtCursor& c, const uint4* packed, int nc, int g, int r) {
+  if (c.vl < c.ulast) {
+    ++c.vl;
+    if (++c.cl == nc) {
+      c.cl = 0;
+      ++c.tl;
+      c.base = mt_sub_base(packed, nc, c.tl, g, r);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void mt_prefetch(uint4 (&buf)[D], MtCursor& cur, const uint4* packed,
+                                            int nc, int g, int r) {
+  static_for<D>([&](auto P) {
+    buf[(int)P] = load_stream16(cur.base + (int64_t)cur.cl * kBlockU4);
+    mt_next(cur, packed, nc, g, r);
+  });
+}
+
+// Stream units [u0, u1) (sub-blocks from t0, nc super-chunks each; the first
+// D already in buf) and add each sub-block's sums into
+// sums[sub - t0][token][row].  Lane (r, g): token min(r, mb - 1) as the
+// second operand (columns of tokens >= mb are dropped), inputs 64 j + 16 g
+// .. + 15 of super-chunk cc, i.e. x~ unit 16 cc + ((4 j + g) ^ token).
+template <int D>
+__device__ __forceinline__ void mt_stream(uint4 (&buf)[D], MtCursor& cur, const uint4* packed,
+                                          int nc, int t0, int u0, int u1, int g, int r, int mb,
+                                          const uint4* xs, int kp16, int* sums) {
+  const int tr = min(r, mb - 1);
+  const uint4* xrow = xs + tr * kp16;
+  bl_v4i acc = {0, 0, 0, 0};
+  int tc = t0 + u0 / nc, cc = u0 - (u0 / nc) * nc;
+  auto flush = [&]() __attribute__((always_inline)) {
+    if (r < mb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        atomicAdd(&sums[((tc - t0) * kTokBlock + r) * 16 + 4 * g + i], acc[i]);
+    }
+    acc = bl_v4i{0, 0, 0, 0};
+  };
+  auto consume = [&](const uint4& w) __attribute__((always_inline)) {
+    const uint32_t wj[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 x4 = xrow[cc * 16 + ((4 * j + g) ^ tr)];
+      const bl_v4i xv = {(int)x4.x, (int)x4.y, (int)x4.z, (int)x4.w};
+      const bl_v4i a = {(int)unpack_x64(wj[j], 0), (int)unpack_x64(wj[j], 1),
+                        (int)unpack_x64(wj[j], 2), (int)unpack_x64(wj[j], 3)};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xv, acc, 0, 0, 0);
+    }
+    if (++cc == nc) {
+      flush();
+      cc = 0;
+      ++tc;
+    }
+  };
+  int v = u0;
+  for (; v + D <= u1; v += D) {
+    static_for<D>([&](auto P) {
+      constexpr int p = decltype(P)::value;
+      consume(buf[p]);
+      buf[p] = load_stream16(cur.base + (int64_t)cur.cl * kBlockU4);
+      mt_next(cur, packed, nc, g, r);
+    });
+  }
+  static_for<D>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    if (v + p < u1) consume(buf[p]);
+  });
+  if (u1 > u0 && cc != 0) flush();
+}
+
+// Outputs of sub-blocks t0 .. t0 + nsub - 1 for tokens tok0 .. tok0 + mb - 1
+// from the LDS sums (64 * acc, exact), four consecutive rows per thread.
+__device__ __forceinline__ void mt_epilogue(const int* sums, const float* fac, int t0, int nsub,
+                                            int mb, int tok0, int n, bool relu2, bool ybf16,
+                                            bool vec, void* y, int32_t* acc_out, int nt) {
+  const int quads = nsub * 4;
+  for (int i = threadIdx.x; i < quads * mb; i += nt) {
+    const int m = i / quads, qd = i - m * quads;
+    const int sub = qd >> 2, rr = (qd & 3) * 4;
+    const int row0 = (t0 + sub) * 16 + rr;
+    if (row0 >= n) continue;
+    const bl_v4i a4 = *reinterpret_cast<const bl_v4i*>(sums + (sub * kTokBlock + m) * 16 + rr);
+    const float f = fac[m];
+    const int64_t idx = (int64_t)(tok0 + m) * n + row0;
+    int v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = a4[e] >> 6;
+    if (vec && row0 + 3 < n) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = (float)v[e] * f;
+        if (relu2) o[e] = o[e] > 0.0f ? o[e] * o[e] : 0.0f;
+      }
+      if (acc_out != nullptr)
+        *reinterpret_cast<int4*>(acc_out + idx) = make_int4(v[0], v[1], v[2], v[3]);
+      if (ybf16)
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + idx) =
+            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+      else
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + idx) =
+            make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (row0 + e >= n) continue;
+        if (acc_out != nullptr) acc_out[idx + e] = v[e];
+        store_out(y, idx + e, v[e], f, relu2, ybf16);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ plain GEMV --
+// x~ [m][K_pad] and s given.  LDS: x~ [mba][kp16] uint4 (mba = min(16, m)
+// rows, swizzled), sums [nsub_alloc][16][16] int, fac [16] float.
+template <int WAVES, int D, int XR>
+__global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ scale,
+    const uint4* __restrict__ packed, const float* __restrict__ gamma, int m, int n, int nc,
+    int S, int P, int TB, int nsub_alloc, int mba, int relu2, int ybf16, int vec_out,
+    void* __restrict__ y, int32_t* __restrict__ acc_out) {
+  constexpr int NT = 64 * WAVES;
+  extern __shared__ uint4 lds[];
+  const MtWork wk = mt_work((int)blockIdx.x, P, TB);
+  const int tok0 = kTokBlock * wk.tb;
+  const int mb = min(kTokBlock, m - tok0);
+  const int t0 = (int)((int64_t)S * wk.p / P), t1 = (int)((int64_t)S * (wk.p + 1) / P);
+  const int nsub = t1 - t0, units = nsub * nc;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int kp16 = nc * 16;
+  const int u0 = (int)((int64_t)units * wave / WAVES);
+  const int u1 = (int)((int64_t)units * (wave + 1) / WAVES);
+  int* sums = reinterpret_cast<int*>(lds + mba * kp16);
+  float* fac = reinterpret_cast<float*>(sums + nsub_alloc * kTokBlock * 16);
+
+  // x~ of the block first (loads retire in issue order), clamped so no load
+  // sits behind a branch
+  const int xu = mb * kp16;
+  const uint4* xg = reinterpret_cast<const uint4*>(xq) + (int64_t)tok0 * kp16;
+  uint4 xr[XR];
+#pragma unroll
+  for (int j = 0; j < XR; ++j) xr[j] = xg[min((int)threadIdx.x + NT * j, xu - 1)];
+  uint4 buf[D];
+  MtCursor cur = mt_cursor(packed, nc, t0, u0, u1, g, r);
+  mt_prefetch<D>(buf, cur, packed, nc, g, r);
+  const float gm = *gamma;
+  if ((int)threadIdx.x < mb) fac[threadIdx.x] = gamma_over_s(gm, scale[tok0 + threadIdx.x]);
+  for (int i = threadIdx.x; i < nsub * kTokBlock * 16; i += NT) sums[i] = 0;
+#pragma unroll
+  for (int j = 0; j < XR; ++j) {
+    const int i = (int)threadIdx.x + NT * j;
+    if (i < xu) {
+      const int t = i / kp16, q = i - t * kp16;
+      lds[t * kp16 + (q ^ (t & 15))] = xr[j];
+    }
+  }
+  for (int i = (int)threadIdx.x + NT * XR; i < xu; i += NT) {
+    const int t = i / kp16, q = i - t * kp16;
+    lds[t * kp16 + (q ^ (t & 15))] = xg[i];
+  }
+  __syncthreads();
+
+  mt_stream<D>(buf, cur, packed, nc, t0, u0, u1, g, r, mb, lds, kp16, sums);
+  __syncthreads();
+  mt_epilogue(sums, fac, t0, nsub, mb, tok0, n, relu2 != 0, ybf16 != 0, vec_out != 0, y,
+              acc_out, NT);
+}
+
+// ----------------------------------------------------- fused decode step --
+// A table of products sharing the tokens (FusedArgs; `splits` of an entry
+// holds its workgroup count, P row ranges x TB token blocks).  A workgroup
+// quantizes its block's activation rows into LDS, one wave per token:
+//   1. the token's row is loaded (XR 16-byte units per lane, clamped: units
+//      past the row repeat the last, which the max ignores), then the first
+//      D weight units;
+//   2. with RMSNorm (entries flagged for it; the BitLinear listing of
+//      "End-to-End Implementation: Building a Native BitLinear Layer"
+//      applies nn.RMSNorm before quantize_activations_int8): the fp64 sum of
+//      squares in a fixed order (lanes, then the xor butterfly),
+//      r = rms_factor(sum, K, eps), and y = fp32(fp32(x * r) * w) replaces
+//      x below; these rows are read in three passes, four units per lane
+//      at a time (from the caches after the first), with the gain;
+//   3. beta = max|x| (sign-cleared fp32 bits, a wave max) and
+//      s = fp32(127 / max(beta, eps)) exactly as bitlinear_quant_act;
+//   4. x~ = clamp(rint(fp32(x * s))) (quant_mt4) into LDS, zero past K; the
+//      entry's first row range also writes x~ and s out when asked.
+// Rows must be whole 16-byte units at 16-byte alignment (checked on the host).
+//
+// quant_mt4 leaves out the clamp, which this prologue costs a VALU operation
+// per element (every workgroup quantizes its block's whole rows): for finite
+// inputs it never binds.  With b = max(beta, eps) >= |x| and s = fp32(127 / b)
+// <= (127 / b)(1 + 2^-24), |x s| <= 127 (1 + 2^-24), whose fp32 rounding is at
+// most 127 + 2^-17, so rint gives at most 127 in magnitude.  Adding 1.5 * 2^23
+// rounds a product of magnitude below 2^22 to the nearest integer, ties to
+// even, in the low mantissa bits; three v_perm pack the low bytes.
+__device__ __forceinline__ uint32_t quant_mt4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                              float s) {
+  // the product must be rounded to fp32 before the rounding add: contracted
+  // into one fma, rint would see the exact product (__fmul_rn is a plain
+  // multiply here, and device code contracts by default)
+#pragma clang fp contract(off)
+  uint32_t q[4] = {a, b, c, d};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    q[i] = __float_as_uint(__fmul_rn(__uint_as_float(q[i]), s) + 12582912.0f);
+  const uint32_t lo = __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+template <int WAVES, int D, int XR, bool BF16, bool NORM>
+__global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
+    int m_all, int nseg, int wb1, int wb2, int wb3, int wb4, int wb5, int wb6, int wb7, int wb8,
+    int wb9, int wb10, int wb11, int wb12, FusedArgs args) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int EPU = BF16 ? 8 : 4;                  // activations per 16-byte unit
+  extern __shared__ uint4 lds[];
+  const int bid = (int)blockIdx.x;
+  const int wb[12] = {wb1, wb2, wb3, wb4, wb5, wb6, wb7, wb8, wb9, wb10, wb11, wb12};
+  int si = 0;
+#pragma unroll
+  for (int i = 0; i < 12; ++i) si = bid >= wb[i] ? i + 1 : si;
+  if (nseg > 13) {
+#pragma unroll
+    for (int i = 13; i < kMaxFused; ++i)
+      if (i < nseg && bid >= args.wg_begin[i]) si = i;
+  }
+  const FusedSeg& sg = args.seg[si];
+  const int TB = (m_all + kTokBlock - 1) / kTokBlock;
+  const int P = sg.splits / TB;
+  const MtWork wk = mt_work(bid - sg.wg_begin, P, TB);
+  const int tok0 = kTokBlock * wk.tb;
+  const int mb = min(kTokBlock, m_all - tok0);
+  const int mba = min(kTokBlock, m_all);
+  const int nc = sg.nc, n = sg.n, k = sg.k;
+  const int S = ((n + kRowBlock - 1) / kRowBlock) * 4;
+  const int t0 = (int)((int64_t)S * wk.p / P), t1 = (int)((int64_t)S * (wk.p + 1) / P);
+  const int nsub = t1 - t0, units = nsub * nc;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int kp16 = nc * 16;
+  const int u0 = (int)((int64_t)units * wave / WAVES);
+  const int u1 = (int)((int64_t)units * (wave + 1) / WAVES);
+  int* sums = reinterpret_cast<int*>(lds + mba * kp16);
+  float* fac = reinterpret_cast<float*>(sums + args.nsub_alloc * kTokBlock * 16);
+  const uint4* packed = reinterpret_cast<const uint4*>(sg.packed);
+  const int nu = k / EPU;                             // units per row (whole units)
+  const bool nrm = NORM && sg.rmsnorm();
+  const uint4* gw = reinterpret_cast<const uint4*>(sg.norm_weight);
+  const bool have_w = nrm && gw != nullptr;
+  const bool first = wk.p == 0;
+
+  // 1. this wave's first token (waves past the block load its last token
+  //    again: no load behind a branch), then the weights
+  //    (a buffer load past the row's nu units returns zeros, which the max
+  //    ignores and which are never stored; the whole offset is in the
+  //    range-checked vector offset)
+  auto load_row = [&](int t, uint4 (&xr)[XR]) __attribute__((always_inline)) {
+    const uint4* row = reinterpret_cast<const uint4*>(sg.x) + (int64_t)(tok0 + t) * nu;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(row), 0, nu * 16, kBufferDword3);
+#pragma unroll
+    for (int j = 0; j < XR; ++j) {
+      const bl_v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + j * 1024, 0, 0);
+      xr[j] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+    }
+  };
+  uint4 xr[XR];
+  load_row(min(wave, mb - 1), xr);
+  uint4 buf[D];
+  MtCursor cur = mt_cursor(packed, nc, t0, u0, u1, g, r);
+  mt_prefetch<D>(buf, cur, packed, nc, g, r);
+  const float gm = *sg.gamma;
+  for (int i = threadIdx.x; i < nsub * kTokBlock * 16; i += NT) sums[i] = 0;
+
+  // the EPU values of a 16-byte activation unit as fp32 bit patterns
+  auto expand = [&](const uint4& x, uint32_t (&v)[8]) __attribute__((always_inline)) {
+    if (BF16) {
+      v[0] = x.x << 16; v[1] = x.x & 0xFFFF0000u; v[2] = x.y << 16; v[3] = x.y & 0xFFFF0000u;
+      v[4] = x.z << 16; v[5] = x.z & 0xFFFF0000u; v[6] = x.w << 16; v[7] = x.w & 0xFFFF0000u;
+    } else {
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    }
+  };
+  // running max of |value| over units: sign-cleared bits compare as
+  // magnitudes; bf16 pairs as two 16-bit lanes (v_pk_max_u16), widened to
+  // fp32 bits at the end (the top half of an fp32 is its bf16)
+  auto unit_max = [&](u16x2& m16, uint32_t& m32, const uint4& x) __attribute__((always_inline)) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (BF16)
+        m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(u16x2, w[e] & 0x7FFF7FFFu));
+      else
+        m32 = max(m32, w[e] & 0x7FFFFFFFu);
+    }
+  };
+  auto max_bits = [&](const u16x2& m16, uint32_t m32) __attribute__((always_inline)) {
+    return BF16 ? (uint32_t)max(m16[0], m16[1]) << 16 : m32;
+  };
+  // x~ of unit u (values v) into the token's LDS row (swizzled) and out
+  uint32_t* xw = reinterpret_cast<uint32_t*>(lds);
+  const int64_t kpad = (int64_t)kp16 * 16;
+  auto put = [&](int t, int u, const uint32_t (&v)[8], float sv, uint32_t* rowo)
+      __attribute__((always_inline)) {
+    uint32_t* rowl = xw + t * kp16 * 4;
+    if (BF16) {
+      const uint32_t d0 = quant_mt4(v[0], v[1], v[2], v[3], sv);
+      const uint32_t d1 = quant_mt4(v[4], v[5], v[6], v[7], sv);
+      const int q = u >> 1;                           // x~ unit, half u & 1
+      *reinterpret_cast<uint2*>(rowl + ((q ^ t) << 2) + ((u & 1) << 1)) = make_uint2(d0, d1);
+      if (rowo != nullptr) *reinterpret_cast<uint2*>(rowo + 2 * u) = make_uint2(d0, d1);
+    } else {
+      const uint32_t d0 = quant_mt4(v[0], v[1], v[2], v[3], sv);
+      const int q = u >> 2;
+      rowl[((q ^ t) << 2) + (u & 3)] = d0;
+      if (rowo != nullptr) rowo[u] = d0;
+    }
+  };
+  // y = (x r) w of unit u (RMSNorm), gains from the caches
+  auto normed = [&](const uint4& x, int u, float rn, uint32_t (&v)[8])
+      __attribute__((always_inline)) {
+    expand(x, v);
+    uint32_t wv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (have_w) {
+      const uint4 w0 = gw[u * (EPU / 4)];
+      wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
+      if (BF16) {
+        const uint4 w1 = gw[u * (EPU / 4) + 1];
+        wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) {
+      const float w = have_w ? __uint_as_float(wv[e]) : 1.0f;
+      v[e] = __float_as_uint(rms_apply(__uint_as_float(v[e]), rn, w));
+    }
+  };
+
+  for (int t = wave; t < mb; t += WAVES) {
+    const bool out = first && sg.xq_out != nullptr;
+    uint32_t* rowo = out ? reinterpret_cast<uint32_t*>(sg.xq_out + (int64_t)(tok0 + t) * kpad)
+                         : nullptr;
+    float sv;
+    if (NORM && nrm) {
+      // 2-4 with RMSNorm: three passes over the row (from the caches), four
+      // units per lane at a time
+      const uint4* row = reinterpret_cast<const uint4*>(sg.x) + (int64_t)(tok0 + t) * nu;
+      double ss = 0.0;
+      for (int ub = 0; ub < nu; ub += 256) {
+        uint4 xv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xv[c] = row[min(ub + lane + 64 * c, nu - 1)];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (ub + lane + 64 * c < nu) {
+            uint32_t v[8];
+            expand(xv[c], v);
+#pragma unroll
+            for (int e = 0; e < EPU; ++e) {
+              const double d = (double)__uint_as_float(v[e]);
+              ss += d * d;
+            }
+          }
+        }
+      }
+      const float rn = rms_factor(wave_sum_f64(ss), k, sg.norm_eps);
+      uint32_t mx = 0;
+      for (int ub = 0; ub < nu; ub += 256) {
+        uint4 xv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xv[c] = row[min(ub + lane + 64 * c, nu - 1)];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint32_t v[8];
+          normed(xv[c], min(ub + lane + 64 * c, nu - 1), rn, v);
+#pragma unroll
+          for (int e = 0; e < EPU; ++e) mx = max(mx, v[e] & 0x7FFFFFFFu);
+        }
+      }
+      mx = wave_max_u32(mx);
+      sv = (float)(127.0 / (double)fmaxf(__uint_as_float(mx), args.eps));
+      for (int ub = 0; ub < nu; ub += 256) {
+        uint4 xv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xv[c] = row[min(ub + lane + 64 * c, nu - 1)];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int u = ub + lane + 64 * c;
+          if (u < nu) {
+            uint32_t v[8];
+            normed(xv[c], u, rn, v);
+            put(t, u, v, sv, rowo);
+          }
+        }
+      }
+    } else {
+      // 3-4 from the held row
+      if (t != wave) load_row(t, xr);
+      u16x2 m16 = {0, 0};
+      uint32_t m32 = 0;
+#pragma unroll
+      for (int j = 0; j < XR; ++j) unit_max(m16, m32, xr[j]);
+      const uint32_t mx = wave_max_u32(max_bits(m16, m32));
+      sv = (float)(127.0 / (double)fmaxf(__uint_as_float(mx), args.eps));
+#pragma unroll
+      for (int j = 0; j < XR; ++j) {
+        const int u = lane + 64 * j;
+        if (u < nu) {
+          uint32_t v[8];
+          expand(xr[j], v);
+          put(t, u, v, sv, rowo);
+        }
+      }
+    }
+    uint32_t* rowl = xw + t * kp16 * 4;
+    for (int d = k / 4 + lane; d < kp16 * 4; d += 64) {
+      rowl[(((d >> 2) ^ t) << 2) + (d & 3)] = 0u;
+      if (out) rowo[d] = 0u;
+    }
+    if (lane == 0) {
+      fac[t] = gamma_over_s(gm, sv);
+      if (first && sg.scale_out != nullptr) sg.scale_out[tok0 + t] = sv;
+    }
+  }
+  __syncthreads();
+
+  mt_stream<D>(buf, cur, packed, nc, t0, u0, u1, g, r, mb, lds, kp16, sums);
+  __syncthreads();
+  const bool ybf = sg.y_bf16();
+  const bool vec = (n & 3) == 0 && ((uintptr_t)sg.y & (ybf ? 7 : 15)) == 0 &&
+                   (sg.acc_out == nullptr || ((uintptr_t)sg.acc_out & 15) == 0);
+  mt_epilogue(sums, fac, t0, nsub, mb, tok0, n, sg.relu2(), ybf, vec, sg.y, sg.acc_out, NT);
+}
+
+template <int WAVES, int D, int XR>
+void run_mt(const int8_t* xq, const float* scale, const uint32_t* packed, const float* gamma,
+            int m, int n, int nc, int S, int P, int TB, int nsub_alloc, int mba, bool relu2,
+            bool bf16, int vec_out, void* y, int32_t* acc_out, size_t lds, hipStream_t stream) {
+  gemv_stream_mt_kernel<WAVES, D, XR><<<P * TB, 64 * WAVES, lds, stream>>>(
+      xq, scale, reinterpret_cast<const uint4*>(packed), gamma, m, n, nc, S, P, TB, nsub_alloc,
+      mba, relu2, bf16, vec_out, y, acc_out);
+}
+
+template <int WAVES, int D, int XR, bool NORM>
+void run_mt_fused(const FusedArgs& args, int m, const int (&wb)[13], int groups, size_t lds,
+                  bool bf16, hipStream_t stream) {
+#define BL_MF(B)                                                                               \
+  gemv_stream_mt_fused_kernel<WAVES, D, XR, B, NORM><<<groups, 64 * WAVES, lds, stream>>>(     \
+      m, args.nseg, wb[1], wb[2], wb[3], wb[4], wb[5], wb[6], wb[7], wb[8], wb[9], wb[10],     \
+      wb[11], wb[12], args)
+  if (bf16)
+    BL_MF(true);
+  else
+    BL_MF(false);
+#undef BL_MF
+}
+
+}  // namespace
+
+size_t stream_mt_lds_bytes(int64_t m, int64_t nc, int nsub_alloc) {
+  const int64_t mba = m < kTokBlock ? m : kTokBlock;
+  return (size_t)(mba * nc * 256) + (size_t)nsub_alloc * kTokBlock * 16 * 4 + kTokBlock * 4;
+}
+
+hipError_t launch_gemv_stream_mt(const int8_t* xq, const float* scale, const uint32_t* packed,
+                                 const float* gamma, int64_t m, int64_t n, int64_t k, int P,
+                                 bool relu2, bool bf16, void* y, int32_t* acc_out,
+                                 hipStream_t stream) {
+  const int nc = (int)cdiv(k, kSuperK);
+  const int S = (int)(cdiv(n, kRowBlock) * 4);
+  const int TB = (int)cdiv(m, kTokBlock);
+  if (P < 1 || P > S || m < 1) return hipErrorInvalidValue;
+  const int nsub_alloc = (int)cdiv(S, P);
+  const int mba = (int)(m < kTokBlock ? m : kTokBlock);
+  const size_t lds = stream_mt_lds_bytes(m, nc, nsub_alloc);
+  const int vec_out = n % 4 == 0 && (uintptr_t)y % (bf16 ? 8 : 16) == 0 &&
+                      (acc_out == nullptr || (uintptr_t)acc_out % 16 == 0);
+  const int xr = (int)cdiv((int64_t)mba * nc * 16, 64 * 16);
+#define BL_MT(XR)                                                                          \
+  run_mt<16, 3, XR>(xq, scale, packed, gamma, (int)m, (int)n, nc, S, P, TB, nsub_alloc, mba, \
+                    relu2, bf16, vec_out, y, acc_out, lds, stream)
+  if (xr <= 2)
+    BL_MT(2);
+  else if (xr <= 4)
+    BL_MT(4);
+  else
+    BL_MT(8);
+#undef BL_MT
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_stream_mt_fused(const FusedArgs& args, int m, bool x_bf16, bool norm,
+                                       int xr, int groups, size_t lds, hipStream_t stream) {
+  int wb[13];
+  for (int i = 1; i < 13; ++i) wb[i] = i < args.nseg ? args.wg_begin[i] : INT_MAX;
+  wb[0] = 0;
+#define BL_MTF(XR)                                                                 \
+  if (norm)                                                                        \
+    run_mt_fused<16, 3, XR, true>(args, m, wb, groups, lds, x_bf16, stream);       \
+  else                                                                             \
+    run_mt_fused<16, 3, XR, false>(args, m, wb, groups, lds, x_bf16, stream)
+  if (xr <= 4) {
+    BL_MTF(4);
+  } else if (xr <= 8) {
+    BL_MTF(8);
+  } else if (xr <= 16) {
+    BL_MTF(16);
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef BL_MTF
+  return hipGetLastError();
+}
+
+}  // namespace bl

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 2
+#define BITLINEAR_ABI_VERSION 3
 
 /* Largest K: the kernels accumulate 64 * x~ * W~ in int32, so
  * 64 * 127 * K must stay below 2^31. */
@@ -245,9 +245,9 @@ bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t 
  *   workspace  bitlinear_forward_fused_workspace_bytes(ops, nops, m) bytes,
  *              with the contract of bitlinear_forward's workspace.
  * Every workgroup recomputes its entry's per-token absmax from the whole row
- * of x (all workgroups get the same s and x~), so the activations are read
- * from cache once (1-2 tokens) or twice (3-64 tokens, int8 matrix cores,
- * one block of up to 16 tokens per workgroup) per workgroup; meant for
+ * of x (all workgroups get the same s and x~), so each workgroup reads the
+ * activations of its tokens (one block of up to 16 from 3 tokens) from
+ * cache once, or twice when a row does not fit its registers; meant for
  * decode-sized batches.  From 3 tokens no workspace is needed (the size
  * query returns 0).
  * Entries with rmsnorm set normalize x first (same numbers as
@@ -304,6 +304,24 @@ bl_status bitlinear_forward_noalloc(const int8_t* xq, const float* scale, const 
                                     const float* gamma, int64_t m, int64_t n, int64_t k,
                                     int epilogue, int y_dtype, void* y, int32_t* acc_out,
                                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * bitlinear_forward_kernel, bitlinear_forward_fused_kernel -- which kernel
+ * bitlinear_forward (and bitlinear_forward_noalloc) or
+ * bitlinear_forward_fused would launch for these arguments: the host-side
+ * plan only, nothing is launched and no device memory is touched.  Every
+ * kernel gives the same numbers; the choice is speed only.  Returns one of
+ * the BL_KERNEL_* values, or a negative bl_status when the arguments would
+ * be refused (sizes as the call checks them; for the fused step the
+ * pointers' alignment too, since it decides the kernel).
+ * ---------------------------------------------------------------------- */
+#define BL_KERNEL_DOT4_GEMV 0      /* 1-2 tokens, v_dot4 (fused: the dot4 decode step) */
+#define BL_KERNEL_GEMM 1           /* matrix-core GEMM, more than 64 tokens */
+#define BL_KERNEL_MFMA_GEMV 2      /* windowed matrix-core GEMV (fused: its fused form) */
+#define BL_KERNEL_STREAM_GEMV 3    /* streaming matrix-core GEMV, 1-2 tokens */
+#define BL_KERNEL_STREAM_MT 4      /* streaming matrix-core GEMV, blocks of 16 tokens */
+int bitlinear_forward_kernel(int64_t m, int64_t n, int64_t k);
+int bitlinear_forward_fused_kernel(const bl_linear* ops, int nops, int64_t m);
 
 /* Zero-fill a forward workspace with a device kernel (no hipMemset, so it can
  * be captured in a HIP graph).  bytes must be a multiple of 4. */

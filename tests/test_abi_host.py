@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(bl):
     raw = ctypes.CDLL(bl.LIB_PATH)
     for name in _declared_functions():
         assert hasattr(raw, name), name
-    assert bl.lib.bitlinear_abi_version() == 2
+    assert bl.lib.bitlinear_abi_version() == 3
 
 
 @pytest.mark.parametrize("n,k", [(1, 1), (64, 256), (65, 257), (2560, 6912), (28672, 8192), (130, 520)])
@@ -242,3 +242,81 @@ def test_workspace_init_rejects(bl):
     assert w(None, 64, None) == 1
     assert w(FAKE, 6, None) == 1
     assert w(FAKE + 2, 8, None) == 3
+
+
+# ------------------------------------------------------------- kernel plans --
+# bitlinear_forward_kernel / bitlinear_forward_fused_kernel are host-only
+# queries of the dispatch plan; the GPU parity cases rely on them to cover
+# every kernel.
+@pytest.mark.parametrize("m,n,k,kernel", [
+    (1, 256, 256, "dot4_gemv"),
+    (2, 300, 40000, "dot4_gemv"),           # split K
+    (1, 28672, 8192, "stream_gemv"),
+    (2, 8192, 28672, "stream_gemv"),
+    (64, 8192, 8192, "stream_mt"),          # long rows, <= 128 row blocks, > 32 tokens
+    (32, 1024, 8192, "stream_mt"),          # <= 16 row blocks, > 16 tokens
+    (32, 8192, 8192, "mfma_gemv"),
+    (3, 2560, 2560, "mfma_gemv"),
+    (64, 2560, 6912, "mfma_gemv"),          # rows of 27 super-chunks
+    (16, 2560, 16384, "mfma_gemv"),         # x~ of 16 tokens past the LDS
+    (512, 1024, 8192, "mfma_gemv"),         # few output tiles: token blocks
+    (2048, 6912, 2560, "gemm"),
+])
+def test_forward_kernel_plan(bl, m, n, k, kernel):
+    assert bl.forward_kernel(m, n, k) == kernel
+
+
+def test_forward_kernel_plan_rejects(bl):
+    with pytest.raises(bl.BitLinearError):
+        bl.forward_kernel(0, 10, 10)
+    with pytest.raises(bl.BitLinearError):
+        bl.forward_kernel(1, 10, bl.BL_MAX_K + 1)
+
+
+def _fake_table(bl, specs, x_offset=0):
+    """bl_linear entries with distinct 256-byte aligned fake addresses (the
+    plan query reads sizes and alignment only)."""
+    arr = (bl.BLLinear * len(specs))()
+    for i, (n, k, xdt, norm) in enumerate(specs):
+        base = 0x10000000 * (i + 1)
+        arr[i] = bl.BLLinear(base + x_offset, bl.BL_BF16 if xdt == "bf16" else bl.BL_F32,
+                             base + 0x1000000, base + 0x2000000, n, k, 0, bl.BL_BF16,
+                             base + 0x3000000, None, None, None, 1 if norm else 0,
+                             2.0 ** -23, None)
+    return arr
+
+
+@pytest.mark.parametrize("m,specs,x_offset,kernel", [
+    (1, [(28672, 8192, "bf16", False)], 0, "stream_gemv"),
+    (1, [(300, 512, "bf16", False)], 0, "dot4_gemv"),                    # short rows
+    (8, [(2560, 2560, "bf16", False), (640, 2560, "bf16", False)], 0, "stream_mt"),
+    (64, [(2560, 6912, "bf16", True)], 0, "stream_mt"),
+    (33, [(1000, 4096, "f32", False)], 0, "stream_mt"),
+    (8, [(1000, 4096, "f32", False)], 4, "mfma_gemv"),                   # x not 16-byte aligned
+    (16, [(2048, 8200, "f32", False)], 0, "mfma_gemv"),                  # fp32 row past 16 units per lane
+    (2, [(1100, 28672, "bf16", True)], 0, "mfma_gemv"),                  # RMSNorm, x~ past the LDS
+])
+def test_forward_fused_kernel_plan(bl, m, specs, x_offset, kernel):
+    arr = _fake_table(bl, specs, x_offset)
+    r = bl.lib.bitlinear_forward_fused_kernel(arr, len(specs), m)
+    assert r >= 0 and bl.KERNEL_NAMES[r] == kernel
+
+
+def test_forward_fused_kernel_plan_rejects(bl):
+    arr = _fake_table(bl, [(100, 100, "f32", False)])
+    assert bl.lib.bitlinear_forward_fused_kernel(arr, 1, bl.BL_FUSED_MAX_M + 1) == -bl.BL_ERR_UNSUPPORTED_SHAPE
+    assert bl.lib.bitlinear_forward_fused_kernel(arr, 0, 4) == -bl.BL_ERR_INVALID_ARG
+    assert bl.lib.bitlinear_forward_fused_kernel(arr, 1, 0) == -bl.BL_ERR_INVALID_ARG
+
+
+def test_gpu_cases_cover_every_kernel(bl):
+    """The forward and fused-step parity cases reach every kernel."""
+    from test_gpu_parity import FWD_CASES
+    from test_gpu_fused import FUSED_CASES
+    kinds = {bl.forward_kernel(m, n, k) for (m, n, k, *_rest) in FWD_CASES}
+    assert kinds == set(bl.KERNEL_NAMES.values()), kinds
+    fused = set()
+    for m, specs in FUSED_CASES:
+        arr = _fake_table(bl, [(n, k, xdt, False) for (n, k, _r, _y, xdt) in specs])
+        fused.add(bl.KERNEL_NAMES[bl.lib.bitlinear_forward_fused_kernel(arr, len(specs), m)])
+    assert fused == {"dot4_gemv", "stream_gemv", "stream_mt", "mfma_gemv"}, fused

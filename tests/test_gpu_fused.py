@@ -90,6 +90,13 @@ FUSED_CASES = [
     (17, [(300, 1000, True, "f32", "bf16"), (64, 8200, False, "bf16", "bf16")]),    # a block of 1
     (40, [(2560, 2560, False, "bf16", "bf16"), (640, 2560, False, "bf16", "bf16")]),
     (64, [(500, 777, False, "bf16", "f32"), (16400, 512, True, "bf16", "bf16")]),  # >= 256 row blocks
+    # the multi-token streaming kernel (rows of whole aligned 16-byte units,
+    # one activation dtype, a row within 16 units per lane)
+    (64, [(2560, 6912, False, "bf16", "bf16")]),                                   # 14 units per lane
+    (33, [(1000, 4096, True, "f32", "f32"), (70, 2048, False, "bf16", "f32")]),    # fp32 x, 16 units
+    (3, [(64, 256, False, "f32", "bf16")] * 3),
+    (50, [(2560, 2560, False, "bf16", "bf16"), (640, 2560, False, "bf16", "bf16"),
+          (640, 2560, True, "bf16", "bf16")]),                                      # a block of 2
 ]
 
 

@@ -146,12 +146,17 @@ FUSED_NORM_CASES = [
     (1, [(1024, 4096, True, "f32", False, True), (300, 2048, False, "f32", True, False)]),
     (2, [(2000, 3000, True, "bf16", True, True), (64, 256, False, "bf16", False, True)]),
     (1, [(64, 256, False, "bf16", True, True)]),              # short rows: still streaming
-    # the matrix-core fused kernel
+    # the fused windowed matrix-core kernel
     (2, [(1100, 28672, False, "bf16", True, True)]),          # 2 tokens, rows past its registers
     (1, [(300, 1001, False, "f32", True, True)]),             # odd K: element loads
     (5, [(2560, 2560, False, "bf16", True, True), (500, 777, True, "f32", True, True)]),
     (16, [(6912, 2560, True, "bf16", False, True), (2560, 6912, False, "bf16", True, True)]),
     (40, [(1000, 3000, True, "bf16", True, True), (64, 8200, False, "bf16", True, False)]),
+    # the multi-token streaming kernel (one dtype, whole aligned units)
+    (8, [(2560, 2560, False, "bf16", True, True), (640, 2560, False, "bf16", True, True),
+         (640, 2560, False, "bf16", True, True)], True),
+    (33, [(3000, 4096, False, "f32", True, True), (640, 2048, True, "f32", False, True)]),
+    (64, [(2560, 6912, False, "bf16", True, True), (300, 512, True, "bf16", False, False)]),
 ]
 
 

@@ -209,6 +209,9 @@ FWD_CASES = [
     (1, 16448, 4100, True, "bf16", "bf16"),      # 1028 sub-blocks over 256 workgroups
     (2, 1088, 32000, False, "f32", "bf16"),      # x~ of two tokens fills the LDS
     (1, 3000, 28672, False, "bf16", "bf16"),     # 16 waves x 3 units in flight
+    # 3 to 64 tokens: the multi-token streaming GEMV where x~ of a 16-token
+    # block fits the LDS (most of the rows below), else the windowed MFMA
+    # GEMV (rows of >= 16384 inputs); the kernel plan tests list which
     # windowed MFMA GEMV, 3 to 16 tokens: 2 row groups x 4 slices
     (3, 130, 520, True, "f32", "f32"),           # 3 super-chunks: an empty slice
     (4, 300, 1000, False, "f32", "bf16"),
@@ -244,6 +247,14 @@ FWD_CASES = [
     (256, 384, 768, False, "f32", "bf16"),
     (200, 1001, 700, False, "bf16", "f32"),      # odd N: element stores
     (200, 6000, 512, True, "bf16", "bf16"),      # short rows, many blocks
+    # multi-token streaming GEMV (long rows of few row blocks past 16-32
+    # tokens; x~ of a 16-token block within the LDS): row ranges x blocks
+    (33, 2560, 8200, False, "bf16", "bf16"),     # 3 blocks, the last of 1 token; 80 row ranges
+    (64, 1030, 8192, False, "f32", "bf16"),      # 128 KiB of x~; N % 4 != 0: element stores
+    (20, 100, 8000, True, "bf16", "f32"),        # one row range per sub-block, 2 blocks
+    (40, 130, 8100, False, "f32", "bf16"),       # 12 row ranges: not a multiple of 8
+    (48, 8192, 9000, True, "bf16", "bf16"),      # x~ staging past 8 units per thread
+    (17, 1000, 8192, False, "bf16", "bf16"),     # a last block of 1 token, 64 row ranges
     # wide-wave MFMA GEMM (more than 64 tokens, >= 128 tiles)
     (1000, 6100, 300, True, "bf16", "bf16"),     # 64 x 512 tiles, ragged M, N, K
     (1024, 6144, 512, False, "f32", "bf16"),     # 64 x 512, vector stores
