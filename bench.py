@@ -567,6 +567,18 @@ def recorded_traffic():
         return None
 
 
+def copy_calibration(torch):
+    """A plain copy of COPY_BYTES, three times: what FETCH_SIZE / WRITE_SIZE
+    read for it scales the counters of the other kernels to bytes."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def pmc_driver(B, torch, args):
     """Launches to read counters or traces from.
     c5gemv: a plain copy of COPY_BYTES (the counter calibration), then the
@@ -574,8 +586,10 @@ def pmc_driver(B, torch, args):
             their rotating copies (one token);
     step:   `steps` headline decode steps (eager);
     prefill: the two 2048-token prefill GEMMs, `steps` times each;
-    mfma:   the windowed MFMA GEMV at 64 tokens on the 2B-class shapes and
-            the 100B-class k/v at 512 tokens, `steps` times each."""
+    mfma:   the copy calibration, then bitlinear_forward at --m tokens on the
+            2B-class q/up/down (--m <= 64) or the 100B-class k/v (--m > 64),
+            `steps` times each over rotating copies;
+    c3:     `steps` passes of the 2B-class stack at --m tokens."""
     import datagen
     if args.pmc_driver == "prefill":
         W = Weights(B, torch, datagen.WORKLOADS["c4"], copies=1)
@@ -601,23 +615,20 @@ def pmc_driver(B, torch, args):
         print(json.dumps({"pmc_driver": "c3", "steps": args.steps, "m": args.m}))
         return
     if args.pmc_driver == "mfma":
-        for wlname, m, names in (("c2", 64, ("q", "up", "down")), ("c5", 512, ("k",))):
-            W = Weights(B, torch, datagen.WORKLOADS[wlname], names=names)
-            X = Inputs(B, torch, W, m)
-            for nm in names:
-                for i in range(args.steps):
-                    forward_call(B, W, X, nm, i, None)()
-                torch.cuda.synchronize()
-            del W, X
-            torch.cuda.empty_cache()
-        print(json.dumps({"pmc_driver": "mfma", "steps": args.steps}))
+        # the copy calibration, then bitlinear_forward at args.m tokens: the
+        # 2B-class q, up and down up to 64 tokens, the 100B-class k and v
+        # beyond, each over its rotating copies
+        copy_calibration(torch)
+        wlname, names = ("c2", ("q", "up", "down")) if args.m <= 64 else ("c5", ("k", "v"))
+        W = Weights(B, torch, datagen.WORKLOADS[wlname], names=names)
+        X = Inputs(B, torch, W, args.m)
+        for nm in names:
+            for i in range(args.steps):
+                forward_call(B, W, X, nm, i, None)()
+            torch.cuda.synchronize()
+        print(json.dumps({"pmc_driver": "mfma", "steps": args.steps, "m": args.m}))
         return
-    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    del src, dst
+    copy_calibration(torch)
     W = Weights(B, torch, datagen.WORKLOADS["c5"],
                 names=None if args.pmc_driver == "step" else ["up", "down"])
     X = Inputs(B, torch, W, 1)
@@ -674,7 +685,8 @@ def summarize(directory, command, name):
         return statistics.median(v) if v else None
 
     f = lambda v, fmt: "-" if v is None else format(v, fmt)
-    if "FETCH_SIZE" in ctrs or "WRITE_SIZE" in ctrs:
+    updown = any("gemv_stream_fused_kernel" in k for (k, c) in vals)
+    if updown and ("FETCH_SIZE" in ctrs or "WRITE_SIZE" in ctrs):
         def largest(kern_sub, ctr):
             v = [x for (k, c), xs in vals.items() if kern_sub in k and c == ctr for x in xs]
             return max(v) if v else None
@@ -749,20 +761,32 @@ def summarize(directory, command, name):
                                                "SQ_WAIT_INST_ANY", "SQ_BUSY_CYCLES")) + " |")
         out.append((f"{name}_lds_counters.md", "\n".join(lines) + "\n"))
     if ctrs and not out:
-        # any other counter set: one row per kernel, medians per dispatch
+        # any other counter set: one row per kernel, medians per dispatch;
+        # FETCH_SIZE / WRITE_SIZE also as bytes, scaled by the copy kernel's
         cols = sorted(ctrs)
+        scale = {}
+        for ctr, per in (("FETCH_SIZE", "FETCH"), ("WRITE_SIZE", "WRITE")):
+            cv = [x for (k, c), xs in vals.items() if "copy" in k and c == ctr for x in xs]
+            if cv:
+                scale[ctr] = (COPY_BYTES / 1024) / max(cv)
         kernels = sorted({k for (k, c) in vals})
+        extra = [c for c in ("FETCH_SIZE", "WRITE_SIZE") if c in scale]
         lines = ["# Counters per dispatch (rocprofv3 --pmc)", "",
                  f"Command: `{command}`", "",
-                 "Medians over the dispatches of each kernel instance.", "",
-                 "| kernel | dispatches | us | " + " | ".join(cols) + " |",
-                 "|---|---|---|" + "---|" * len(cols)]
+                 "Medians over the dispatches of each kernel instance." +
+                 (" Bytes = KiB x 1024 x (copy bytes / the copy kernel's KiB): " +
+                  ", ".join(f"{c} scale {scale[c]:.4f}" for c in extra) if extra else ""), "",
+                 "| kernel | dispatches | us | " + " | ".join(cols) +
+                 "".join(f" | {c} bytes" for c in extra) + " |",
+                 "|---|---|---|" + "---|" * (len(cols) + len(extra))]
         for k in kernels:
             us = statistics.median(durs[k]) if durs.get(k) else None
             nd = max(len(xs) for (kk, c), xs in vals.items() if kk == k)
+            mv = {c: statistics.median(vals[(k, c)]) if (k, c) in vals else None for c in cols}
             lines.append(f"| {k} | {nd} | {f(us, '.2f')} | " +
-                         " | ".join(f(statistics.median(vals[(k, c)]) if (k, c) in vals else None,
-                                      ".6g") for c in cols) + " |")
+                         " | ".join(f(mv[c], ".6g") for c in cols) +
+                         "".join(f" | {f(mv[c] * 1024 * scale[c] if mv[c] is not None else None, '.4g')}"
+                                 for c in extra) + " |")
         out.append((f"{name}_counters.md", "\n".join(lines) + "\n"))
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for fname, text in out:
@@ -781,7 +805,7 @@ def main():
     ap.add_argument("--pmc-driver", nargs="?", const="c5gemv",
                     choices=["c5gemv", "step", "prefill", "mfma", "c3"],
                     help="only launch what counters or traces are read from")
-    ap.add_argument("--m", type=int, default=64, help="tokens for --pmc-driver c3")
+    ap.add_argument("--m", type=int, default=64, help="tokens for --pmc-driver mfma / c3")
     ap.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSVs")
     ap.add_argument("--name", default="gemv_fused_c5_updown",
                     help="kernel and workload the summaries are named for")

@@ -467,21 +467,27 @@ const char* bitlinear_status_string(int status) {
   }
 }
 
-int64_t bitlinear_padded_n(int64_t n) { return n <= 0 ? 0 : padded_n(n); }
-int64_t bitlinear_padded_k(int64_t k) { return k <= 0 ? 0 : padded_k(k); }
+// Size queries: 0 outside the sizes the entry points accept (1..BL_MAX_MN
+// rows and tokens, 1..BL_MAX_K inputs), where every product below fits in
+// int64 (2^24 * 2^18 = 2^42).
+static bool mn_ok(int64_t v) { return v >= 1 && v <= BL_MAX_MN; }
+static bool k_ok(int64_t k) { return k >= 1 && k <= BL_MAX_K; }
+
+int64_t bitlinear_padded_n(int64_t n) { return mn_ok(n) ? padded_n(n) : 0; }
+int64_t bitlinear_padded_k(int64_t k) { return k_ok(k) ? padded_k(k) : 0; }
 
 size_t bitlinear_packed_bytes(int64_t n, int64_t k) {
-  if (n <= 0 || k <= 0) return 0;
+  if (!mn_ok(n) || !k_ok(k)) return 0;
   return (size_t)(padded_n(n) * padded_k(k) / 4);
 }
 
 size_t bitlinear_xq_bytes(int64_t m, int64_t k) {
-  if (m <= 0 || k <= 0) return 0;
+  if (!mn_ok(m) || !k_ok(k)) return 0;
   return (size_t)(m * padded_k(k));
 }
 
 size_t bitlinear_pack_workspace_bytes(int64_t n, int64_t k) {
-  if (n <= 0 || k <= 0) return 0;
+  if (!mn_ok(n) || !k_ok(k)) return 0;
   return pack_workspace_bytes(n, k);
 }
 

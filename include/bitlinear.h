@@ -84,6 +84,8 @@ typedef enum { BL_EPI_NONE = 0, BL_EPI_RELU2 = 1 } bl_epilogue;
  *   order, i.e. for consecutive inputs k.
  * ---------------------------------------------------------------------- */
 
+/* Size queries return 0 for sizes the entry points refuse (n or m outside
+ * 1..BL_MAX_MN, k outside 1..BL_MAX_K). */
 /* Row count rounded up to 64. */
 int64_t bitlinear_padded_n(int64_t n);
 /* Input count rounded up to 256; also the row stride (bytes) of x~. */
