@@ -742,7 +742,7 @@ def summarize(directory, command, name):
             lines.append(f"| {k} | {f(us, '.2f')} | {f(ghz, '.3f')} | {f(util, '.3f')} | "
                          f"{f(ops, '.4g')} | {f(tops, '.0f')} | {f(waves, '.0f')} | {f(wr, '.2f')} |")
         out.append((f"{name}_mfma_counters.md", "\n".join(lines) + "\n"))
-    if "SQ_INSTS_LDS" in ctrs or "SQ_LDS_BANK_CONFLICT" in ctrs:
+    if "SQ_LDS_BANK_CONFLICT" in ctrs:
         kernels = sorted({k for (k, c), xs in vals.items() if c in ("SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT")
                           and max(xs) > 0})
         lines = ["# LDS and wait counters (rocprofv3 --pmc)", "",
