@@ -212,6 +212,7 @@ struct FusedPlan {
   bool unsupported = false;             // no kernel takes this table
   bool norm = false;                    // some entry has RMSNorm
   bool stream = false;                  // 1..2 tokens: the streaming matrix-core kernel
+  bool stream_wide = false;             // its 16-wave shape (rows past 8 waves' registers)
   int xr = 0;                           // its activation units per thread and token
   int nsub_alloc = 0;                   // its sub-blocks per workgroup, at most
   int64_t nc_max = 0;
@@ -248,10 +249,17 @@ static bool stream_fused_plan(const bl_linear* ops, int nops, int64_t m, bool no
     if (nu > nu_max) nu_max = nu;
   }
   if (nc_max < 8 && !norm) return false;
-  int waves, depth;
-  stream_shape((int)m, nc_max, &waves, &depth);
-  const int64_t xr = cdiv(nu_max, 64 * waves);
-  if (m * xr > 8 || (norm && m * xr > 4)) return false;
+  // 8 waves when every token's row fits their registers, else 16
+  bool wide = false;
+  int64_t xr = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    wide = pass == 1;
+    int waves, depth;
+    stream_fused_shape(wide, &waves, &depth);
+    xr = cdiv(nu_max, 64 * waves);
+    if (!(m * xr > 8 || (norm && m * xr > 4))) break;
+    if (wide) return false;
+  }
   // one workgroup per CU at most: a 16-wave workgroup fills a CU, so a
   // workgroup past the 256th would wait for a whole round
   int64_t gs[kMaxFused], total = 0;
@@ -280,6 +288,7 @@ static bool stream_fused_plan(const bl_linear* ops, int nops, int64_t m, bool no
   const size_t lds = stream_lds_bytes((int)m, nc_max, nsub_alloc);
   if (lds > kStreamMaxLds) return false;
   p->stream = true;
+  p->stream_wide = wide;
   p->norm = norm;
   p->xr = (int)xr;
   p->nsub_alloc = nsub_alloc;
@@ -571,7 +580,7 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
   }
   if (plan.stream) {
     args.nsub_alloc = plan.nsub_alloc;
-    const hipError_t e = launch_gemv_stream_fused(args, (int)m, plan.nc_max,
+    const hipError_t e = launch_gemv_stream_fused(args, (int)m, plan.stream_wide,
                                                   ops[0].x_dtype == BL_BF16, plan.norm, plan.xr,
                                                   begin, plan.lds,
                                                   reinterpret_cast<hipStream_t>(stream));

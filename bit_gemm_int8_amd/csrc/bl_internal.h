@@ -112,11 +112,12 @@ hipError_t launch_gemv_fused(const FusedArgs& args, int m, int waves, int qpl, b
 // per workgroup, x~ of every token in LDS).
 size_t stream_lds_bytes(int m, int64_t nc, int nsub_alloc);
 void stream_shape(int m, int64_t nc, int* waves, int* depth);
+void stream_fused_shape(bool wide, int* waves, int* depth);
 hipError_t launch_gemv_stream(int m, const int8_t* xq, const float* scale,
                               const uint32_t* packed, const float* gamma, int64_t n, int64_t k,
                               int grid, bool relu2, bool bf16, void* y, int32_t* acc_out,
                               hipStream_t stream);
-hipError_t launch_gemv_stream_fused(const FusedArgs& args, int m, int64_t nc_max, bool x_bf16,
+hipError_t launch_gemv_stream_fused(const FusedArgs& args, int m, bool wide, bool x_bf16,
                                     bool norm, int xr, int groups, size_t lds,
                                     hipStream_t stream);
 

@@ -78,6 +78,7 @@ FUSED_CASES = [
     (2, [(2000, 3000, True, "bf16", "f32"), (1040, 8192, False, "f32", "f32")]),
     (2, [(8192, 8192, False, "bf16", "bf16"), (1024, 8192, False, "bf16", "bf16"),
          (1024, 8192, False, "bf16", "bf16")]),
+    (2, [(1040, 28672, False, "bf16", "bf16"), (300, 4096, True, "bf16", "bf16")]),  # 16 waves: rows past 8 waves' registers
     # 3 to 16 tokens: int8 matrix cores
     (8, [(2560, 2560, False, "bf16", "bf16"), (640, 2560, False, "bf16", "bf16"),
          (6912, 2560, True, "bf16", "bf16")]),                                        # all bf16
