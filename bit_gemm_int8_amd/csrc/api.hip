@@ -174,6 +174,24 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
         tiles = t;
       }
     }
+    // Few tiles on short rows (<= 16 super-chunks): the multi-token
+    // streaming GEMV when the matrix has >= 32 row blocks or the batch is
+    // >= 512 tokens, else the windowed MFMA GEMV in token blocks (MI355X,
+    // 2B-class q and k/v at 128-1024 tokens: q at 512 tokens 12.6 -> 9.5 us,
+    // k/v at 1024 tokens 8.9 -> 6.9 us; on rows of 32 super-chunks, the
+    // 100B-class k/v, the two tie)
+    if (tiles < kCUs / 2 && nc <= 16 && (nb >= 32 || m >= 512)) {
+      const int64_t subs = nb * 4;
+      const int64_t P = mt_row_ranges(m, subs);
+      if (stream_mt_lds_bytes(m, nc, (int)cdiv(subs, P)) <= kMtMaxLds) {
+        p.kind = 4;
+        p.qpl = (int)P;
+        p.splits = 1;
+        p.slots = 0;
+        p.ws_bytes = 0;
+        return p;
+      }
+    }
     if (tiles < kCUs / 2) {
       p.kind = 2;
       p.variant = nb >= 256 ? 6 : nb <= 64 ? 3 : nc >= 24 ? 7 : 5;

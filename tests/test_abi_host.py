@@ -260,6 +260,9 @@ def test_workspace_init_rejects(bl):
     (64, 2560, 6912, "mfma_gemv"),          # rows of 27 super-chunks
     (16, 2560, 16384, "mfma_gemv"),         # x~ of 16 tokens past the LDS
     (512, 1024, 8192, "mfma_gemv"),         # few output tiles: token blocks
+    (512, 640, 2560, "stream_mt"),          # few tiles, short rows, >= 512 tokens
+    (256, 2560, 2560, "stream_mt"),         # few tiles, short rows, >= 32 row blocks
+    (256, 640, 2560, "mfma_gemv"),
     (2048, 6912, 2560, "gemm"),
 ])
 def test_forward_kernel_plan(bl, m, n, k, kernel):

@@ -255,6 +255,10 @@ FWD_CASES = [
     (40, 130, 8100, False, "f32", "bf16"),       # 12 row ranges: not a multiple of 8
     (48, 8192, 9000, True, "bf16", "bf16"),      # x~ staging past 8 units per thread
     (17, 1000, 8192, False, "bf16", "bf16"),     # a last block of 1 token, 64 row ranges
+    # ... and larger batches with few output tiles on short rows
+    (512, 2560, 2560, True, "bf16", "bf16"),     # 32 token blocks x 8 row ranges
+    (1000, 640, 3000, False, "f32", "bf16"),     # a last block of 8 tokens; 4 row ranges (not grouped)
+    (300, 2100, 1000, False, "bf16", "f32"),     # 19 token blocks, 8 row ranges (XCD-grouped)
     # wide-wave MFMA GEMM (more than 64 tokens, >= 128 tiles)
     (1000, 6100, 300, True, "bf16", "bf16"),     # 64 x 512 tiles, ragged M, N, K
     (1024, 6144, 512, False, "f32", "bf16"),     # 64 x 512, vector stores
