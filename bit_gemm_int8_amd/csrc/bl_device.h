@@ -9,6 +9,7 @@
 
 typedef int32_t bl_v4i __attribute__((ext_vector_type(4)));
 typedef int32_t bl_v16i __attribute__((ext_vector_type(16)));
+typedef uint16_t bl_u16x2 __attribute__((ext_vector_type(2)));
 
 namespace bl {
 
@@ -118,6 +119,29 @@ __device__ __forceinline__ float rms_factor(double sumsq, int k, float norm_eps)
 // y = fp32(fp32(x * r) * w): two separately rounded multiplies.
 __device__ __forceinline__ float rms_apply(float x, float r, float w) {
   return __fmul_rn(__fmul_rn(x, r), w);
+}
+
+// Four activations (fp32 bit patterns) to four int8 codes rint(fp32(v * s))
+// packed in byte order, for s = fp32(127 / b) with b = max(beta, eps) >= |v|
+// (the activation quant of a row whose absmax is beta).  The clamp to
+// [-128, 127] is left out: it never binds for finite inputs, since
+// |v s| <= 127 (1 + 2^-24), whose fp32 rounding is at most 127 + 2^-17, so
+// rint stays within [-127, 127].  Adding 1.5 * 2^23 rounds a product of
+// magnitude below 2^22 to the nearest integer, ties to even, in the low
+// mantissa bits; three v_perm pack the low bytes.  The product must be
+// rounded to fp32 before that add: contracted into one fma, rint would see
+// the exact product (__fmul_rn is a plain multiply, and device code
+// contracts by default), hence contract(off).
+__device__ __forceinline__ uint32_t quant4_rne(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                               float s) {
+#pragma clang fp contract(off)
+  uint32_t q[4] = {a, b, c, d};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    q[i] = __float_as_uint(__fmul_rn(__uint_as_float(q[i]), s) + 12582912.0f);
+  const uint32_t lo = __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 // Rescale factor gamma / s as the correctly rounded fp32 quotient (the fp64

@@ -220,40 +220,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_kernel(
 //   2. beta = max|x| per token (sign-cleared fp32 bits, DPP in the wave, LDS
 //      across waves) and s = fp32(127 / max(beta, eps)) exactly as
 //      bitlinear_quant_act computes it;
-//   3. x~ = clamp(rint(fp32(x * s))) of every held unit into LDS (the
-//      1.5 * 2^23 rounding of quant4_magic, checked against rintf), zero past
-//      K; every workgroup of an entry computes the same s and x~ bit for bit.
+//   3. x~ = clamp(rint(fp32(x * s))) of every held unit into LDS
+//      (quant4_rne, whose clamp cannot bind), zero past K; every workgroup
+//      of an entry computes the same s and x~ bit for bit.
 // Rows must be whole 16-byte units at 16-byte alignment (checked on the host).
-template <bool BF16>
-__device__ __forceinline__ uint32_t unit_absmax_bits(const uint4& u) {
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-  uint32_t mx = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (BF16) {
-      mx = max(mx, (w[e] << 16) & 0x7FFFFFFFu);
-      mx = max(mx, w[e] & 0x7FFF0000u);
-    } else {
-      mx = max(mx, w[e] & 0x7FFFFFFFu);
-    }
-  }
-  return mx;
-}
-
-__device__ __forceinline__ uint32_t quant4_of(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
-                                              float s) {
-  uint32_t q[4] = {a, b, c, d};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float p = __fmul_rn(__uint_as_float(q[i]), s);     // one fp32 multiply
-    p = fminf(fmaxf(p, -128.0f), 127.0f);
-    q[i] = __float_as_uint(p + 12582912.0f);          // rint, half to even, in the low bits
-  }
-  const uint32_t lo = __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u);
-  const uint32_t hi = __builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u);
-  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-}
-
 // With NORM, entries flagged for RMSNorm first normalize each token (the
 // BitLinear listing of "End-to-End Implementation: Building a Native
 // BitLinear Layer" applies nn.RMSNorm before quantize_activations_int8):
@@ -383,16 +353,30 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_fused_kernel(
     }
   };
 
-  // 2. beta and s per token
+  // 2. beta and s per token (bf16 without RMSNorm: the magnitudes of a word's
+  //    two activations as 16-bit lanes, v_pk_max_u16, widened at the end:
+  //    the top half of an fp32 is its bf16)
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     uint32_t mx = 0;
+    if (BF16 && !(NORM && nrm)) {
+      bl_u16x2 m16 = {0, 0};
 #pragma unroll
-    for (int j = 0; j < XR; ++j) {
-      uint32_t v[8];
-      vals(m, j, v);
+      for (int j = 0; j < XR; ++j) {
+        const uint32_t w[4] = {xr[m][j].x, xr[m][j].y, xr[m][j].z, xr[m][j].w};
 #pragma unroll
-      for (int e = 0; e < EPU; ++e) mx = max(mx, v[e] & 0x7FFFFFFFu);
+        for (int e = 0; e < 4; ++e)
+          m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(bl_u16x2, w[e] & 0x7FFF7FFFu));
+      }
+      mx = (uint32_t)max(m16[0], m16[1]) << 16;
+    } else {
+#pragma unroll
+      for (int j = 0; j < XR; ++j) {
+        uint32_t v[8];
+        vals(m, j, v);
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) mx = max(mx, v[e] & 0x7FFFFFFFu);
+      }
     }
     mx = wave_max_u32(mx);
     if (lane == 0) red[wave][m] = mx;
@@ -418,11 +402,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_fused_kernel(
         uint32_t v[8];
         vals(m, j, v);
         if (BF16) {
-          const uint32_t d0 = quant4_of(v[0], v[1], v[2], v[3], sv[m]);
-          const uint32_t d1 = quant4_of(v[4], v[5], v[6], v[7], sv[m]);
+          const uint32_t d0 = quant4_rne(v[0], v[1], v[2], v[3], sv[m]);
+          const uint32_t d1 = quant4_rne(v[4], v[5], v[6], v[7], sv[m]);
           reinterpret_cast<uint2*>(xw + m * kp16 * 4)[u] = make_uint2(d0, d1);
         } else {
-          xw[m * kp16 * 4 + u] = quant4_of(v[0], v[1], v[2], v[3], sv[m]);
+          xw[m * kp16 * 4 + u] = quant4_rne(v[0], v[1], v[2], v[3], sv[m]);
         }
       }
     }

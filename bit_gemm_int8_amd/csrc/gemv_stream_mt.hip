@@ -35,7 +35,6 @@ namespace bl {
 namespace {
 
 constexpr int kTokBlock = 16;
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 // Word 3 of a raw buffer resource on gfx9 (untyped 32-bit data; loads past
 // num_records return zero).
 constexpr int kBufferDword3 = 0x00020000;
@@ -265,32 +264,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_kernel(
 //      at a time (from the caches after the first), with the gain;
 //   3. beta = max|x| (sign-cleared fp32 bits, a wave max) and
 //      s = fp32(127 / max(beta, eps)) exactly as bitlinear_quant_act;
-//   4. x~ = clamp(rint(fp32(x * s))) (quant_mt4) into LDS, zero past K; the
-//      entry's first row range also writes x~ and s out when asked.
+//   4. x~ = clamp(rint(fp32(x * s))) (quant4_rne, whose clamp cannot bind)
+//      into LDS, zero past K; the entry's first row range also writes x~
+//      and s out when asked.
 // Rows must be whole 16-byte units at 16-byte alignment (checked on the host).
-//
-// quant_mt4 leaves out the clamp, which this prologue costs a VALU operation
-// per element (every workgroup quantizes its block's whole rows): for finite
-// inputs it never binds.  With b = max(beta, eps) >= |x| and s = fp32(127 / b)
-// <= (127 / b)(1 + 2^-24), |x s| <= 127 (1 + 2^-24), whose fp32 rounding is at
-// most 127 + 2^-17, so rint gives at most 127 in magnitude.  Adding 1.5 * 2^23
-// rounds a product of magnitude below 2^22 to the nearest integer, ties to
-// even, in the low mantissa bits; three v_perm pack the low bytes.
-__device__ __forceinline__ uint32_t quant_mt4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
-                                              float s) {
-  // the product must be rounded to fp32 before the rounding add: contracted
-  // into one fma, rint would see the exact product (__fmul_rn is a plain
-  // multiply here, and device code contracts by default)
-#pragma clang fp contract(off)
-  uint32_t q[4] = {a, b, c, d};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    q[i] = __float_as_uint(__fmul_rn(__uint_as_float(q[i]), s) + 12582912.0f);
-  const uint32_t lo = __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u);
-  const uint32_t hi = __builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u);
-  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-}
-
 template <int WAVES, int D, int XR, bool BF16, bool NORM>
 __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
     int m_all, int nseg, int wb1, int wb2, int wb3, int wb4, int wb5, int wb6, int wb7, int wb8,
@@ -369,17 +346,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
   // running max of |value| over units: sign-cleared bits compare as
   // magnitudes; bf16 pairs as two 16-bit lanes (v_pk_max_u16), widened to
   // fp32 bits at the end (the top half of an fp32 is its bf16)
-  auto unit_max = [&](u16x2& m16, uint32_t& m32, const uint4& x) __attribute__((always_inline)) {
+  auto unit_max = [&](bl_u16x2& m16, uint32_t& m32, const uint4& x) __attribute__((always_inline)) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (BF16)
-        m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(u16x2, w[e] & 0x7FFF7FFFu));
+        m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(bl_u16x2, w[e] & 0x7FFF7FFFu));
       else
         m32 = max(m32, w[e] & 0x7FFFFFFFu);
     }
   };
-  auto max_bits = [&](const u16x2& m16, uint32_t m32) __attribute__((always_inline)) {
+  auto max_bits = [&](const bl_u16x2& m16, uint32_t m32) __attribute__((always_inline)) {
     return BF16 ? (uint32_t)max(m16[0], m16[1]) << 16 : m32;
   };
   // x~ of unit u (values v) into the token's LDS row (swizzled) and out
@@ -389,13 +366,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
       __attribute__((always_inline)) {
     uint32_t* rowl = xw + t * kp16 * 4;
     if (BF16) {
-      const uint32_t d0 = quant_mt4(v[0], v[1], v[2], v[3], sv);
-      const uint32_t d1 = quant_mt4(v[4], v[5], v[6], v[7], sv);
+      const uint32_t d0 = quant4_rne(v[0], v[1], v[2], v[3], sv);
+      const uint32_t d1 = quant4_rne(v[4], v[5], v[6], v[7], sv);
       const int q = u >> 1;                           // x~ unit, half u & 1
       *reinterpret_cast<uint2*>(rowl + ((q ^ t) << 2) + ((u & 1) << 1)) = make_uint2(d0, d1);
       if (rowo != nullptr) *reinterpret_cast<uint2*>(rowo + 2 * u) = make_uint2(d0, d1);
     } else {
-      const uint32_t d0 = quant_mt4(v[0], v[1], v[2], v[3], sv);
+      const uint32_t d0 = quant4_rne(v[0], v[1], v[2], v[3], sv);
       const int q = u >> 2;
       rowl[((q ^ t) << 2) + (u & 3)] = d0;
       if (rowo != nullptr) rowo[u] = d0;
@@ -481,7 +458,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
     } else {
       // 3-4 from the held row
       if (t != wave) load_row(t, xr);
-      u16x2 m16 = {0, 0};
+      bl_u16x2 m16 = {0, 0};
       uint32_t m32 = 0;
 #pragma unroll
       for (int j = 0; j < XR; ++j) unit_max(m16, m32, xr[j]);
