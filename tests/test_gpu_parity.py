@@ -525,3 +525,70 @@ def test_graph_replays_match_eager(B):
         work()                                         # eager work between replays
         torch.cuda.synchronize()
     assert not host(ws.buf).any(), "workspace not left zero-filled"
+
+
+def test_graph_replays_match_eager_batched(B):
+    # the batched-decode kernels under graph capture: a fused step on the
+    # multi-token streaming kernel (8 tokens, shared input), a plain product
+    # on it (48 tokens, long rows) and one on the windowed MFMA GEMV (16
+    # tokens), replayed with eager work between the replays, against the
+    # eager bits and the oracle
+    import torch
+    assert B.forward_kernel(48, 1030, 8192) == "stream_mt"
+    assert B.forward_kernel(16, 2560, 2560) == "mfma_gemv"
+    mats = {name: random_case(20 + i, 1, n, k)[0] for i, (name, n, k) in
+            enumerate((("q", 2560, 2560), ("k", 640, 2560), ("mt", 1030, 8192), ("win", 2560, 2560)))}
+    packed = {nm: B.pack_weights(dev(w)) for nm, w in mats.items()}
+    _, x8 = random_case(30, 8, 1, 2560, x_kind="t3")
+    x8d = x_device(x8, "bf16")[0]
+    _, x48 = random_case(31, 48, 1, 8192, x_kind="t3")
+    xq48, s48 = B.quant_act(dev(x48))
+    _, x16 = random_case(32, 16, 1, 2560, x_kind="t3")
+    xq16, s16 = B.quant_act(dev(x16))
+    ys = {"q": torch.empty((8, 2560), dtype=torch.bfloat16, device="cuda"),
+          "k": torch.empty((8, 640), dtype=torch.bfloat16, device="cuda"),
+          "mt": torch.empty((48, 1030), dtype=torch.float32, device="cuda"),
+          "win": torch.empty((16, 2560), dtype=torch.bfloat16, device="cuda")}
+    ws = B.Workspace()
+    step = B.FusedStep([dict(x=x8d, packed=packed[nm][0], gamma=packed[nm][1], n=n, k=2560,
+                             y=ys[nm], relu2=(nm == "k")) for nm, n in (("q", 2560), ("k", 640))],
+                       workspace=ws)
+    assert step.kernel() == "stream_mt"
+
+    def work():
+        step()
+        B.forward(xq48, s48, packed["mt"][0], packed["mt"][1], 1030, 8192, y=ys["mt"], workspace=ws)
+        B.forward(xq16, s16, packed["win"][0], packed["win"][1], 2560, 2560, relu2=True,
+                  y=ys["win"], workspace=ws)
+
+    work()
+    torch.cuda.synchronize()
+    ref = {nm: t.clone() for nm, t in ys.items()}
+    # the eager results against the oracle
+    x8o = x_device(x8, "bf16")[1]                      # the bf16 values x8d holds
+    for nm, xo, relu2, ydt in (("q", x8o, False, "bf16"), ("k", x8o, True, "bf16"),
+                               ("mt", x48, False, "f32"), ("win", x16, True, "bf16")):
+        g = host(packed[nm][1])[0]
+        r = O.forward(xo, mats[nm], relu2=relu2, y_dtype=ydt, gamma=g)
+        assert_y_close(host(ref[nm]), r["y"], ydt, f"eager {nm}")
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        work()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in ys.values():
+            t.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for nm, t in ys.items():
+            a, b = (t.view(torch.int16), ref[nm].view(torch.int16)) if t.dtype == torch.bfloat16 \
+                else (t.view(torch.int32), ref[nm].view(torch.int32))
+            assert torch.equal(a, b), f"replay {rep}, {nm}"
+        work()
+        torch.cuda.synchronize()
