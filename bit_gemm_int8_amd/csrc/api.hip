@@ -71,7 +71,7 @@ static bool mt_plan(int64_t m, int64_t n, int64_t k, FwdPlan* p) {
   const int64_t nc = cdiv(k, kSuperK);
   if (nc < 32 || !((m > 32 && nb <= 128) || (m > 16 && nb <= 16))) return false;
   const int64_t P = mt_row_ranges(m, subs);
-  if (stream_mt_lds_bytes(m, nc, (int)cdiv(subs, P)) > kMtMaxLds) return false;
+  if (stream_mt_lds_bytes(m, nc, (int)cdiv(subs, P), 16) > kMtMaxLds) return false;
   p->kind = 4;
   p->qpl = (int)P;
   p->splits = 1;
@@ -183,7 +183,7 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     if (tiles < kCUs / 2 && nc <= 16 && (nb >= 32 || m >= 512)) {
       const int64_t subs = nb * 4;
       const int64_t P = mt_row_ranges(m, subs);
-      if (stream_mt_lds_bytes(m, nc, (int)cdiv(subs, P)) <= kMtMaxLds) {
+      if (stream_mt_lds_bytes(m, nc, (int)cdiv(subs, P), 16) <= kMtMaxLds) {
         p.kind = 4;
         p.qpl = (int)P;
         p.splits = 1;
@@ -235,6 +235,7 @@ struct FusedPlan {
   int nsub_alloc = 0;                   // its sub-blocks per workgroup, at most
   int64_t nc_max = 0;
   bool mt = false;                      // the multi-token streaming kernel
+  int mt_tok = 16;                      // its tokens per block: 8 or 16
   bool mfma = false;                    // 3..64 tokens: the fused MFMA kernel
   int variant = 0;                      // its wave layout
   int waves = 8;
@@ -342,7 +343,13 @@ static bool mt_fused_plan(const bl_linear* ops, int nops, int64_t m, bool norm, 
   }
   const int64_t xr = cdiv(nu_max, 64);
   if (xr > 16) return false;
-  const int64_t tb = cdiv(m, 16);
+  // 8-token blocks halve each workgroup's quantization (every row range
+  // quantizes its block's rows) at the cost of re-reading the weights twice
+  // as often: faster up to 32 tokens and on rows of >= 16 super-chunks
+  // (MI355X, 2B-class set: 16 / 32 tokens 9-17% per launch; 64 tokens only
+  // the 2560x6912 down product, 11.3 -> 10.2 us)
+  const int tok = (m <= 32 || nc_max >= 16) ? 8 : 16;
+  const int64_t tb = cdiv(m, tok);
   const int64_t budget = (kCUs / tb) < 1 ? 1 : kCUs / tb;
   const int64_t step = tb > 1 ? 8 : 1;
   int64_t ps[kMaxFused], total = 0;
@@ -370,9 +377,10 @@ static bool mt_fused_plan(const bl_linear* ops, int nops, int64_t m, bool norm, 
     const int spw = (int)cdiv(subs, ps[i]);
     if (spw > nsub_alloc) nsub_alloc = spw;
   }
-  const size_t lds = stream_mt_lds_bytes(m, nc_max, nsub_alloc);
+  const size_t lds = stream_mt_lds_bytes(m, nc_max, nsub_alloc, tok);
   if (lds > kMtMaxLds) return false;
   p->mt = true;
+  p->mt_tok = tok;
   p->norm = norm;
   p->xr = (int)xr;
   p->nsub_alloc = nsub_alloc;
@@ -606,7 +614,8 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
   }
   if (plan.mt) {
     args.nsub_alloc = plan.nsub_alloc;
-    const hipError_t e = launch_gemv_stream_mt_fused(args, (int)m, ops[0].x_dtype == BL_BF16,
+    const hipError_t e = launch_gemv_stream_mt_fused(args, (int)m, plan.mt_tok,
+                                                     ops[0].x_dtype == BL_BF16,
                                                      plan.norm, plan.xr, begin, plan.lds,
                                                      reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? BL_OK : BL_ERR_HIP;

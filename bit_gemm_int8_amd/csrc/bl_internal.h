@@ -122,15 +122,17 @@ hipError_t launch_gemv_stream_fused(const FusedArgs& args, int m, bool wide, boo
                                     hipStream_t stream);
 
 // Multi-token streaming GEMV on the matrix cores (x~ of a block of up to 16
-// tokens in LDS, whole 16-row sub-blocks per row range, P row ranges x
-// ceil(m / 16) token blocks of workgroups).
-size_t stream_mt_lds_bytes(int64_t m, int64_t nc, int nsub_alloc);
+// tokens in LDS -- 8 or 16 in the fused form, `tok` --, whole 16-row
+// sub-blocks per row range, P row ranges x ceil(m / tok) token blocks of
+// workgroups).
+size_t stream_mt_lds_bytes(int64_t m, int64_t nc, int nsub_alloc, int tok);
 hipError_t launch_gemv_stream_mt(const int8_t* xq, const float* scale, const uint32_t* packed,
                                  const float* gamma, int64_t m, int64_t n, int64_t k, int P,
                                  bool relu2, bool bf16, void* y, int32_t* acc_out,
                                  hipStream_t stream);
-hipError_t launch_gemv_stream_mt_fused(const FusedArgs& args, int m, bool x_bf16, bool norm,
-                                       int xr, int groups, size_t lds, hipStream_t stream);
+hipError_t launch_gemv_stream_mt_fused(const FusedArgs& args, int m, int tok, bool x_bf16,
+                                       bool norm, int xr, int groups, size_t lds,
+                                       hipStream_t stream);
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t padded_n(int64_t n) { return 64 * cdiv(n, 64); }

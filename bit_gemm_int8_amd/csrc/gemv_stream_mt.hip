@@ -34,7 +34,7 @@
 namespace bl {
 namespace {
 
-constexpr int kTokBlock = 16;
+constexpr int kTokBlock = 16;   // tokens per block of the plain form (the fused form: TBK)
 // Word 3 of a raw buffer resource on gfx9 (untyped 32-bit data; loads past
 // num_records return zero).
 constexpr int kBufferDword3 = 0x00020000;
@@ -99,7 +99,7 @@ __device__ __forceinline__ void mt_prefetch(uint4 (&buf)[D], MtCursor& cur, cons
 // sums[sub - t0][token][row].  Lane (r, g): token min(r, mb - 1) as the
 // second operand (columns of tokens >= mb are dropped), inputs 64 j + 16 g
 // .. + 15 of super-chunk cc, i.e. x~ unit 16 cc + ((4 j + g) ^ token).
-template <int D>
+template <int D, int TBK>
 __device__ __forceinline__ void mt_stream(uint4 (&buf)[D], MtCursor& cur, const uint4* packed,
                                           int nc, int t0, int u0, int u1, int g, int r, int mb,
                                           const uint4* xs, int kp16, int* sums) {
@@ -111,7 +111,7 @@ __device__ __forceinline__ void mt_stream(uint4 (&buf)[D], MtCursor& cur, const 
     if (r < mb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        atomicAdd(&sums[((tc - t0) * kTokBlock + r) * 16 + 4 * g + i], acc[i]);
+        atomicAdd(&sums[((tc - t0) * TBK + r) * 16 + 4 * g + i], acc[i]);
     }
     acc = bl_v4i{0, 0, 0, 0};
   };
@@ -149,6 +149,7 @@ __device__ __forceinline__ void mt_stream(uint4 (&buf)[D], MtCursor& cur, const 
 
 // Outputs of sub-blocks t0 .. t0 + nsub - 1 for tokens tok0 .. tok0 + mb - 1
 // from the LDS sums (64 * acc, exact), four consecutive rows per thread.
+template <int TBK>
 __device__ __forceinline__ void mt_epilogue(const int* sums, const float* fac, int t0, int nsub,
                                             int mb, int tok0, int n, bool relu2, bool ybf16,
                                             bool vec, void* y, int32_t* acc_out, int nt) {
@@ -158,7 +159,7 @@ __device__ __forceinline__ void mt_epilogue(const int* sums, const float* fac, i
     const int sub = qd >> 2, rr = (qd & 3) * 4;
     const int row0 = (t0 + sub) * 16 + rr;
     if (row0 >= n) continue;
-    const bl_v4i a4 = *reinterpret_cast<const bl_v4i*>(sums + (sub * kTokBlock + m) * 16 + rr);
+    const bl_v4i a4 = *reinterpret_cast<const bl_v4i*>(sums + (sub * TBK + m) * 16 + rr);
     const float f = fac[m];
     const int64_t idx = (int64_t)(tok0 + m) * n + row0;
     int v[4];
@@ -242,10 +243,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_kernel(
   }
   __syncthreads();
 
-  mt_stream<D>(buf, cur, packed, nc, t0, u0, u1, g, r, mb, lds, kp16, sums);
+  mt_stream<D, kTokBlock>(buf, cur, packed, nc, t0, u0, u1, g, r, mb, lds, kp16, sums);
   __syncthreads();
-  mt_epilogue(sums, fac, t0, nsub, mb, tok0, n, relu2 != 0, ybf16 != 0, vec_out != 0, y,
-              acc_out, NT);
+  mt_epilogue<kTokBlock>(sums, fac, t0, nsub, mb, tok0, n, relu2 != 0, ybf16 != 0, vec_out != 0,
+                         y, acc_out, NT);
 }
 
 // ----------------------------------------------------- fused decode step --
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_kernel(
 //      into LDS, zero past K; the entry's first row range also writes x~
 //      and s out when asked.
 // Rows must be whole 16-byte units at 16-byte alignment (checked on the host).
-template <int WAVES, int D, int XR, bool BF16, bool NORM>
+template <int TBK, int WAVES, int D, int XR, bool BF16, bool NORM>
 __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
     int m_all, int nseg, int wb1, int wb2, int wb3, int wb4, int wb5, int wb6, int wb7, int wb8,
     int wb9, int wb10, int wb11, int wb12, FusedArgs args) {
@@ -286,12 +287,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
       if (i < nseg && bid >= args.wg_begin[i]) si = i;
   }
   const FusedSeg& sg = args.seg[si];
-  const int TB = (m_all + kTokBlock - 1) / kTokBlock;
+  const int TB = (m_all + TBK - 1) / TBK;
   const int P = sg.splits / TB;
   const MtWork wk = mt_work(bid - sg.wg_begin, P, TB);
-  const int tok0 = kTokBlock * wk.tb;
-  const int mb = min(kTokBlock, m_all - tok0);
-  const int mba = min(kTokBlock, m_all);
+  const int tok0 = TBK * wk.tb;
+  const int mb = min(TBK, m_all - tok0);
+  const int mba = min(TBK, m_all);
   const int nc = sg.nc, n = sg.n, k = sg.k;
   const int S = ((n + kRowBlock - 1) / kRowBlock) * 4;
   const int t0 = (int)((int64_t)S * wk.p / P), t1 = (int)((int64_t)S * (wk.p + 1) / P);
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
   const int u0 = (int)((int64_t)units * wave / WAVES);
   const int u1 = (int)((int64_t)units * (wave + 1) / WAVES);
   int* sums = reinterpret_cast<int*>(lds + mba * kp16);
-  float* fac = reinterpret_cast<float*>(sums + args.nsub_alloc * kTokBlock * 16);
+  float* fac = reinterpret_cast<float*>(sums + args.nsub_alloc * TBK * 16);
   const uint4* packed = reinterpret_cast<const uint4*>(sg.packed);
   const int nu = k / EPU;                             // units per row (whole units)
   const bool nrm = NORM && sg.rmsnorm();
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
   MtCursor cur = mt_cursor(packed, nc, t0, u0, u1, g, r);
   mt_prefetch<D>(buf, cur, packed, nc, g, r);
   const float gm = *sg.gamma;
-  for (int i = threadIdx.x; i < nsub * kTokBlock * 16; i += NT) sums[i] = 0;
+  for (int i = threadIdx.x; i < nsub * TBK * 16; i += NT) sums[i] = 0;
 
   // the EPU values of a 16-byte activation unit as fp32 bit patterns
   auto expand = [&](const uint4& x, uint32_t (&v)[8]) __attribute__((always_inline)) {
@@ -486,12 +487,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
   }
   __syncthreads();
 
-  mt_stream<D>(buf, cur, packed, nc, t0, u0, u1, g, r, mb, lds, kp16, sums);
+  mt_stream<D, TBK>(buf, cur, packed, nc, t0, u0, u1, g, r, mb, lds, kp16, sums);
   __syncthreads();
   const bool ybf = sg.y_bf16();
   const bool vec = (n & 3) == 0 && ((uintptr_t)sg.y & (ybf ? 7 : 15)) == 0 &&
                    (sg.acc_out == nullptr || ((uintptr_t)sg.acc_out & 15) == 0);
-  mt_epilogue(sums, fac, t0, nsub, mb, tok0, n, sg.relu2(), ybf, vec, sg.y, sg.acc_out, NT);
+  mt_epilogue<TBK>(sums, fac, t0, nsub, mb, tok0, n, sg.relu2(), ybf, vec, sg.y, sg.acc_out, NT);
 }
 
 template <int WAVES, int D, int XR>
@@ -503,11 +504,11 @@ void run_mt(const int8_t* xq, const float* scale, const uint32_t* packed, const 
       mba, relu2, bf16, vec_out, y, acc_out);
 }
 
-template <int WAVES, int D, int XR, bool NORM>
+template <int TBK, int WAVES, int D, int XR, bool NORM>
 void run_mt_fused(const FusedArgs& args, int m, const int (&wb)[13], int groups, size_t lds,
                   bool bf16, hipStream_t stream) {
 #define BL_MF(B)                                                                               \
-  gemv_stream_mt_fused_kernel<WAVES, D, XR, B, NORM><<<groups, 64 * WAVES, lds, stream>>>(     \
+  gemv_stream_mt_fused_kernel<TBK, WAVES, D, XR, B, NORM><<<groups, 64 * WAVES, lds, stream>>>( \
       m, args.nseg, wb[1], wb[2], wb[3], wb[4], wb[5], wb[6], wb[7], wb[8], wb[9], wb[10],     \
       wb[11], wb[12], args)
   if (bf16)
@@ -519,9 +520,9 @@ void run_mt_fused(const FusedArgs& args, int m, const int (&wb)[13], int groups,
 
 }  // namespace
 
-size_t stream_mt_lds_bytes(int64_t m, int64_t nc, int nsub_alloc) {
-  const int64_t mba = m < kTokBlock ? m : kTokBlock;
-  return (size_t)(mba * nc * 256) + (size_t)nsub_alloc * kTokBlock * 16 * 4 + kTokBlock * 4;
+size_t stream_mt_lds_bytes(int64_t m, int64_t nc, int nsub_alloc, int tok) {
+  const int64_t mba = m < tok ? m : tok;
+  return (size_t)(mba * nc * 256) + (size_t)nsub_alloc * tok * 16 * 4 + tok * 4;
 }
 
 hipError_t launch_gemv_stream_mt(const int8_t* xq, const float* scale, const uint32_t* packed,
@@ -534,7 +535,7 @@ hipError_t launch_gemv_stream_mt(const int8_t* xq, const float* scale, const uin
   if (P < 1 || P > S || m < 1) return hipErrorInvalidValue;
   const int nsub_alloc = (int)cdiv(S, P);
   const int mba = (int)(m < kTokBlock ? m : kTokBlock);
-  const size_t lds = stream_mt_lds_bytes(m, nc, nsub_alloc);
+  const size_t lds = stream_mt_lds_bytes(m, nc, nsub_alloc, kTokBlock);
   const int vec_out = n % 4 == 0 && (uintptr_t)y % (bf16 ? 8 : 16) == 0 &&
                       (acc_out == nullptr || (uintptr_t)acc_out % 16 == 0);
   const int xr = (int)cdiv((int64_t)mba * nc * 16, 64 * 16);
@@ -551,16 +552,24 @@ hipError_t launch_gemv_stream_mt(const int8_t* xq, const float* scale, const uin
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_stream_mt_fused(const FusedArgs& args, int m, bool x_bf16, bool norm,
-                                       int xr, int groups, size_t lds, hipStream_t stream) {
+hipError_t launch_gemv_stream_mt_fused(const FusedArgs& args, int m, int tok, bool x_bf16,
+                                       bool norm, int xr, int groups, size_t lds,
+                                       hipStream_t stream) {
   int wb[13];
   for (int i = 1; i < 13; ++i) wb[i] = i < args.nseg ? args.wg_begin[i] : INT_MAX;
   wb[0] = 0;
-#define BL_MTF(XR)                                                                 \
+  if (tok != 8 && tok != 16) return hipErrorInvalidValue;
+#define BL_MTT(T, XR)                                                              \
   if (norm)                                                                        \
-    run_mt_fused<16, 3, XR, true>(args, m, wb, groups, lds, x_bf16, stream);       \
+    run_mt_fused<T, 16, 3, XR, true>(args, m, wb, groups, lds, x_bf16, stream);    \
   else                                                                             \
-    run_mt_fused<16, 3, XR, false>(args, m, wb, groups, lds, x_bf16, stream)
+    run_mt_fused<T, 16, 3, XR, false>(args, m, wb, groups, lds, x_bf16, stream)
+#define BL_MTF(XR)                                                                 \
+  if (tok == 8) {                                                                  \
+    BL_MTT(8, XR);                                                                 \
+  } else {                                                                         \
+    BL_MTT(16, XR);                                                                \
+  }
   if (xr <= 4) {
     BL_MTF(4);
   } else if (xr <= 8) {
@@ -571,6 +580,7 @@ hipError_t launch_gemv_stream_mt_fused(const FusedArgs& args, int m, bool x_bf16
     return hipErrorInvalidValue;
   }
 #undef BL_MTF
+#undef BL_MTT
   return hipGetLastError();
 }
 
