@@ -343,32 +343,60 @@ static bool mt_fused_plan(const bl_linear* ops, int nops, int64_t m, bool norm, 
   }
   const int64_t xr = cdiv(nu_max, 64);
   if (xr > 16) return false;
-  // 8-token blocks halve each workgroup's quantization (every row range
-  // quantizes its block's rows) at the cost of re-reading the weights twice
-  // as often: faster up to 32 tokens and on rows of >= 16 super-chunks
-  // (MI355X, 2B-class set: 16 / 32 tokens 9-17% per launch; 64 tokens only
-  // the 2560x6912 down product, 11.3 -> 10.2 us)
-  const int tok = (m <= 32 || nc_max >= 16) ? 8 : 16;
+  // Row ranges for tok tokens per block: about one workgroup per CU over the
+  // ceil(m / tok) blocks, shared in proportion to the entries' packed bytes,
+  // multiples of 8 when there are several blocks.
+  auto allocate = [&](int tok, int64_t (&ps)[kMaxFused]) {
+    const int64_t tb = cdiv(m, tok);
+    const int64_t budget = (kCUs / tb) < 1 ? 1 : kCUs / tb;
+    const int64_t step = tb > 1 ? 8 : 1;
+    int64_t total = 0;
+    for (int i = 0; i < nops; ++i) {
+      const int64_t subs = cdiv(ops[i].n, kRowBlock) * 4;
+      const int64_t w = subs * cdiv(ops[i].k, kSuperK);
+      int64_t pi = (budget * w + units / 2) / units;
+      if (pi >= step) pi -= pi % step;
+      ps[i] = pi < 1 ? 1 : pi > subs ? subs : pi;
+      total += ps[i];
+    }
+    while (total > budget) {
+      int big = 0;
+      for (int i = 1; i < nops; ++i) big = ps[i] > ps[big] ? i : big;
+      const int64_t dec = ps[big] > step ? step : ps[big] - 1;
+      if (dec <= 0) break;
+      ps[big] -= dec;
+      total -= dec;
+    }
+  };
+  // Tokens per block, 8 or 16: every row range quantizes its block's rows
+  // (tok * K elements of VALU work per workgroup), and every block re-reads
+  // the weights.  The plan takes the block size whose slowest workgroup
+  // costs least, with one 1 KiB weight unit streamed worth 620 elements
+  // quantized (fitted to per-launch times on MI355X over the 2B- and
+  // 100B-class groups at 16, 32 and 64 tokens, where it picks the faster
+  // size every time: 8-token blocks are 9-17% faster on the 2B set at 16-32
+  // tokens and win at 64 tokens on short outputs and long rows; 16-token
+  // blocks win on the large 100B outputs).
+  int tok = 16;
+  int64_t ps[kMaxFused];
+  double best = -1.0;
+  for (int t : {16, 8}) {
+    int64_t q[kMaxFused];
+    allocate(t, q);
+    double cost = 0.0;
+    for (int i = 0; i < nops; ++i) {
+      const int64_t subs = cdiv(ops[i].n, kRowBlock) * 4;
+      const double c = (double)(t < m ? t : m) * (double)ops[i].k / 620.0 +
+                       (double)(cdiv(subs, q[i]) * cdiv(ops[i].k, kSuperK));
+      if (c > cost) cost = c;
+    }
+    if (best < 0.0 || cost < best) {
+      best = cost;
+      tok = t;
+      for (int i = 0; i < nops; ++i) ps[i] = q[i];
+    }
+  }
   const int64_t tb = cdiv(m, tok);
-  const int64_t budget = (kCUs / tb) < 1 ? 1 : kCUs / tb;
-  const int64_t step = tb > 1 ? 8 : 1;
-  int64_t ps[kMaxFused], total = 0;
-  for (int i = 0; i < nops; ++i) {
-    const int64_t subs = cdiv(ops[i].n, kRowBlock) * 4;
-    const int64_t w = subs * cdiv(ops[i].k, kSuperK);
-    int64_t pi = (budget * w + units / 2) / units;
-    if (pi >= step) pi -= pi % step;
-    ps[i] = pi < 1 ? 1 : pi > subs ? subs : pi;
-    total += ps[i];
-  }
-  while (total > budget) {
-    int big = 0;
-    for (int i = 1; i < nops; ++i) big = ps[i] > ps[big] ? i : big;
-    const int64_t dec = ps[big] > step ? step : ps[big] - 1;
-    if (dec <= 0) break;
-    ps[big] -= dec;
-    total -= dec;
-  }
   int groups = 0, nsub_alloc = 1;
   for (int i = 0; i < nops; ++i) {
     const int64_t subs = cdiv(ops[i].n, kRowBlock) * 4;
