@@ -128,20 +128,66 @@ __device__ __forceinline__ float rms_apply(float x, float r, float w) {
 // |v s| <= 127 (1 + 2^-24), whose fp32 rounding is at most 127 + 2^-17, so
 // rint stays within [-127, 127].  Adding 1.5 * 2^23 rounds a product of
 // magnitude below 2^22 to the nearest integer, ties to even, in the low
-// mantissa bits; three v_perm pack the low bytes.  The product must be
-// rounded to fp32 before that add: contracted into one fma, rint would see
-// the exact product (__fmul_rn is a plain multiply, and device code
-// contracts by default), hence contract(off).
+// mantissa bits, whose low byte is the code in two's complement; each add
+// writes that byte straight into its byte of the result (SDWA dst_sel
+// BYTE_i, the other bytes kept), so a value costs two VALU operations and
+// no byte permutes.  The product must be rounded to fp32 before that add:
+// contracted into one fma, rint would see the exact product (__fmul_rn is a
+// plain multiply, and device code contracts by default), hence
+// contract(off) -- the add sits in asm, which no contraction crosses anyway.
 __device__ __forceinline__ uint32_t quant4_rne(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                                float s) {
 #pragma clang fp contract(off)
-  uint32_t q[4] = {a, b, c, d};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    q[i] = __float_as_uint(__fmul_rn(__uint_as_float(q[i]), s) + 12582912.0f);
-  const uint32_t lo = __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u);
-  const uint32_t hi = __builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u);
-  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  const float magic = 12582912.0f;
+  const float p0 = __fmul_rn(__uint_as_float(a), s), p1 = __fmul_rn(__uint_as_float(b), s);
+  const float p2 = __fmul_rn(__uint_as_float(c), s), p3 = __fmul_rn(__uint_as_float(d), s);
+  uint32_t r;
+  asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD "
+      "src1_sel:DWORD" : "=v"(r) : "v"(p0), "s"(magic));
+  asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+      "src1_sel:DWORD" : "+v"(r) : "v"(p1), "s"(magic));
+  asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+      "src1_sel:DWORD" : "+v"(r) : "v"(p2), "s"(magic));
+  asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD "
+      "src1_sel:DWORD" : "+v"(r) : "v"(p3), "s"(magic));
+  return r;
+}
+
+// Running max of |x| over the two bf16 values of a word, one VALU operation
+// per word: v_pk_maximum3_f16(acc, w, -w) reads each 16-bit lane as fp16.
+// Both formats put sign, exponent and mantissa in that order, so for bit
+// patterns that are finite in fp16 (fp16 denormals included: the mode keeps
+// them) the fp16 order of the magnitudes is the bf16 order.  A bf16
+// magnitude above 0x7C00 (|x| > 2^121, or not finite) is a NaN in fp16 and
+// makes the accumulator a NaN, which absmax_bf16x2_bits reports.
+__device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t acc, uint32_t w) {
+  uint32_t r;
+  asm("v_pk_maximum3_f16 %0, %1, %2, %2 neg_lo:[0,0,1] neg_hi:[0,0,1]"
+      : "=v"(r) : "v"(acc), "v"(w));
+  return r;
+}
+constexpr uint32_t kAbsmaxInexact = 0xFFFFFFFFu;
+// The larger lane of an absmax_bf16x2 accumulator (started at 0) as fp32
+// bits (a bf16 is the top half of its fp32), or kAbsmaxInexact when a lane
+// saw a magnitude that fp16 cannot order; that flag exceeds every result,
+// so it survives a max reduction, and the caller then takes the exact
+// sign-cleared 16-bit max.
+__device__ __forceinline__ uint32_t absmax_bf16x2_bits(uint32_t acc) {
+  const uint32_t m = max(acc & 0xFFFFu, acc >> 16);
+  return m > 0x7C00u ? kAbsmaxInexact : m << 16;
+}
+// Exact running max of the sign-cleared 16-bit lanes (the path for the
+// flagged case).
+__device__ __forceinline__ bl_u16x2 absmax_bf16x2_exact(bl_u16x2 acc, uint32_t w) {
+  return __builtin_elementwise_max(acc, __builtin_bit_cast(bl_u16x2, w & 0x7FFF7FFFu));
+}
+// Running max of |x| over fp32 values, two per VALU operation
+// (v_max3_f32 with |.| on the new operands); for finite values the result's
+// bits are the largest sign-cleared bit pattern.
+__device__ __forceinline__ uint32_t absmax_f32x2(uint32_t acc, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(acc), "v"(a), "v"(b));
+  return r;
 }
 
 // Rescale factor gamma / s as the correctly rounded fp32 quotient (the fp64

@@ -217,8 +217,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_kernel(
 //   1. the activations are loaded first (XR 16-byte units per thread and
 //      token, clamped: the units past the row repeat the last one, which the
 //      max ignores), then the first D weight units;
-//   2. beta = max|x| per token (sign-cleared fp32 bits, DPP in the wave, LDS
-//      across waves) and s = fp32(127 / max(beta, eps)) exactly as
+//   2. beta = max|x| per token (absmax_bf16x2 / absmax_f32x2, DPP in the
+//      wave, LDS across waves) and s = fp32(127 / max(beta, eps)) exactly as
 //      bitlinear_quant_act computes it;
 //   3. x~ = clamp(rint(fp32(x * s))) of every held unit into LDS
 //      (quant4_rne, whose clamp cannot bind), zero past K; every workgroup
@@ -353,43 +353,71 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_fused_kernel(
     }
   };
 
-  // 2. beta and s per token (bf16 without RMSNorm: the magnitudes of a word's
-  //    two activations as 16-bit lanes, v_pk_max_u16, widened at the end:
-  //    the top half of an fp32 is its bf16)
+  // 2. beta and s per token: bf16 without RMSNorm one v_pk_maximum3_f16 per
+  //    word (absmax_bf16x2; a magnitude above 2^121 flags the block, which
+  //    then takes the exact sign-cleared 16-bit max), fp32 values two per
+  //    v_max3_f32 (absmax_f32x2); DPP in the wave, LDS across waves
+  const bool pk = BF16 && !(NORM && nrm);
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     uint32_t mx = 0;
-    if (BF16 && !(NORM && nrm)) {
-      bl_u16x2 m16 = {0, 0};
+    if (pk) {
+      uint32_t acc[2] = {0u, 0u};
 #pragma unroll
       for (int j = 0; j < XR; ++j) {
-        const uint32_t w[4] = {xr[m][j].x, xr[m][j].y, xr[m][j].z, xr[m][j].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(bl_u16x2, w[e] & 0x7FFF7FFFu));
+        acc[0] = absmax_bf16x2(acc[0], xr[m][j].x); acc[1] = absmax_bf16x2(acc[1], xr[m][j].y);
+        acc[0] = absmax_bf16x2(acc[0], xr[m][j].z); acc[1] = absmax_bf16x2(acc[1], xr[m][j].w);
       }
-      mx = (uint32_t)max(m16[0], m16[1]) << 16;
+      mx = absmax_bf16x2_bits(absmax_bf16x2(acc[0], acc[1]));
     } else {
 #pragma unroll
       for (int j = 0; j < XR; ++j) {
         uint32_t v[8];
         vals(m, j, v);
 #pragma unroll
-        for (int e = 0; e < EPU; ++e) mx = max(mx, v[e] & 0x7FFFFFFFu);
+        for (int e = 0; e < EPU; e += 2) mx = absmax_f32x2(mx, v[e], v[e + 1]);
       }
     }
     mx = wave_max_u32(mx);
     if (lane == 0) red[wave][m] = mx;
   }
   __syncthreads();
-  float sv[M];
+  uint32_t bmax[M];
+  bool inexact = false;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     uint32_t b = red[0][m];
 #pragma unroll
     for (int w = 1; w < WAVES; ++w) b = max(b, red[w][m]);
-    sv[m] = (float)(127.0 / (double)fmaxf(__uint_as_float(b), args.eps));
+    bmax[m] = b;
+    inexact = inexact || (pk && b == kAbsmaxInexact);
   }
+  if (inexact) {                                      // uniform: every thread read the same
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      bl_u16x2 m16 = {0, 0};
+#pragma unroll
+      for (int j = 0; j < XR; ++j) {
+        m16 = absmax_bf16x2_exact(m16, xr[m][j].x); m16 = absmax_bf16x2_exact(m16, xr[m][j].y);
+        m16 = absmax_bf16x2_exact(m16, xr[m][j].z); m16 = absmax_bf16x2_exact(m16, xr[m][j].w);
+      }
+      const uint32_t mx = wave_max_u32((uint32_t)max(m16[0], m16[1]) << 16);
+      if (lane == 0) red[wave][m] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      uint32_t b = red[0][m];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) b = max(b, red[w][m]);
+      bmax[m] = b;
+    }
+  }
+  float sv[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    sv[m] = (float)(127.0 / (double)fmaxf(__uint_as_float(bmax[m]), args.eps));
 
   // 3. x~ into LDS (bytes EPU*u .. of token m), zero from K to K_pad
   uint32_t* xw = reinterpret_cast<uint32_t*>(lds);

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_kernel(
 //      r = rms_factor(sum, K, eps), and y = fp32(fp32(x * r) * w) replaces
 //      x below; these rows are read in three passes, four units per lane
 //      at a time (from the caches after the first), with the gain;
-//   3. beta = max|x| (sign-cleared fp32 bits, a wave max) and
+//   3. beta = max|x| (absmax_bf16x2 / absmax_f32x2, then a wave max) and
 //      s = fp32(127 / max(beta, eps)) exactly as bitlinear_quant_act;
 //   4. x~ = clamp(rint(fp32(x * s))) (quant4_rne, whose clamp cannot bind)
 //      into LDS, zero past K; the entry's first row range also writes x~
@@ -344,21 +344,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
       v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
     }
   };
-  // running max of |value| over units: sign-cleared bits compare as
-  // magnitudes; bf16 pairs as two 16-bit lanes (v_pk_max_u16), widened to
-  // fp32 bits at the end (the top half of an fp32 is its bf16)
-  auto unit_max = [&](bl_u16x2& m16, uint32_t& m32, const uint4& x) __attribute__((always_inline)) {
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (BF16)
-        m16 = __builtin_elementwise_max(m16, __builtin_bit_cast(bl_u16x2, w[e] & 0x7FFF7FFFu));
-      else
-        m32 = max(m32, w[e] & 0x7FFFFFFFu);
+  // running max of |value| over units, two accumulators: bf16 words one
+  // v_pk_maximum3_f16 each (absmax_bf16x2), fp32 pairs one v_max3_f32
+  auto unit_max = [&](uint32_t (&acc)[2], const uint4& x) __attribute__((always_inline)) {
+    if (BF16) {
+      acc[0] = absmax_bf16x2(acc[0], x.x); acc[1] = absmax_bf16x2(acc[1], x.y);
+      acc[0] = absmax_bf16x2(acc[0], x.z); acc[1] = absmax_bf16x2(acc[1], x.w);
+    } else {
+      acc[0] = absmax_f32x2(acc[0], x.x, x.y); acc[1] = absmax_f32x2(acc[1], x.z, x.w);
     }
   };
-  auto max_bits = [&](const bl_u16x2& m16, uint32_t m32) __attribute__((always_inline)) {
-    return BF16 ? (uint32_t)max(m16[0], m16[1]) << 16 : m32;
+  auto max_bits = [&](const uint32_t (&acc)[2]) __attribute__((always_inline)) {
+    return BF16 ? absmax_bf16x2_bits(absmax_bf16x2(acc[0], acc[1]))
+                : absmax_f32x2(acc[0], acc[1], acc[1]);
   };
   // x~ of unit u (values v) into the token's LDS row (swizzled) and out
   uint32_t* xw = reinterpret_cast<uint32_t*>(lds);
@@ -437,7 +435,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
           uint32_t v[8];
           normed(xv[c], min(ub + lane + 64 * c, nu - 1), rn, v);
 #pragma unroll
-          for (int e = 0; e < EPU; ++e) mx = max(mx, v[e] & 0x7FFFFFFFu);
+          for (int e = 0; e < EPU; e += 2) mx = absmax_f32x2(mx, v[e], v[e + 1]);
         }
       }
       mx = wave_max_u32(mx);
@@ -459,11 +457,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
     } else {
       // 3-4 from the held row
       if (t != wave) load_row(t, xr);
-      bl_u16x2 m16 = {0, 0};
-      uint32_t m32 = 0;
+      uint32_t acc[2] = {0u, 0u};
 #pragma unroll
-      for (int j = 0; j < XR; ++j) unit_max(m16, m32, xr[j]);
-      const uint32_t mx = wave_max_u32(max_bits(m16, m32));
+      for (int j = 0; j < XR; ++j) unit_max(acc, xr[j]);
+      uint32_t mx = wave_max_u32(max_bits(acc));
+      if (BF16 && mx == kAbsmaxInexact) {             // |x| > 2^121 somewhere: exact max
+        bl_u16x2 m16 = {0, 0};
+#pragma unroll
+        for (int j = 0; j < XR; ++j) {
+          m16 = absmax_bf16x2_exact(m16, xr[j].x); m16 = absmax_bf16x2_exact(m16, xr[j].y);
+          m16 = absmax_bf16x2_exact(m16, xr[j].z); m16 = absmax_bf16x2_exact(m16, xr[j].w);
+        }
+        mx = wave_max_u32((uint32_t)max(m16[0], m16[1]) << 16);
+      }
       sv = (float)(127.0 / (double)fmaxf(__uint_as_float(mx), args.eps));
 #pragma unroll
       for (int j = 0; j < XR; ++j) {

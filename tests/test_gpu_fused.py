@@ -156,6 +156,70 @@ def test_fused_c2_decode_set(B, m):
     _check(B, ops, refs)
 
 
+def _extreme_rows(m, k, seed):
+    """bf16 bit patterns [m, k] of t3 activations with rows whose magnitudes
+    test the fused prologue's absmax: above 2^121 (past what fp16 orders:
+    the exact path), exactly 2^121 (fp16's infinity pattern), all in fp16's
+    denormal range (below 2^-119, with a max above the smallest eps), signed
+    zeros, and a negative max in the last unit of the row."""
+    from datagen import to_bf16_bits
+    rng = np.random.default_rng(seed)
+    _, x = random_case(seed, m, 1, k, x_kind="t3")
+    bits = to_bf16_bits(x)
+    kinds = ["above", "tiny", "at", "above_neg", "zeros", "last"]
+    for i in range(m):
+        kind = kinds[i % len(kinds)] if i < 2 * len(kinds) else "plain"
+        j = int(rng.integers(0, k))
+        if kind == "above":
+            bits[i, j] = 0x7C01
+        elif kind == "at":
+            bits[i, j] = 0xFC00                         # -2^121
+        elif kind == "above_neg":
+            bits[i, j] = 0xFC80                         # -2^122
+        elif kind == "tiny":
+            bits[i] = rng.integers(0, 1 << 16, k).astype(np.uint16) & 0x83FF
+            bits[i, j] = 0x03F0                         # ~1.4e-36, above the smallest eps
+        elif kind == "zeros":
+            bits[i] = np.where(rng.integers(0, 2, k) == 1, 0x8000, 0x0000).astype(np.uint16)
+            bits[i, j] = 0xBF80                         # -1
+        elif kind == "last":
+            bits[i, k - 1] = 0xC2F0                     # -120, in the row's last unit
+    return bits
+
+
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+@pytest.mark.parametrize("m", [1, 2, 5, 16, 40])
+def test_fused_absmax_extremes(B, m, xdt):
+    """The fused prologue's absmax (fp16 maximum of bf16 pairs with its
+    exact fallback, fp32 max3 of magnitudes) against the oracle on extreme
+    rows, at 1-2 tokens (streaming kernel) and 3-64 (multi-token kernel),
+    with the smallest activation eps the ABI accepts."""
+    import torch
+    from datagen import bf16_bits_to_f32
+    from test_oracle_pins import EPS_MIN
+    n, k = 1040, 1024
+    bits = _extreme_rows(m, k, 7100 + m)
+    xo = bf16_bits_to_f32(bits)
+    xd = dev(bits.view(np.int16)).view(torch.bfloat16) if xdt == "bf16" else dev(xo)
+    w, _ = random_case(7200 + m, 1, n, k)
+    packed, gamma = B.pack_weights(dev(w))
+    g = host(gamma)[0]
+    ops = [dict(x=xd, packed=packed, gamma=gamma, n=n, k=k,
+                y=torch.empty((m, n), dtype=torch.float32, device="cuda"),
+                acc_out=torch.empty((m, n), dtype=torch.int32, device="cuda"),
+                xq_out=torch.full((m, O.padded_k(k)), 99, dtype=torch.int8, device="cuda"),
+                scale_out=torch.empty(m, dtype=torch.float32, device="cuda"))]
+    step = B.FusedStep(ops, eps=float(EPS_MIN))
+    log(f"absmax extremes m={m} x={xdt} kernel={step.kernel()}")
+    step()
+    r = O.forward(xo, w, gamma=g, act_eps=EPS_MIN, y_dtype="f32")
+    o = ops[0]
+    np.testing.assert_array_equal(host(o["scale_out"]), r["s"])
+    np.testing.assert_array_equal(host(o["xq_out"])[:, :k], r["xq"])
+    np.testing.assert_array_equal(host(o["acc_out"]), r["acc"])
+    assert_y_close(host(o["y"]), r["y"], "f32", f"extremes m={m} {xdt}")
+
+
 def test_fused_rejects(B):
     import torch
     m = B.BL_FUSED_MAX_M + 1
