@@ -49,7 +49,8 @@ BL_MAX_FUSED = 16
 BL_FUSED_MAX_M = 64
 BL_MAX_MULTI = 16
 # kernels a call can run (bitlinear_forward_kernel / _fused_kernel)
-KERNEL_NAMES = {0: "dot4_gemv", 1: "gemm", 2: "mfma_gemv", 3: "stream_gemv", 4: "stream_mt"}
+KERNEL_NAMES = {0: "dot4_gemv", 1: "gemm", 2: "mfma_gemv", 3: "stream_gemv", 4: "stream_mt",
+                5: "two_pass"}
 
 
 class BLLinear(ctypes.Structure):

@@ -245,6 +245,11 @@ struct FusedPlan {
   size_t ws_bytes = 0;
   int splits[kMaxFused] = {};
   size_t slot_off[kMaxFused] = {};      // bytes
+  bool two_pass = false;                // quantize each input once, then each product's forward
+  int src[kMaxFused] = {};              // two_pass: the entry whose x~ and s an entry reads
+  size_t xq_off[kMaxFused] = {};        // two_pass: workspace offsets of a source's x~ and s
+  size_t s_off[kMaxFused] = {};         //   (unused where the entry gives xq_out / scale_out)
+  size_t scratch_off = 0;               // two_pass: where the x~ / s scratch starts
 };
 
 // The fused step on the streaming kernel: every entry's rows whole aligned
@@ -419,6 +424,60 @@ static bool mt_fused_plan(const bl_linear* ops, int nops, int64_t m, bool norm, 
   return true;
 }
 
+// Two entries read the same activations when x, its dtype, K and the
+// RMSNorm settings agree (their x~ and s are then the same).
+static bool same_input(const bl_linear& a, const bl_linear& b) {
+  if (a.x != b.x || a.x_dtype != b.x_dtype || a.k != b.k || (a.rmsnorm != 0) != (b.rmsnorm != 0))
+    return false;
+  return a.rmsnorm == 0 || (a.norm_weight == b.norm_weight &&
+                            __builtin_bit_cast(uint32_t, a.norm_eps) ==
+                                __builtin_bit_cast(uint32_t, b.norm_eps));
+}
+
+// The fused step for activation rows of more than 16 KiB at 3 or more
+// tokens, which a multi-token workgroup cannot hold in registers and which
+// would cost every workgroup tok * K elements of quantization: each distinct
+// input is quantized once (the bitlinear_quant_act or
+// bitlinear_rmsnorm_quant_act kernel; an entry that asks for xq_out or
+// scale_out gets its own quantization, written there), then every product
+// runs its bitlinear_forward plan on that x~, and a fill kernel clears the
+// x~ / s scratch, so the workspace is left zero-filled as its contract
+// requires.  Workspace: the largest forward split-K slot region, then the
+// scratch, each 256-byte aligned.
+static void two_pass_plan(const bl_linear* ops, int nops, int64_t m, FusedPlan* p) {
+  auto up256 = [](size_t b) { return (b + 255) / 256 * 256; };
+  size_t slots = 0;
+  for (int i = 0; i < nops; ++i) {
+    const size_t w = forward_plan(m, ops[i].n, ops[i].k).ws_bytes;
+    if (w > slots) slots = w;
+  }
+  size_t off = up256(slots);
+  p->scratch_off = off;
+  for (int i = 0; i < nops; ++i) {
+    const bl_linear& o = ops[i];
+    const bool own = o.xq_out != nullptr || o.scale_out != nullptr;
+    int src = i;
+    if (!own)
+      for (int j = 0; j < i && src == i; ++j)
+        if (p->src[j] == j && ops[j].xq_out == nullptr && ops[j].scale_out == nullptr &&
+            same_input(ops[j], o))
+          src = j;
+    p->src[i] = src;
+    p->splits[i] = 1;
+    if (src != i) continue;
+    if (o.xq_out == nullptr) {
+      p->xq_off[i] = off;
+      off += up256((size_t)(m * padded_k(o.k)));
+    }
+    if (o.scale_out == nullptr) {
+      p->s_off[i] = off;
+      off += up256((size_t)(4 * m));
+    }
+  }
+  p->two_pass = true;
+  p->ws_bytes = off;
+}
+
 FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   // T = super-chunks a workgroup should stream: the set's total over ~512
   // groups, kept within [8, 32].  Entries with up to 2T super-chunks keep
@@ -438,6 +497,16 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   for (int i = 0; i < nops; ++i) norm = norm || ops[i].rmsnorm != 0;
   if (m <= 2 && stream_fused_plan(ops, nops, m, norm, &p)) return p;
   if ((m >= 3 || norm) && m <= BL_FUSED_MAX_M && mt_fused_plan(ops, nops, m, norm, &p)) return p;
+  if (m >= 3) {
+    bool long_rows = false;                          // an activation row of more than 16 KiB
+    for (int i = 0; i < nops; ++i)
+      long_rows = long_rows || ops[i].k * (ops[i].x_dtype == BL_BF16 ? 2 : 4) > 16 * 1024;
+    if (long_rows) {
+      p.norm = norm;
+      two_pass_plan(ops, nops, m, &p);
+      return p;
+    }
+  }
   // RMSNorm tables the streaming kernel does not take run on the matrix-core
   // fused kernel at any token count
   p.norm = norm;
@@ -602,6 +671,40 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
     if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return BL_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return BL_ERR_MISALIGNED;
   }
+  if (plan.two_pass) {
+    const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    char* ws = reinterpret_cast<char*>(workspace);
+    const int8_t* xq[kMaxFused] = {};
+    const float* sc[kMaxFused] = {};
+    for (int i = 0; i < nops; ++i) {
+      const bl_linear& o = ops[i];
+      if (plan.src[i] != i) continue;
+      int8_t* q = o.xq_out != nullptr ? o.xq_out : reinterpret_cast<int8_t*>(ws + plan.xq_off[i]);
+      float* s = o.scale_out != nullptr ? o.scale_out : reinterpret_cast<float*>(ws + plan.s_off[i]);
+      const bool xb = o.x_dtype == BL_BF16;
+      const hipError_t e =
+          o.rmsnorm ? launch_rmsnorm_quant(o.x, xb, m, o.k, padded_k(o.k), o.norm_weight,
+                                           o.norm_eps, eps, q, s, hs)
+                    : launch_quant_act(o.x, xb, m, o.k, padded_k(o.k), eps, q, s, hs);
+      if (e != hipSuccess) return BL_ERR_HIP;
+      xq[i] = q;
+      sc[i] = s;
+    }
+    for (int i = 0; i < nops; ++i) {
+      const bl_linear& o = ops[i];
+      const int j = plan.src[i];
+      const FwdPlan fp = forward_plan(m, o.n, o.k);
+      const hipError_t e = launch_forward(fp, xq[j], sc[j], reinterpret_cast<const uint32_t*>(o.packed),
+                                          o.gamma, m, o.n, o.k, o.epilogue == BL_EPI_RELU2,
+                                          o.y_dtype == BL_BF16, o.y, o.acc_out, workspace, hs);
+      if (e != hipSuccess) return BL_ERR_HIP;
+    }
+    if (plan.ws_bytes > plan.scratch_off &&
+        launch_fill_zero(reinterpret_cast<uint32_t*>(ws + plan.scratch_off),
+                         (plan.ws_bytes - plan.scratch_off) / 4, hs) != hipSuccess)
+      return BL_ERR_HIP;
+    return BL_OK;
+  }
   FusedArgs args{};
   args.nseg = nops;
   args.eps = eps;
@@ -688,6 +791,7 @@ int bitlinear_forward_fused_kernel(const bl_linear* ops, int nops, int64_t m) {
   if (m < 1) return -BL_ERR_INVALID_ARG;
   const FusedPlan p = fused_plan(ops, nops, m);
   if (p.unsupported) return -BL_ERR_UNSUPPORTED_SHAPE;
+  if (p.two_pass) return BL_KERNEL_TWO_PASS;
   if (p.stream) return BL_KERNEL_STREAM_GEMV;
   if (p.mt) return BL_KERNEL_STREAM_MT;
   if (p.mfma) return BL_KERNEL_MFMA_GEMV;

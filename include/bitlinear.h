@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 3
+#define BITLINEAR_ABI_VERSION 4
 
 /* Largest K: the kernels accumulate 64 * x~ * W~ in int32, so
  * 64 * 127 * K must stay below 2^31. */
@@ -234,7 +234,8 @@ bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t 
 
 /* ------------------------------------------------------------------------
  * bitlinear_forward_fused -- the decode step of several BitLinear layers that
- * read the same token batch size, in one launch: for each entry, per-token
+ * read the same token batch size, in one launch (but see long rows below):
+ * for each entry, per-token
  * absmax int8 quantization of its activations ("8-Bit Activation
  * Quantization: absmax Scaling") and y = (x~ W~^T) * gamma / s ("Matrix
  * Multiplication as Pure Integer Addition"), with the same numbers as
@@ -251,7 +252,12 @@ bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t 
  * activations of its tokens (one block of up to 16 from 3 tokens) from
  * cache once, or twice when a row does not fit its registers; meant for
  * decode-sized batches.  From 3 tokens no workspace is needed (the size
- * query returns 0).
+ * query returns 0), except for tables with an activation row of more than
+ * 16 KiB (bf16 K > 8192, fp32 K > 4096): there every distinct input is
+ * quantized once by its own launch (into xq_out / scale_out when the entry
+ * gives them, else into the workspace), each product then runs its
+ * bitlinear_forward plan, and a last launch clears the workspace scratch, so
+ * the workspace contract holds (BL_KERNEL_TWO_PASS).
  * Entries with rmsnorm set normalize x first (same numbers as
  * bitlinear_rmsnorm_quant_act followed by bitlinear_forward).  At 1-2
  * tokens a table with such an entry needs, for every entry, rows of whole
@@ -322,6 +328,8 @@ bl_status bitlinear_forward_noalloc(const int8_t* xq, const float* scale, const 
 #define BL_KERNEL_MFMA_GEMV 2      /* windowed matrix-core GEMV (fused: its fused form) */
 #define BL_KERNEL_STREAM_GEMV 3    /* streaming matrix-core GEMV, 1-2 tokens */
 #define BL_KERNEL_STREAM_MT 4      /* streaming matrix-core GEMV, blocks of 16 tokens */
+#define BL_KERNEL_TWO_PASS 5       /* fused step only: activation quant launches, then each
+                                      product's bitlinear_forward plan */
 int bitlinear_forward_kernel(int64_t m, int64_t n, int64_t k);
 int bitlinear_forward_fused_kernel(const bl_linear* ops, int nops, int64_t m);
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(bl):
     raw = ctypes.CDLL(bl.LIB_PATH)
     for name in _declared_functions():
         assert hasattr(raw, name), name
-    assert bl.lib.bitlinear_abi_version() == 3
+    assert bl.lib.bitlinear_abi_version() == 4
 
 
 @pytest.mark.parametrize("n,k", [(1, 1), (64, 256), (65, 257), (2560, 6912), (28672, 8192), (130, 520)])
@@ -296,7 +296,10 @@ def _fake_table(bl, specs, x_offset=0):
     (64, [(2560, 6912, "bf16", True)], 0, "stream_mt"),
     (33, [(1000, 4096, "f32", False)], 0, "stream_mt"),
     (8, [(1000, 4096, "f32", False)], 4, "mfma_gemv"),                   # x not 16-byte aligned
-    (16, [(2048, 8200, "f32", False)], 0, "mfma_gemv"),                  # fp32 row past 16 units per lane
+    (16, [(2048, 8200, "f32", False)], 0, "two_pass"),                   # fp32 row past 16 KiB
+    (16, [(8192, 28672, "bf16", False)], 0, "two_pass"),                 # bf16 row past 16 KiB
+    (3, [(640, 2560, "bf16", True), (300, 9000, "f32", False)], 0, "two_pass"),
+    (16, [(2048, 1004, "bf16", False)], 0, "mfma_gemv"),                 # rows not whole 16-byte units
     (2, [(1100, 28672, "bf16", True)], 0, "mfma_gemv"),                  # RMSNorm, x~ past the LDS
 ])
 def test_forward_fused_kernel_plan(bl, m, specs, x_offset, kernel):
@@ -317,9 +320,9 @@ def test_gpu_cases_cover_every_kernel(bl):
     from test_gpu_parity import FWD_CASES
     from test_gpu_fused import FUSED_CASES
     kinds = {bl.forward_kernel(m, n, k) for (m, n, k, *_rest) in FWD_CASES}
-    assert kinds == set(bl.KERNEL_NAMES.values()), kinds
+    assert kinds == set(bl.KERNEL_NAMES.values()) - {"two_pass"}, kinds
     fused = set()
     for m, specs in FUSED_CASES:
         arr = _fake_table(bl, [(n, k, xdt, False) for (n, k, _r, _y, xdt) in specs])
         fused.add(bl.KERNEL_NAMES[bl.lib.bitlinear_forward_fused_kernel(arr, len(specs), m)])
-    assert fused == {"dot4_gemv", "stream_gemv", "stream_mt", "mfma_gemv"}, fused
+    assert fused == {"dot4_gemv", "stream_gemv", "stream_mt", "mfma_gemv", "two_pass"}, fused

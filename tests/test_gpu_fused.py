@@ -220,6 +220,80 @@ def test_fused_absmax_extremes(B, m, xdt):
     assert_y_close(host(o["y"]), r["y"], "f32", f"extremes m={m} {xdt}")
 
 
+@pytest.mark.parametrize("m", [3, 16, 64])
+def test_two_pass_shared_inputs_and_workspace(B, m):
+    """Tables with an activation row of more than 16 KiB at 3 or more tokens
+    (the two-pass plan): entries that share an input and ask for no x~ read
+    one quantization from the workspace scratch, an entry with xq_out and
+    scale_out gets its own, RMSNorm entries with a gain run the normalizing
+    quantization.  Every output against the oracle; the workspace is all
+    zeros after the step, and a split-K forward that reuses it stays exact."""
+    import torch
+    from test_gpu_norm import check_norm_quant
+    k1, k2 = 9000, 5000
+    _, x1 = random_case(8100 + m, m, 1, k1, x_kind="t3")
+    x1[m // 2] = 0.0
+    _, x2 = random_case(8200 + m, m, 1, k2, x_kind="t3")
+    x1d, x1o = x_device(x1, "bf16")
+    x2d, x2o = x_device(x2, "f32")
+    gain = (np.random.default_rng(m).random(k2, dtype=np.float32) + 0.5).astype(np.float32)
+    gd = dev(gain)
+    neps = 2.0 ** -23
+    # (input, n, relu2, y dtype, outputs asked for)
+    specs = [(1, 700, False, "bf16", False), (1, 130, True, "f32", False),
+             (1, 2100, False, "bf16", False), (2, 640, False, "f32", True),
+             (1, 300, True, "bf16", True), (2, 96, False, "bf16", False)]
+    ops, ws_w = [], []
+    for i, (src, n, relu2, ydt, outs) in enumerate(specs):
+        k = k1 if src == 1 else k2
+        w, _ = random_case(8300 + 31 * i + m, 1, n, k)
+        packed, gamma = B.pack_weights(dev(w))
+        o = dict(x=x1d if src == 1 else x2d, packed=packed, gamma=gamma, n=n, k=k, relu2=relu2,
+                 y=torch.empty((m, n), dtype=torch.bfloat16 if ydt == "bf16" else torch.float32,
+                               device="cuda"),
+                 acc_out=torch.empty((m, n), dtype=torch.int32, device="cuda"))
+        if src == 2:
+            o.update(rmsnorm=True, norm_weight=gd, norm_eps=neps)
+        if outs:
+            o.update(xq_out=torch.full((m, O.padded_k(k)), 99, dtype=torch.int8, device="cuda"),
+                     scale_out=torch.empty(m, dtype=torch.float32, device="cuda"))
+        ops.append(o)
+        ws_w.append(w)
+    ws = B.Workspace()
+    step = B.FusedStep(ops, workspace=ws)
+    assert step.kernel() == "two_pass" and step.nbytes > 0
+    log(f"two-pass m={m} workspace={step.nbytes}")
+    for rep in range(2):
+        step()
+        torch.cuda.synchronize()
+        assert not host(ws.buf[:step.nbytes]).any(), "workspace left non-zero"
+        # the RMSNorm input: its own outputs (entry 3) against the oracle
+        xq3, s3 = host(ops[3]["xq_out"]), host(ops[3]["scale_out"])
+        check_norm_quant(x2o, gain, neps, xq3, s3, f"two-pass m={m} norm")
+        r1 = O.forward(x1o, ws_w[4], gamma=host(ops[4]["gamma"])[0])
+        np.testing.assert_array_equal(host(ops[4]["xq_out"])[:, :k1], r1["xq"])
+        np.testing.assert_array_equal(host(ops[4]["scale_out"]), r1["s"])
+        for i, (src, n, relu2, ydt, outs) in enumerate(specs):
+            g = host(ops[i]["gamma"])[0]
+            assert gamma_agrees(g, ws_w[i])
+            codes = O.ternary_codes(ws_w[i], g)
+            xq = r1["xq"] if src == 1 else xq3[:, :k2]
+            sv = r1["s"] if src == 1 else s3
+            acc = O.contract(xq, codes)
+            np.testing.assert_array_equal(host(ops[i]["acc_out"]), acc, err_msg=f"entry {i}")
+            yo = O.round_output(O.dequant(acc, g, sv, relu2), ydt)
+            assert_y_close(host(ops[i]["y"]), yo, ydt, f"two-pass m={m} entry {i} rep {rep}")
+    # the same workspace then serves a split-K product
+    n5, k5 = 200, 20000
+    assert B.forward_workspace_bytes(1, n5, k5) > 0
+    w5, x5 = random_case(8400 + m, 1, n5, k5, x_kind="t3")
+    packed5, gamma5 = B.pack_weights(dev(w5))
+    xq5, s5 = B.quant_act(dev(x5))
+    y5, acc5 = B.forward(xq5, s5, packed5, gamma5, n5, k5, acc_out=True, workspace=ws)
+    r5 = O.forward(x5, w5, gamma=host(gamma5)[0])
+    np.testing.assert_array_equal(host(acc5), r5["acc"])
+
+
 def test_fused_rejects(B):
     import torch
     m = B.BL_FUSED_MAX_M + 1
