@@ -507,6 +507,110 @@ def run_cpu_baseline(W, budget_s=8.0):
                       f"{s1} in {e1:.1f} s on one core"}
 
 
+def run_cpu_configs(budget_s=1.0):
+    """The oracle per configuration on bounded samples, on one core and on
+    every core the process may use: the 256x256 layer whole; the 2B-class
+    decode set at one token; one 2B-class stack layer at 1, 8 and 64 tokens
+    (4 of the tokens timed, scaled to the batch and to 30 layers per pass);
+    each 2048-token prefill GEMM (16 tokens timed, scaled to 2048).  The
+    oracle's product loops over tokens, so its time is linear in them.
+    Per input group the activation quant, per product the integer product
+    and the dequant with its output rounding; codes prepared untimed.  The
+    100B-class layer is the headline step timed above."""
+    import datagen
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+
+    def prep(wname):
+        wl = datagen.WORKLOADS[wname]
+        codes = {}
+        for nm in wl.matrices:
+            w = datagen.workload_weights(wl, nm)
+            g = O.absmean_gamma(w)
+            codes[nm] = (O.ternary_codes(w, g), g)
+            del w
+        return wl, codes
+
+    def inputs(wl, m):
+        out = {}
+        for g in wl.groups():
+            if wl.x_dtype == "bf16":
+                bits, _ = datagen.activations(wl, g, m)
+                out[g] = datagen.bf16_bits_to_f32(bits)
+            else:
+                out[g] = datagen.activations_f32(wl, g, m)
+        return out
+
+    def layer(wl, codes, xs):
+        q = {g: O.quant_act(x) for g, x in xs.items()}
+        for nm, (c, g) in codes.items():
+            _, _, relu2, grp = wl.matrices[nm]
+            xq, sv = q[grp]
+            O.round_output(O.dequant(O.contract(xq, c), g, sv, relu2), wl.y_dtype)
+
+    allc = len(os.sched_getaffinity(0))
+
+    def per_call(fn):
+        out = []
+        for lim in (1, allc):
+            with threadpool_limits(limits=lim):
+                n, t0 = 0, time.perf_counter()
+                while True:
+                    fn()
+                    n += 1
+                    el = time.perf_counter() - t0
+                    if el > budget_s:
+                        break
+            out.append(el / n)
+        return out                                   # seconds per call: one core, all cores
+
+    def entry(sec, scale, nbytes=None, ops=None, what=""):
+        r = {"sample": what}
+        for tag, t in zip(("one_core", "all_cores"), sec):
+            d = {"ms": round(t * scale * 1e3, 2)}
+            if nbytes:
+                d["GBs"] = round(nbytes / (t * scale) / 1e9, 4)
+            if ops:
+                d["TOPS"] = round(ops / (t * scale) / 1e12, 6)
+            r[tag] = d
+        return r
+
+    res = {"cores": allc}
+    wl, codes = prep("c1")
+    xs = inputs(wl, 4)
+    res["c1"] = entry(per_call(lambda: layer(wl, codes, xs)), 1.0, what="the whole 4x256->256 layer")
+    wl, codes = prep("c2")
+    xs = inputs(wl, 1)
+    nb = sum(fused_bytes(1, n, k) for (n, k, _, _) in wl.matrices.values())
+    res["c2"] = entry(per_call(lambda: layer(wl, codes, xs)), 1.0, nbytes=nb,
+                      what="the decode set (q,k,v,o,up,down) at one token")
+    wl, codes = prep("c3")
+    res["c3"] = {}
+    for m in (1, 8, 64):
+        sm = min(m, 4)
+        xs = inputs(wl, m)
+        xs = {g: x[:sm] for g, x in xs.items()}
+        nb = wl.layers * sum(fused_bytes(m, n, k) for (n, k, _, _) in wl.matrices.values())
+        res["c3"][str(m)] = entry(per_call(lambda: layer(wl, codes, xs)), wl.layers * m / sm,
+                                  nbytes=nb, what=f"one layer, {sm} of {m} tokens timed, scaled "
+                                                  f"x{m / sm:g} to {m} tokens and x{wl.layers} to a pass")
+    del codes
+    wl, codes = prep("c4")
+    res["c4"] = {}
+    M, sm = 2048, 16
+    xs_all = inputs(wl, sm)
+    for nm, (c, g) in codes.items():
+        n, k, relu2, grp = wl.matrices[nm]
+        x = xs_all[grp]
+
+        def gemm(x=x, c=c, g=g, relu2=relu2):
+            xq, sv = O.quant_act(x)
+            O.round_output(O.dequant(O.contract(xq, c), g, sv, relu2), wl.y_dtype)
+        res["c4"][nm] = entry(per_call(gemm), M / sm, ops=2.0 * M * n * k,
+                              what=f"{sm} of {M} tokens through {M}x{k}->{n} timed, scaled x{M // sm}")
+    return res
+
+
 def host_cpu_model():
     name = "unknown"
     try:
@@ -837,6 +941,9 @@ def main():
         extra["c5"] = run_c5(B, torch, W)
     cpu = None if args.no_cpu else run_cpu_baseline(W)
     del W
+    if cpu is not None and not args.no_extra:
+        log("oracle per configuration")
+        cpu["per_config"] = run_cpu_configs()
     torch.cuda.empty_cache()
     if not args.no_extra:
         extra["prefill"] = run_prefill(B, torch)

@@ -227,7 +227,6 @@ hipError_t launch_forward(const FwdPlan& plan, const int8_t* xq, const float* sc
 }
 
 struct FusedPlan {
-  bool unsupported = false;             // no kernel takes this table
   bool norm = false;                    // some entry has RMSNorm
   bool stream = false;                  // 1..2 tokens: the streaming matrix-core kernel
   bool stream_wide = false;             // its 16-wave shape (rows past 8 waves' registers)
@@ -666,7 +665,6 @@ bl_status bitlinear_forward_fused(const bl_linear* ops, int nops, int64_t m, flo
   if (!valid_act_eps(eps)) return BL_ERR_INVALID_ARG;
   if (m == 0) return BL_OK;
   const FusedPlan plan = fused_plan(ops, nops, m);
-  if (plan.unsupported) return BL_ERR_UNSUPPORTED_SHAPE;
   if (plan.ws_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return BL_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return BL_ERR_MISALIGNED;
@@ -790,7 +788,6 @@ int bitlinear_forward_fused_kernel(const bl_linear* ops, int nops, int64_t m) {
   if (st != BL_OK) return -(int)st;
   if (m < 1) return -BL_ERR_INVALID_ARG;
   const FusedPlan p = fused_plan(ops, nops, m);
-  if (p.unsupported) return -BL_ERR_UNSUPPORTED_SHAPE;
   if (p.two_pass) return BL_KERNEL_TWO_PASS;
   if (p.stream) return BL_KERNEL_STREAM_GEMV;
   if (p.mt) return BL_KERNEL_STREAM_MT;

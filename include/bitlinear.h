@@ -260,10 +260,11 @@ bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t 
  * the workspace contract holds (BL_KERNEL_TWO_PASS).
  * Entries with rmsnorm set normalize x first (same numbers as
  * bitlinear_rmsnorm_quant_act followed by bitlinear_forward).  At 1-2
- * tokens a table with such an entry needs, for every entry, rows of whole
- * 16-byte units at 16-byte alignment, one activation dtype, and x~ of
- * every token within 64 KiB (2 * padded_k <= 65536 at two tokens);
- * otherwise BL_ERR_UNSUPPORTED_SHAPE.
+ * tokens such a table runs on the streaming kernel when every entry has
+ * rows of whole 16-byte units at 16-byte alignment, one activation dtype,
+ * and x~ of every token within 64 KiB (2 * padded_k <= 65536 at two
+ * tokens), and on the fused matrix-core kernel otherwise; every table the
+ * checks above accept has a kernel.
  * ---------------------------------------------------------------------- */
 #define BL_MAX_FUSED 16
 #define BL_FUSED_MAX_M 64

@@ -530,14 +530,17 @@ def test_graph_replays_match_eager(B):
 def test_graph_replays_match_eager_batched(B):
     # the batched-decode kernels under graph capture: a fused step on the
     # multi-token streaming kernel (8 tokens, shared input), a plain product
-    # on it (48 tokens, long rows) and one on the windowed MFMA GEMV (16
-    # tokens), replayed with eager work between the replays, against the
-    # eager bits and the oracle
+    # on it (48 tokens, long rows), one on the windowed MFMA GEMV (16
+    # tokens) and a two-pass fused step (4 tokens, rows of 9000 bf16, shared
+    # input: quantization, two products and the scratch fill in the graph),
+    # replayed with eager work between the replays, against the eager bits
+    # and the oracle; the workspace stays zero-filled
     import torch
     assert B.forward_kernel(48, 1030, 8192) == "stream_mt"
     assert B.forward_kernel(16, 2560, 2560) == "mfma_gemv"
     mats = {name: random_case(20 + i, 1, n, k)[0] for i, (name, n, k) in
-            enumerate((("q", 2560, 2560), ("k", 640, 2560), ("mt", 1030, 8192), ("win", 2560, 2560)))}
+            enumerate((("q", 2560, 2560), ("k", 640, 2560), ("mt", 1030, 8192), ("win", 2560, 2560),
+                       ("tp1", 300, 9000), ("tp2", 200, 9000)))}
     packed = {nm: B.pack_weights(dev(w)) for nm, w in mats.items()}
     _, x8 = random_case(30, 8, 1, 2560, x_kind="t3")
     x8d = x_device(x8, "bf16")[0]
@@ -545,18 +548,27 @@ def test_graph_replays_match_eager_batched(B):
     xq48, s48 = B.quant_act(dev(x48))
     _, x16 = random_case(32, 16, 1, 2560, x_kind="t3")
     xq16, s16 = B.quant_act(dev(x16))
+    _, x4 = random_case(33, 4, 1, 9000, x_kind="t3")
+    x4d, x4o = x_device(x4, "bf16")
     ys = {"q": torch.empty((8, 2560), dtype=torch.bfloat16, device="cuda"),
           "k": torch.empty((8, 640), dtype=torch.bfloat16, device="cuda"),
           "mt": torch.empty((48, 1030), dtype=torch.float32, device="cuda"),
-          "win": torch.empty((16, 2560), dtype=torch.bfloat16, device="cuda")}
+          "win": torch.empty((16, 2560), dtype=torch.bfloat16, device="cuda"),
+          "tp1": torch.empty((4, 300), dtype=torch.bfloat16, device="cuda"),
+          "tp2": torch.empty((4, 200), dtype=torch.float32, device="cuda")}
     ws = B.Workspace()
     step = B.FusedStep([dict(x=x8d, packed=packed[nm][0], gamma=packed[nm][1], n=n, k=2560,
                              y=ys[nm], relu2=(nm == "k")) for nm, n in (("q", 2560), ("k", 640))],
                        workspace=ws)
     assert step.kernel() == "stream_mt"
+    step2 = B.FusedStep([dict(x=x4d, packed=packed[nm][0], gamma=packed[nm][1], n=n, k=9000,
+                              y=ys[nm], relu2=(nm == "tp2")) for nm, n in (("tp1", 300), ("tp2", 200))],
+                        workspace=ws)
+    assert step2.kernel() == "two_pass" and step2.nbytes > 0
 
     def work():
         step()
+        step2()
         B.forward(xq48, s48, packed["mt"][0], packed["mt"][1], 1030, 8192, y=ys["mt"], workspace=ws)
         B.forward(xq16, s16, packed["win"][0], packed["win"][1], 2560, 2560, relu2=True,
                   y=ys["win"], workspace=ws)
@@ -567,7 +579,8 @@ def test_graph_replays_match_eager_batched(B):
     # the eager results against the oracle
     x8o = x_device(x8, "bf16")[1]                      # the bf16 values x8d holds
     for nm, xo, relu2, ydt in (("q", x8o, False, "bf16"), ("k", x8o, True, "bf16"),
-                               ("mt", x48, False, "f32"), ("win", x16, True, "bf16")):
+                               ("mt", x48, False, "f32"), ("win", x16, True, "bf16"),
+                               ("tp1", x4o, False, "bf16"), ("tp2", x4o, True, "f32")):
         g = host(packed[nm][1])[0]
         r = O.forward(xo, mats[nm], relu2=relu2, y_dtype=ydt, gamma=g)
         assert_y_close(host(ref[nm]), r["y"], ydt, f"eager {nm}")
@@ -590,5 +603,6 @@ def test_graph_replays_match_eager_batched(B):
             a, b = (t.view(torch.int16), ref[nm].view(torch.int16)) if t.dtype == torch.bfloat16 \
                 else (t.view(torch.int32), ref[nm].view(torch.int32))
             assert torch.equal(a, b), f"replay {rep}, {nm}"
+        assert not host(ws.buf).any(), f"replay {rep}: workspace left non-zero"
         work()
         torch.cuda.synchronize()
