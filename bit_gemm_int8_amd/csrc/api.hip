@@ -71,7 +71,7 @@ static bool mt_plan(int64_t m, int64_t n, int64_t k, FwdPlan* p) {
   const int64_t nc = cdiv(k, kSuperK);
   if (nc < 32 || !((m > 32 && nb <= 128) || (m > 16 && nb <= 16))) return false;
   const int64_t P = mt_row_ranges(m, subs);
-  if (stream_mt_lds_bytes(m, nc, (int)cdiv(subs, P), 16) > kMtMaxLds) return false;
+  if (stream_mt_lds_bytes(m, nc, (int)cdiv(subs, P), 16, 0) > kMtMaxLds) return false;
   p->kind = 4;
   p->qpl = (int)P;
   p->splits = 1;
@@ -183,7 +183,7 @@ FwdPlan forward_plan(int64_t m, int64_t n, int64_t k) {
     if (tiles < kCUs / 2 && nc <= 16 && (nb >= 32 || m >= 512)) {
       const int64_t subs = nb * 4;
       const int64_t P = mt_row_ranges(m, subs);
-      if (stream_mt_lds_bytes(m, nc, (int)cdiv(subs, P), 16) <= kMtMaxLds) {
+      if (stream_mt_lds_bytes(m, nc, (int)cdiv(subs, P), 16, 0) <= kMtMaxLds) {
         p.kind = 4;
         p.qpl = (int)P;
         p.splits = 1;
@@ -381,12 +381,26 @@ static bool mt_fused_plan(const bl_linear* ops, int nops, int64_t m, bool norm, 
   // size every time: 8-token blocks are 9-17% faster on the 2B set at 16-32
   // tokens and win at 64 tokens on short outputs and long rows; 16-token
   // blocks win on the large 100B outputs).
+  // RMSNorm entries with a gain stage it in LDS (the longest such row)
+  int64_t gain_k = 0;
+  for (int i = 0; i < nops; ++i)
+    if (norm && ops[i].rmsnorm && ops[i].norm_weight != nullptr && ops[i].k > gain_k)
+      gain_k = ops[i].k;
+  auto lds_of = [&](int t, const int64_t (&q)[kMaxFused]) {
+    int na = 1;
+    for (int i = 0; i < nops; ++i) {
+      const int spw = (int)cdiv(cdiv(ops[i].n, kRowBlock) * 4, q[i]);
+      if (spw > na) na = spw;
+    }
+    return stream_mt_lds_bytes(m, nc_max, na, t, gain_k);
+  };
   int tok = 16;
   int64_t ps[kMaxFused];
   double best = -1.0;
   for (int t : {16, 8}) {
     int64_t q[kMaxFused];
     allocate(t, q);
+    if (lds_of(t, q) > kMtMaxLds) continue;
     double cost = 0.0;
     for (int i = 0; i < nops; ++i) {
       const int64_t subs = cdiv(ops[i].n, kRowBlock) * 4;
@@ -400,6 +414,7 @@ static bool mt_fused_plan(const bl_linear* ops, int nops, int64_t m, bool norm, 
       for (int i = 0; i < nops; ++i) ps[i] = q[i];
     }
   }
+  if (best < 0.0) return false;
   const int64_t tb = cdiv(m, tok);
   int groups = 0, nsub_alloc = 1;
   for (int i = 0; i < nops; ++i) {
@@ -409,7 +424,7 @@ static bool mt_fused_plan(const bl_linear* ops, int nops, int64_t m, bool norm, 
     const int spw = (int)cdiv(subs, ps[i]);
     if (spw > nsub_alloc) nsub_alloc = spw;
   }
-  const size_t lds = stream_mt_lds_bytes(m, nc_max, nsub_alloc, tok);
+  const size_t lds = stream_mt_lds_bytes(m, nc_max, nsub_alloc, tok, gain_k);
   if (lds > kMtMaxLds) return false;
   p->mt = true;
   p->mt_tok = tok;

@@ -124,8 +124,9 @@ hipError_t launch_gemv_stream_fused(const FusedArgs& args, int m, bool wide, boo
 // Multi-token streaming GEMV on the matrix cores (x~ of a block of up to 16
 // tokens in LDS -- 8 or 16 in the fused form, `tok` --, whole 16-row
 // sub-blocks per row range, P row ranges x ceil(m / tok) token blocks of
-// workgroups).
-size_t stream_mt_lds_bytes(int64_t m, int64_t nc, int nsub_alloc, int tok);
+// workgroups).  gain_k: fp32 RMSNorm gain values staged in LDS (the longest
+// row of an entry with a gain; 0 for none).
+size_t stream_mt_lds_bytes(int64_t m, int64_t nc, int nsub_alloc, int tok, int64_t gain_k);
 hipError_t launch_gemv_stream_mt(const int8_t* xq, const float* scale, const uint32_t* packed,
                                  const float* gamma, int64_t m, int64_t n, int64_t k, int P,
                                  bool relu2, bool bf16, void* y, int32_t* acc_out,

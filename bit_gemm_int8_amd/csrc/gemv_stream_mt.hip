@@ -258,11 +258,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_kernel(
 //      D weight units;
 //   2. with RMSNorm (entries flagged for it; the BitLinear listing of
 //      "End-to-End Implementation: Building a Native BitLinear Layer"
-//      applies nn.RMSNorm before quantize_activations_int8): the fp64 sum of
-//      squares in a fixed order (lanes, then the xor butterfly),
-//      r = rms_factor(sum, K, eps), and y = fp32(fp32(x * r) * w) replaces
-//      x below; these rows are read in three passes, four units per lane
-//      at a time (from the caches after the first), with the gain;
+//      applies nn.RMSNorm before quantize_activations_int8), from the held
+//      row: the fp64 sum of squares in the order bitlinear_rmsnorm_quant_act
+//      takes (so both get the same r), r = rms_factor(sum, K, eps), and
+//      y = fp32(fp32(x * r) * w) replaces x below, the gain w staged in LDS
+//      once per workgroup;
 //   3. beta = max|x| (absmax_bf16x2 / absmax_f32x2, then a wave max) and
 //      s = fp32(127 / max(beta, eps)) exactly as bitlinear_quant_act;
 //   4. x~ = clamp(rint(fp32(x * s))) (quant4_rne, whose clamp cannot bind)
@@ -305,6 +305,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
   const int u1 = (int)((int64_t)units * (wave + 1) / WAVES);
   int* sums = reinterpret_cast<int*>(lds + mba * kp16);
   float* fac = reinterpret_cast<float*>(sums + args.nsub_alloc * TBK * 16);
+  float* gl = fac + TBK;                              // RMSNorm gain (entries with one)
   const uint4* packed = reinterpret_cast<const uint4*>(sg.packed);
   const int nu = k / EPU;                             // units per row (whole units)
   const bool nrm = NORM && sg.rmsnorm();
@@ -327,6 +328,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
       xr[j] = make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
     }
   };
+  // an RMSNorm entry's gain (k floats as whole 16-byte pieces: rows are
+  // whole units) is loaded first, so that waiting for it does not wait for
+  // the row and weight loads issued after it (loads complete in order); it
+  // goes to LDS below
+  constexpr int GPT = (XR * 64 * EPU / 4 + NT - 1) / NT;   // gain pieces per thread, at most
+  uint4 gv[NORM ? GPT : 1];
+  if (NORM) {
+    // no load behind a branch (its wait would come at once): indices
+    // clamped, and without a gain the loads read the packed weights, unused
+    const uint4* gsrc = have_w ? gw : packed;
+    const int gn = have_w ? k / 4 : 1;
+#pragma unroll
+    for (int h = 0; h < GPT; ++h) gv[h] = gsrc[min((int)threadIdx.x + NT * h, gn - 1)];
+  }
   uint4 xr[XR];
   load_row(min(wave, mb - 1), xr);
   uint4 buf[D];
@@ -377,24 +392,33 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
       if (rowo != nullptr) rowo[u] = d0;
     }
   };
-  // y = (x r) w of unit u (RMSNorm), gains from the caches
-  auto normed = [&](const uint4& x, int u, float rn, uint32_t (&v)[8])
-      __attribute__((always_inline)) {
-    expand(x, v);
-    uint32_t wv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // the gain into LDS before any wave normalizes
+  if (NORM && have_w) {
+    uint4* g4 = reinterpret_cast<uint4*>(gl);
+#pragma unroll
+    for (int h = 0; h < GPT; ++h) {
+      const int i = (int)threadIdx.x + NT * h;
+      if (i < k / 4) g4[i] = gv[h];
+    }
+    __syncthreads();
+  }
+  // y = fp32(fp32(x * r) * w) of held unit j (RMSNorm); past the row x is 0
+  // and so is y
+  auto normed = [&](int j, float rn, uint32_t (&v)[8]) __attribute__((always_inline)) {
+    expand(xr[j], v);
+    float w[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
     if (have_w) {
-      const uint4 w0 = gw[u * (EPU / 4)];
-      wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
-      if (BF16) {
-        const uint4 w1 = gw[u * (EPU / 4) + 1];
-        wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+      const int u = min(lane + 64 * j, nu - 1);
+      const uint4* g4 = reinterpret_cast<const uint4*>(gl) + u * (EPU / 4);
+#pragma unroll
+      for (int h = 0; h < EPU / 4; ++h) {
+        const uint4 g = g4[h];
+        w[4 * h] = __uint_as_float(g.x); w[4 * h + 1] = __uint_as_float(g.y);
+        w[4 * h + 2] = __uint_as_float(g.z); w[4 * h + 3] = __uint_as_float(g.w);
       }
     }
 #pragma unroll
-    for (int e = 0; e < EPU; ++e) {
-      const float w = have_w ? __uint_as_float(wv[e]) : 1.0f;
-      v[e] = __float_as_uint(rms_apply(__uint_as_float(v[e]), rn, w));
-    }
+    for (int e = 0; e < EPU; ++e) v[e] = __float_as_uint(rms_apply(__uint_as_float(v[e]), rn, w[e]));
   };
 
   for (int t = wave; t < mb; t += WAVES) {
@@ -403,55 +427,50 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
                          : nullptr;
     float sv;
     if (NORM && nrm) {
-      // 2-4 with RMSNorm: three passes over the row (from the caches), four
-      // units per lane at a time
-      const uint4* row = reinterpret_cast<const uint4*>(sg.x) + (int64_t)(tok0 + t) * nu;
-      double ss = 0.0;
-      for (int ub = 0; ub < nu; ub += 256) {
-        uint4 xv[4];
+      // 2-4 with RMSNorm from the held row.  bitlinear_rmsnorm_quant_act
+      // puts unit u on thread u % 256 of 256, each thread adding its units'
+      // squares in order, then sums each 64-thread wave by xor butterfly
+      // and the four waves in order; lane l holds units l + 64 j, the units
+      // of thread l + 64 (j % 4) in order, so four partial sums give the
+      // same fp64 total, bit for bit (units past the row add +0).
+      if (t != wave) load_row(t, xr);
+      double part[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) xv[c] = row[min(ub + lane + 64 * c, nu - 1)];
+      for (int j = 0; j < XR; ++j) {
+        uint32_t v[8];
+        expand(xr[j], v);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (ub + lane + 64 * c < nu) {
-            uint32_t v[8];
-            expand(xv[c], v);
-#pragma unroll
-            for (int e = 0; e < EPU; ++e) {
-              const double d = (double)__uint_as_float(v[e]);
-              ss += d * d;
-            }
-          }
+        for (int e = 0; e < EPU; ++e) {
+          const double d = (double)__uint_as_float(v[e]);
+          part[j & 3] += d * d;
         }
       }
-      const float rn = rms_factor(wave_sum_f64(ss), k, sg.norm_eps);
+      double tot = wave_sum_f64(part[0]);
+#pragma unroll
+      for (int c = 1; c < 4; ++c) tot += wave_sum_f64(part[c]);
+      const float rn = rms_factor(tot, k, sg.norm_eps);
       uint32_t mx = 0;
-      for (int ub = 0; ub < nu; ub += 256) {
-        uint4 xv[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) xv[c] = row[min(ub + lane + 64 * c, nu - 1)];
+      for (int j = 0; j < XR; ++j) {
+        uint32_t v[8];
+        normed(j, rn, v);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          uint32_t v[8];
-          normed(xv[c], min(ub + lane + 64 * c, nu - 1), rn, v);
-#pragma unroll
-          for (int e = 0; e < EPU; e += 2) mx = absmax_f32x2(mx, v[e], v[e + 1]);
-        }
+        for (int e = 0; e < EPU; e += 2) mx = absmax_f32x2(mx, v[e], v[e + 1]);
       }
       mx = wave_max_u32(mx);
       sv = (float)(127.0 / (double)fmaxf(__uint_as_float(mx), args.eps));
-      for (int ub = 0; ub < nu; ub += 256) {
-        uint4 xv[4];
+      // y again from the held row rather than all of it kept from the max
+      // (the compiler would, and spill): the row counts as rewritten here
 #pragma unroll
-        for (int c = 0; c < 4; ++c) xv[c] = row[min(ub + lane + 64 * c, nu - 1)];
+      for (int j = 0; j < XR; ++j)
+        asm volatile("" : "+v"(xr[j].x), "+v"(xr[j].y), "+v"(xr[j].z), "+v"(xr[j].w));
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int u = ub + lane + 64 * c;
-          if (u < nu) {
-            uint32_t v[8];
-            normed(xv[c], u, rn, v);
-            put(t, u, v, sv, rowo);
-          }
+      for (int j = 0; j < XR; ++j) {
+        const int u = lane + 64 * j;
+        if (u < nu) {
+          uint32_t v[8];
+          normed(j, rn, v);
+          put(t, u, v, sv, rowo);
         }
       }
     } else {
@@ -526,9 +545,10 @@ void run_mt_fused(const FusedArgs& args, int m, const int (&wb)[13], int groups,
 
 }  // namespace
 
-size_t stream_mt_lds_bytes(int64_t m, int64_t nc, int nsub_alloc, int tok) {
+size_t stream_mt_lds_bytes(int64_t m, int64_t nc, int nsub_alloc, int tok, int64_t gain_k) {
   const int64_t mba = m < tok ? m : tok;
-  return (size_t)(mba * nc * 256) + (size_t)nsub_alloc * tok * 16 * 4 + tok * 4;
+  return (size_t)(mba * nc * 256) + (size_t)nsub_alloc * tok * 16 * 4 + tok * 4 +
+         (size_t)gain_k * 4;
 }
 
 hipError_t launch_gemv_stream_mt(const int8_t* xq, const float* scale, const uint32_t* packed,
@@ -541,7 +561,7 @@ hipError_t launch_gemv_stream_mt(const int8_t* xq, const float* scale, const uin
   if (P < 1 || P > S || m < 1) return hipErrorInvalidValue;
   const int nsub_alloc = (int)cdiv(S, P);
   const int mba = (int)(m < kTokBlock ? m : kTokBlock);
-  const size_t lds = stream_mt_lds_bytes(m, nc, nsub_alloc, kTokBlock);
+  const size_t lds = stream_mt_lds_bytes(m, nc, nsub_alloc, kTokBlock, 0);
   const int vec_out = n % 4 == 0 && (uintptr_t)y % (bf16 ? 8 : 16) == 0 &&
                       (acc_out == nullptr || (uintptr_t)acc_out % 16 == 0);
   const int xr = (int)cdiv((int64_t)mba * nc * 16, 64 * 16);

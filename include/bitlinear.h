@@ -259,7 +259,12 @@ bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t 
  * bitlinear_forward plan, and a last launch clears the workspace scratch, so
  * the workspace contract holds (BL_KERNEL_TWO_PASS).
  * Entries with rmsnorm set normalize x first (same numbers as
- * bitlinear_rmsnorm_quant_act followed by bitlinear_forward).  At 1-2
+ * bitlinear_rmsnorm_quant_act followed by bitlinear_forward: the
+ * multi-token kernel and the two-pass plan add the squares in fp64 in
+ * bitlinear_rmsnorm_quant_act's order; the streaming kernel (1-2 tokens)
+ * and the fused matrix-core kernel in fixed orders of their own, so there a
+ * token whose mean square lies within the last place of that sum of an fp32
+ * rounding boundary may get the neighbouring fp32 mean square).  At 1-2
  * tokens such a table runs on the streaming kernel when every entry has
  * rows of whole 16-byte units at 16-byte alignment, one activation dtype,
  * and x~ of every token within 64 KiB (2 * padded_k <= 65536 at two

@@ -168,25 +168,39 @@ def test_fused_rmsnorm(B, case):
     _fused_norm_case(B, m, specs, seed=8000 + m * 7 + len(specs), shared=shared)
 
 
-def test_rmsnorm_fused_equals_two_step(B):
+@pytest.mark.parametrize("m,k,xdt", [(1, 4096, "bf16"), (8, 4096, "bf16"), (20, 8192, "bf16"),
+                                      (40, 4096, "f32"), (3, 2560, "bf16")])
+def test_rmsnorm_fused_equals_two_step(B, m, k, xdt):
     """The fused step with RMSNorm gives the same bits as
-    bitlinear_rmsnorm_quant_act followed by bitlinear_forward (1 and 8 tokens)."""
+    bitlinear_rmsnorm_quant_act followed by bitlinear_forward: x~, s, the
+    accumulator and y.  From 3 tokens the fused kernel sums the squares in
+    the standalone kernel's order, so this holds for every token, also one
+    whose mean square sits at an fp32 rounding boundary; rows with outlier
+    channels spread the squares over many binades."""
     import torch
-    for m in (1, 8):
-        w, x = random_case(8100 + m, m, 3000, 4096, x_kind="t3")
-        gain = np.linspace(0.5, 1.5, 4096, dtype=np.float32)
-        xd, _ = x_device(x, "bf16")
-        gd = dev(gain)
-        packed, gamma = B.pack_weights(dev(w))
-        y = torch.empty((m, 3000), dtype=torch.bfloat16, device="cuda")
-        acc = torch.empty((m, 3000), dtype=torch.int32, device="cuda")
-        B.forward_fused([dict(x=xd, packed=packed, gamma=gamma, n=3000, k=4096, y=y,
-                              acc_out=acc, rmsnorm=True, norm_weight=gd, norm_eps=1e-5)])
-        xq, s = B.rmsnorm_quant_act(xd, gd, norm_eps=1e-5)
-        y2, acc2 = B.forward(xq, s, packed, gamma, 3000, 4096, out_dtype=torch.bfloat16,
-                             acc_out=True)
-        assert torch.equal(acc, acc2), m
-        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), m
+    n = 3000
+    w, x = random_case(8100 + m, m, n, k, x_kind="t3")
+    x[:, ::97] *= np.float32(300.0)
+    x[m // 2, :] *= np.float32(1e-3)
+    gain = np.linspace(0.5, 1.5, k, dtype=np.float32)
+    xd, _ = x_device(x, xdt)
+    gd = dev(gain)
+    packed, gamma = B.pack_weights(dev(w))
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    acc = torch.empty((m, n), dtype=torch.int32, device="cuda")
+    xq1 = torch.full((m, O.padded_k(k)), 99, dtype=torch.int8, device="cuda")
+    s1 = torch.empty(m, dtype=torch.float32, device="cuda")
+    step = B.FusedStep([dict(x=xd, packed=packed, gamma=gamma, n=n, k=k, y=y, acc_out=acc,
+                             xq_out=xq1, scale_out=s1, rmsnorm=True, norm_weight=gd,
+                             norm_eps=1e-5)])
+    log(f"fused rmsnorm vs two-step m={m} k={k} {xdt} kernel={step.kernel()}")
+    step()
+    xq, s = B.rmsnorm_quant_act(xd, gd, norm_eps=1e-5)
+    y2, acc2 = B.forward(xq, s, packed, gamma, n, k, out_dtype=torch.bfloat16, acc_out=True)
+    assert torch.equal(xq1, xq), m
+    assert torch.equal(s1.view(torch.int32), s.view(torch.int32)), m
+    assert torch.equal(acc, acc2), m
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), m
 
 
 @pytest.mark.parametrize("rmsnorm", [True, False])
