@@ -233,6 +233,121 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_quant_kernel(
   for (int64_t i = k + tid; i < kpad; i += kThreads) qrow[i] = 0;
 }
 
+// The same for rows of whole 16-byte vectors at 16-byte alignment, at most R
+// per thread, with a 16-byte aligned gain (or none): each thread loads its
+// vectors (and their gain) once and keeps them in registers, so the three
+// passes wait for memory once.  The fp64 sum runs in the same order as
+// rmsnorm_quant_kernel's (vector v of the row on thread v % 256, each
+// thread's vectors and their elements in order, then block_sum_f64), and
+// every other step is the same, so the two give the same bits.
+template <bool BF16, int R>
+__global__ __launch_bounds__(kThreads) void rmsnorm_quant_reg_kernel(
+    const void* __restrict__ x, int64_t k, int64_t kpad, const float* __restrict__ nw,
+    float neps, float eps, int8_t* __restrict__ xq, float* __restrict__ scale) {
+  constexpr int V = BF16 ? 8 : 4;                   // elements per vector
+  constexpr int G = V / 4;                          // gain vectors per input vector
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint4* xrow = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(x) +
+                                                     row * k * (BF16 ? 2 : 4));
+  int8_t* qrow = xq + row * kpad;
+  __shared__ double red64[kThreads / 64];
+  __shared__ uint32_t red[kThreads / 64];
+  const int nvec = (int)(k / V);
+  // loads with clamped indices and no branch (past the row the values are
+  // replaced by zeros below); without a gain the gain loads read x, unused
+  const uint4* gsrc = nw != nullptr ? reinterpret_cast<const uint4*>(nw) : xrow;
+  uint4 u[R], gv[R][G];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int v = min(tid + kThreads * i, nvec - 1);
+    u[i] = xrow[v];
+#pragma unroll
+    for (int h = 0; h < G; ++h) gv[i][h] = gsrc[nw != nullptr ? v * G + h : 0];
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (tid + kThreads * i >= nvec) u[i] = make_uint4(0u, 0u, 0u, 0u);
+  auto vals = [&](int i, float (&f)[8]) __attribute__((always_inline)) {
+    const uint32_t w[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (BF16) {
+        f[2 * e] = __uint_as_float(w[e] << 16);
+        f[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      } else {
+        f[e] = __uint_as_float(w[e]);
+      }
+    }
+  };
+  auto gains = [&](int i, float (&g)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      g[4 * h] = __uint_as_float(gv[i][h].x); g[4 * h + 1] = __uint_as_float(gv[i][h].y);
+      g[4 * h + 2] = __uint_as_float(gv[i][h].z); g[4 * h + 3] = __uint_as_float(gv[i][h].w);
+    }
+    if (nw == nullptr) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) g[e] = 1.0f;
+    }
+  };
+
+  // ---- pass 1: sum of squares (fp64) ----
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (tid + kThreads * i < nvec) {
+      float f[8];
+      vals(i, f);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const double d = (double)f[e];
+        ss += d * d;
+      }
+    }
+  }
+  const float r = rms_factor(block_sum_f64(ss, red64), (int)k, neps);
+
+  // ---- pass 2: max |y| ----
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    float f[8], g[8];
+    vals(i, f);
+    gains(i, g);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const uint32_t b = __float_as_uint(rms_apply(f[e], r, g[e])) & 0x7FFFFFFFu;
+      mx = mx > b ? mx : b;
+    }
+  }
+  const float s = row_scale(mx, eps, red);
+  if (tid == 0) scale[row] = s;
+
+  // ---- pass 3: quantize y (recomputed from the held row, not kept) ----
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    asm volatile("" : "+v"(u[i].x), "+v"(u[i].y), "+v"(u[i].z), "+v"(u[i].w));
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int v = tid + kThreads * i;
+    if (v < nvec) {
+      float f[8], g[8];
+      vals(i, f);
+      gains(i, g);
+      uint32_t o[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        o[e >> 2] |= ((uint32_t)(uint8_t)quantize(rms_apply(f[e], r, g[e]), s)) << (8 * (e & 3));
+      if (BF16)
+        reinterpret_cast<uint2*>(qrow)[v] = make_uint2(o[0], o[1]);
+      else
+        reinterpret_cast<uint32_t*>(qrow)[v] = o[0];
+    }
+  }
+  for (int64_t i = k + tid; i < kpad; i += kThreads) qrow[i] = 0;
+}
+
 }  // namespace
 
 hipError_t launch_rmsnorm_quant(const void* x, bool bf16, int64_t m, int64_t k, int64_t kpad,
@@ -242,6 +357,26 @@ hipError_t launch_rmsnorm_quant(const void* x, bool bf16, int64_t m, int64_t k, 
   dim3 grid((unsigned)m), block(kThreads);
   // V elements per thread and step when a row splits into whole groups of V
   const bool vec = (k % (bf16 ? 8 : 4)) == 0;
+  // rows held in registers: whole aligned vectors, an aligned gain (or none)
+  if (vec && (uintptr_t)x % 16 == 0 && (uintptr_t)norm_weight % 16 == 0) {
+    const int64_t per = cdiv(k / (bf16 ? 8 : 4), kThreads);   // vectors per thread
+#define BL_RQREG(R)                                                                       \
+  do {                                                                                    \
+    if (bf16)                                                                             \
+      rmsnorm_quant_reg_kernel<true, R><<<grid, block, 0, stream>>>(                      \
+          x, k, kpad, norm_weight, norm_eps, eps, xq, scale);                             \
+    else                                                                                  \
+      rmsnorm_quant_reg_kernel<false, R><<<grid, block, 0, stream>>>(                     \
+          x, k, kpad, norm_weight, norm_eps, eps, xq, scale);                             \
+    return hipGetLastError();                                                             \
+  } while (0)
+    if (per <= 1) BL_RQREG(1);
+    if (per <= 2) BL_RQREG(2);
+    if (per <= 4) BL_RQREG(4);
+    if (per <= 8) BL_RQREG(8);
+    if (per <= 16) BL_RQREG(16);
+#undef BL_RQREG
+  }
   if (bf16) {
     if (vec)
       rmsnorm_quant_kernel<true, true><<<grid, block, 0, stream>>>(x, k, kpad, norm_weight,

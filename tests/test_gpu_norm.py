@@ -65,6 +65,33 @@ def check_norm_quant(xo, gain, norm_eps, xq, s, where):
     return oq, os_
 
 
+@pytest.mark.parametrize("m,k,xdt,with_gain", [(3, 2560, "bf16", True), (16, 28672, "bf16", True),
+                                              (5, 4096, "f32", False), (2, 6912, "bf16", False),
+                                              (4, 16384, "f32", True)])
+def test_rmsnorm_register_and_loop_kernels_agree(B, m, k, xdt, with_gain):
+    """bitlinear_rmsnorm_quant_act holds 16-byte aligned rows in registers and
+    loops over the others; both add the squares in the same order, so the
+    same rows give the same bits whether x sits at a 16-byte boundary or 4
+    bytes past one."""
+    import torch
+    _, x = random_case(9300 + m, m, 1, k, x_kind="t3")
+    x[:, ::61] *= np.float32(500.0)
+    xd, _ = x_device(x, xdt)
+    esz = 2 if xdt == "bf16" else 4
+    shift = 4 // esz
+    buf = torch.empty(m * k + 16, dtype=xd.dtype, device="cuda")
+    xs = buf[shift:shift + m * k].view(m, k)
+    xs.copy_(xd)
+    assert xd.data_ptr() % 16 == 0 and xs.data_ptr() % 16 == 4
+    gd = dev(np.linspace(0.25, 2.0, k, dtype=np.float32)) if with_gain else None
+    q1, s1 = B.rmsnorm_quant_act(xd, gd, norm_eps=1e-6)
+    q2, s2 = B.rmsnorm_quant_act(xs, gd, norm_eps=1e-6)
+    assert torch.equal(q1, q2)
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    check_norm_quant(x_device(x, xdt)[1], None if gd is None else host(gd), np.float32(1e-6),
+                     host(q1), host(s1), f"register kernel m={m} k={k}")
+
+
 NQ_CASES = [
     # m, k, x dtype, gain, norm eps
     (1, 8, "bf16", True, 2.0 ** -23),
