@@ -460,6 +460,59 @@ def run_stack_c3(B, torch):
             "per_batch": out}
 
 
+def run_rmsnorm(B, torch):
+    """RMSNorm ahead of the activation quantization: each 2B-class input group
+    as one fused decode launch without and with RMSNorm (a gain), at 1, 8 and
+    64 tokens over the stack's 60 layer copies; and bitlinear_rmsnorm_quant_act
+    against bitlinear_quant_act at decode and prefill sizes."""
+    import datagen
+    wl = datagen.WORKLOADS["c3"]
+    W = Weights(B, torch, wl, copies=2 * wl.layers)
+    gains = {g: torch.linspace(0.5, 1.5, wl.input_k(g), device="cuda") for g in wl.groups()}
+    fused = {}
+    for m in (1, 8, 64):
+        X = Inputs(B, torch, W, m)
+        ws = B.Workspace()
+        for grp in LAYER_GROUPS:
+            row = {}
+            for norm in (False, True):
+                def call(c, grp=grp, norm=norm):
+                    ops = []
+                    for nm in grp:
+                        d = W.mats[nm]
+                        o = dict(x=X.x[d["group"]], packed=d["packed"][c % len(d["packed"])],
+                                 gamma=d["gamma"], n=d["n"], k=d["k"], y=X.y[nm], relu2=d["relu2"])
+                        if norm:
+                            o.update(rmsnorm=True, norm_weight=gains[d["group"]])
+                        ops.append(o)
+                    return B.FusedStep(ops, workspace=ws)()
+                row["rmsnorm" if norm else "plain"] = time_launches(torch, call, 2 * wl.layers,
+                                                                   2 * wl.layers)["median"]
+            fused[f"{'+'.join(grp)} m={m}"] = row
+        del X, ws
+    del W
+    torch.cuda.empty_cache()
+    quant = {}
+    for m, k in ((1, 2560), (16, 8192), (16, 28672), (2048, 2560), (2048, 6912)):
+        xs = [torch.randn(m, k, device="cuda").to(torch.bfloat16) for _ in range(8)]
+        g = torch.linspace(0.5, 1.5, k, device="cuda")
+        xq = torch.empty((m, B.padded_k(k)), dtype=torch.int8, device="cuda")
+        sc = torch.empty(m, dtype=torch.float32, device="cuda")
+        q = lambda c: B._check("bitlinear_quant_act", B.lib.bitlinear_quant_act(
+            xs[c].data_ptr(), B.BL_BF16, m, k, B.EPS_DEFAULT, xq.data_ptr(), sc.data_ptr(),
+            B._stream()))
+        rq = lambda c: B._check("bitlinear_rmsnorm_quant_act", B.lib.bitlinear_rmsnorm_quant_act(
+            xs[c].data_ptr(), B.BL_BF16, m, k, g.data_ptr(), B.NORM_EPS_DEFAULT, B.EPS_DEFAULT,
+            xq.data_ptr(), sc.data_ptr(), B._stream()))
+        quant[f"{m}x{k}"] = {"quant_us": time_launches(torch, q, 8, 16)["median"],
+                             "rmsnorm_quant_us": time_launches(torch, rq, 8, 16)["median"]}
+        del xs
+    return {"workload": "2B-class input groups (q/k/v, o, up, down) as fused decode launches "
+                        "without / with RMSNorm (fp32 gain), 60 layer copies rotating; bf16 "
+                        "activation rows through quant_act / rmsnorm_quant_act",
+            "fused_step_us": fused, "act_quant": quant}
+
+
 # ---------------------------------------------------------- CPU baseline --
 def run_cpu_baseline(W, budget_s=8.0):
     """The oracle as it stands on the headline step (one token through the
@@ -950,6 +1003,8 @@ def main():
         log(f"prefill: {extra['prefill']['TOPS']} TOPS")
         extra["c2"] = run_c2(B, torch)
         extra["stack_c3"] = run_stack_c3(B, torch)
+        extra["rmsnorm"] = run_rmsnorm(B, torch)
+        log("rmsnorm leg done")
     line = {
         "metric": "BitLinear W1.58A8 decode GB/s (% HBM peak) + prefill TOPS (% int8 MFMA)",
         "value": round(value, 2),
