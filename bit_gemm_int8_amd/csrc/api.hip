@@ -510,6 +510,20 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
   bool norm = false;
   for (int i = 0; i < nops; ++i) norm = norm || ops[i].rmsnorm != 0;
   if (m <= 2 && stream_fused_plan(ops, nops, m, norm, &p)) return p;
+  // One RMSNorm product with activation rows of more than 8 KiB from 3
+  // tokens: normalizing tok rows of K in every workgroup of a token block
+  // (about three times the VALU work of the plain quantization) costs more
+  // than quantizing once in the two-pass plan (measured on MI355X: 2B-class
+  // down at 8-64 tokens 14.0-16.2 -> 10.3-13.3 us, 100B-class o and up at
+  // 4-48 tokens 14.9-47.2 -> 11.7-27.3 us; 2B-class o and up with 5 KB rows
+  // about even, and tables of several products faster fused, e.g. the
+  // 100B-class q/k/v at 16 tokens 19.9 fused against 21.7 us).
+  if (m >= 3 && nops == 1 && ops[0].rmsnorm &&
+      ops[0].k * (ops[0].x_dtype == BL_BF16 ? 2 : 4) > 8 * 1024) {
+    p.norm = true;
+    two_pass_plan(ops, nops, m, &p);
+    return p;
+  }
   if ((m >= 3 || norm) && m <= BL_FUSED_MAX_M && mt_fused_plan(ops, nops, m, norm, &p)) return p;
   if (m >= 3) {
     bool long_rows = false;                          // an activation row of more than 16 KiB

@@ -253,7 +253,8 @@ bl_status bitlinear_forward_multi(const int8_t* xq, const float* scale, int64_t 
  * cache once, or twice when a row does not fit its registers; meant for
  * decode-sized batches.  From 3 tokens no workspace is needed (the size
  * query returns 0), except for tables with an activation row of more than
- * 16 KiB (bf16 K > 8192, fp32 K > 4096): there every distinct input is
+ * 16 KiB (bf16 K > 8192, fp32 K > 4096), and for a single RMSNorm entry
+ * with rows of more than 8 KiB: there every distinct input is
  * quantized once by its own launch (into xq_out / scale_out when the entry
  * gives them, else into the workspace), each product then runs its
  * bitlinear_forward plan, and a last launch clears the workspace scratch, so

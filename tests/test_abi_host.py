@@ -293,7 +293,9 @@ def _fake_table(bl, specs, x_offset=0):
     (1, [(28672, 8192, "bf16", False)], 0, "stream_gemv"),
     (1, [(300, 512, "bf16", False)], 0, "dot4_gemv"),                    # short rows
     (8, [(2560, 2560, "bf16", False), (640, 2560, "bf16", False)], 0, "stream_mt"),
-    (64, [(2560, 6912, "bf16", True)], 0, "stream_mt"),
+    (64, [(2560, 6912, "bf16", True)], 0, "two_pass"),                  # one RMSNorm product, 13.5 KiB rows
+    (64, [(2560, 6912, "bf16", True), (640, 6912, "bf16", True)], 0, "stream_mt"),
+    (8, [(2560, 2560, "bf16", True)], 0, "stream_mt"),                    # RMSNorm, 5 KiB rows
     (33, [(1000, 4096, "f32", False)], 0, "stream_mt"),
     (8, [(1000, 4096, "f32", False)], 4, "mfma_gemv"),                   # x not 16-byte aligned
     (16, [(2048, 8200, "f32", False)], 0, "two_pass"),                   # fp32 row past 16 KiB

@@ -195,9 +195,12 @@ def test_fused_rmsnorm(B, case):
     _fused_norm_case(B, m, specs, seed=8000 + m * 7 + len(specs), shared=shared)
 
 
-@pytest.mark.parametrize("m,k,xdt", [(1, 4096, "bf16"), (8, 4096, "bf16"), (20, 8192, "bf16"),
-                                      (40, 4096, "f32"), (3, 2560, "bf16")])
-def test_rmsnorm_fused_equals_two_step(B, m, k, xdt):
+@pytest.mark.parametrize("m,k,xdt,nent,kernel", [
+    (1, 4096, "bf16", 1, "stream_gemv"), (8, 4096, "bf16", 1, "stream_mt"),
+    (20, 8192, "bf16", 2, "stream_mt"),            # rows of 16 units per lane
+    (40, 4096, "f32", 2, "stream_mt"), (3, 2560, "bf16", 1, "stream_mt"),
+    (16, 6912, "bf16", 1, "two_pass")])
+def test_rmsnorm_fused_equals_two_step(B, m, k, xdt, nent, kernel):
     """The fused step with RMSNorm gives the same bits as
     bitlinear_rmsnorm_quant_act followed by bitlinear_forward: x~, s, the
     accumulator and y.  From 3 tokens the fused kernel sums the squares in
@@ -217,10 +220,15 @@ def test_rmsnorm_fused_equals_two_step(B, m, k, xdt):
     acc = torch.empty((m, n), dtype=torch.int32, device="cuda")
     xq1 = torch.full((m, O.padded_k(k)), 99, dtype=torch.int8, device="cuda")
     s1 = torch.empty(m, dtype=torch.float32, device="cuda")
-    step = B.FusedStep([dict(x=xd, packed=packed, gamma=gamma, n=n, k=k, y=y, acc_out=acc,
-                             xq_out=xq1, scale_out=s1, rmsnorm=True, norm_weight=gd,
-                             norm_eps=1e-5)])
-    log(f"fused rmsnorm vs two-step m={m} k={k} {xdt} kernel={step.kernel()}")
+    ops = [dict(x=xd, packed=packed, gamma=gamma, n=n, k=k, y=y, acc_out=acc, xq_out=xq1,
+                scale_out=s1, rmsnorm=True, norm_weight=gd, norm_eps=1e-5)]
+    if nent == 2:                                     # a second product on the same rows
+        ops.append(dict(x=xd, packed=packed, gamma=gamma, n=640, k=k,
+                        y=torch.empty((m, 640), dtype=torch.bfloat16, device="cuda"),
+                        rmsnorm=True, norm_weight=gd, norm_eps=1e-5))
+    step = B.FusedStep(ops)
+    log(f"fused rmsnorm vs two-step m={m} k={k} {xdt} entries={nent} kernel={step.kernel()}")
+    assert step.kernel() == kernel
     step()
     xq, s = B.rmsnorm_quant_act(xd, gd, norm_eps=1e-5)
     y2, acc2 = B.forward(xq, s, packed, gamma, n, k, out_dtype=torch.bfloat16, acc_out=True)
