@@ -253,8 +253,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_kernel(
 // A table of products sharing the tokens (FusedArgs; `splits` of an entry
 // holds its workgroup count, P row ranges x TB token blocks).  A workgroup
 // quantizes its block's activation rows into LDS, one wave per token:
-//   1. the token's row is loaded (XR 16-byte units per lane, clamped: units
-//      past the row repeat the last, which the max ignores), then the first
+//   1. an RMSNorm entry's gain, then the token's row (XR 16-byte units per
+//      lane by range-checked buffer loads: units past the row read as zeros,
+//      which change neither the max nor the sum of squares), then the first
 //      D weight units;
 //   2. with RMSNorm (entries flagged for it; the BitLinear listing of
 //      "End-to-End Implementation: Building a Native BitLinear Layer"
