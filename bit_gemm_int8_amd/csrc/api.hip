@@ -492,20 +492,14 @@ static void two_pass_plan(const bl_linear* ops, int nops, int64_t m, FusedPlan* 
   p->ws_bytes = off;
 }
 
+// The fused step's plan, in this order: at 1-2 tokens the streaming kernel
+// when it takes the table; one RMSNorm product with rows of more than 8 KiB
+// from 3 tokens, the two-pass plan; from 3 tokens (and RMSNorm tables at
+// 1-2 tokens that the streaming kernel does not take) the multi-token
+// kernel; rows of more than 16 KiB from 3 tokens, the two-pass plan; then
+// the fused windowed matrix-core kernel from 3 tokens or with RMSNorm, and
+// the dot4 decode kernel otherwise.
 FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
-  // T = super-chunks a workgroup should stream: the set's total over ~512
-  // groups, kept within [8, 32].  Entries with up to 2T super-chunks keep
-  // one group per row block; longer ones are split (atomic combine) into
-  // ~T-chunk ranges, at two tokens in large sets (T >= 16) at most 2 (each
-  // split re-reads both activation rows for the absmax).  4 waves per group,
-  // except 8 for large two-token sets with a split entry.  (At one token 4
-  // waves measured 9-18% faster than 8 on the 100B-class up and down; at two
-  // tokens, up 4 waves -14%, down 2 splits x 8 waves -23%.)  Rows per group:
-  // 16 (four lanes per row) when that keeps the set within 512 groups, else
-  // 64 (a lane per row): small sets
-  // are bound by each lane's unpack + dot4 work after the data arrive, large
-  // ones by the number of groups, each of which reads and quantizes its x
-  // range.  (Tuned on MI355X over the 2B- and 100B-class shapes.)
   FusedPlan p;
   bool norm = false;
   for (int i = 0; i < nops; ++i) norm = norm || ops[i].rmsnorm != 0;
@@ -535,8 +529,8 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
       return p;
     }
   }
-  // RMSNorm tables the streaming kernel does not take run on the matrix-core
-  // fused kernel at any token count
+  // RMSNorm tables that none of the kernels above takes run on the
+  // matrix-core fused kernel at any token count
   p.norm = norm;
   if (m >= 3 || norm) {
     // Matrix cores: two 16-row groups x 4 K-slices per workgroup, or for
@@ -556,6 +550,19 @@ FusedPlan fused_plan(const bl_linear* ops, int nops, int64_t m) {
     }
     return p;
   }
+  // The dot4 decode kernel.  T = super-chunks a workgroup should stream:
+  // the set's total over ~512 groups, kept within [8, 32].  Entries with up
+  // to 2T super-chunks keep one group per row block; longer ones are split
+  // (atomic combine) into ~T-chunk ranges, at two tokens in large sets
+  // (T >= 16) at most 2 (each split re-reads both activation rows for the
+  // absmax).  4 waves per group, except 8 for large two-token sets with a
+  // split entry.  (At one token 4 waves measured 9-18% faster than 8 on the
+  // 100B-class up and down; at two tokens, up 4 waves -14%, down 2 splits x
+  // 8 waves -23%.)  Rows per group: 16 (four lanes per row) when that keeps
+  // the set within 512 groups, else 64 (a lane per row): small sets are
+  // bound by each lane's unpack + dot4 work after the data arrive, large
+  // ones by the number of groups, each of which reads and quantizes its x
+  // range.  (Tuned on MI355X over the 2B- and 100B-class shapes.)
   int64_t units = 0;
   for (int i = 0; i < nops; ++i) units += cdiv(ops[i].n, kRowBlock) * cdiv(ops[i].k, kSuperK);
   int64_t t = cdiv(units, 512);
