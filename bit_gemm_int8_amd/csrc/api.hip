@@ -380,7 +380,10 @@ static bool mt_fused_plan(const bl_linear* ops, int nops, int64_t m, bool norm, 
   // 100B-class groups at 16, 32 and 64 tokens, where it picks the faster
   // size every time: 8-token blocks are 9-17% faster on the 2B set at 16-32
   // tokens and win at 64 tokens on short outputs and long rows; 16-token
-  // blocks win on the large 100B outputs).
+  // blocks win on the large 100B outputs).  An RMSNorm row costs about three
+  // times the VALU work (fp64 squares, two gain multiplies per pass), so its
+  // elements count three times (2B-class q/k/v and up with RMSNorm at 64
+  // tokens: 8-token blocks 9.9 / 10.4 us against 11.0 / 11.3 us with 16).
   // RMSNorm entries with a gain stage it in LDS (the longest such row)
   int64_t gain_k = 0;
   for (int i = 0; i < nops; ++i)
@@ -404,7 +407,7 @@ static bool mt_fused_plan(const bl_linear* ops, int nops, int64_t m, bool norm, 
     double cost = 0.0;
     for (int i = 0; i < nops; ++i) {
       const int64_t subs = cdiv(ops[i].n, kRowBlock) * 4;
-      const double c = (double)(t < m ? t : m) * (double)ops[i].k / 620.0 +
+      const double c = (double)(t < m ? t : m) * (double)ops[i].k / (ops[i].rmsnorm ? 207.0 : 620.0) +
                        (double)(cdiv(subs, q[i]) * cdiv(ops[i].k, kSuperK));
       if (c > cost) cost = c;
     }
