@@ -271,3 +271,51 @@ def test_bitlinear_module_page_harness_shapes(B, rmsnorm):
                 if np.all(np.abs(yg[i] - r2[i]) <= 1e-5 * np.abs(r2[i])):
                     ref[i] = r2[i]
         assert_y_close(yg, ref, "f32", f"module {shape}")
+
+
+@pytest.mark.parametrize("k,n,relu2,m,kernel", [
+    (2560, 6912, True, 1, "stream_gemv"), (2560, 6912, True, 8, "stream_mt"),
+    (6912, 2560, False, 16, "two_pass"), (6912, 2560, False, 80, None),
+    (2560, 6912, True, 72, None)])
+def test_bitlinear_module_2b_shapes(B, k, n, relu2, m, kernel):
+    """BitLinearW158A8 at the 2B-class up and down shapes with an RMSNorm
+    gain, bf16 activations and fp32 outputs: one token (streaming kernel),
+    8 tokens (multi-token kernel), the down product at 16 tokens (two-pass
+    plan), and past 64 tokens (bitlinear_rmsnorm_quant_act, then
+    bitlinear_forward); every output against the oracle."""
+    import torch
+    from datagen import bf16_bits_to_f32, to_bf16_bits
+    w, x = random_case(8600 + m, m, n, k, x_kind="t3")
+    bits = to_bf16_bits(x)
+    xo = bf16_bits_to_f32(bits)
+    layer = B.BitLinearW158A8(k, n, relu2=relu2, out_dtype=torch.float32).load_weight(dev(w))
+    gain = np.linspace(0.5, 1.5, k, dtype=np.float32)
+    layer.norm_weight = dev(gain)
+    if kernel is not None:
+        probe = B.FusedStep([dict(x=dev(bits.view(np.int16)).view(torch.bfloat16),
+                                  packed=layer.packed, gamma=layer.gamma, n=n, k=k,
+                                  y=torch.empty((m, n), dtype=torch.float32, device="cuda"),
+                                  rmsnorm=True, norm_weight=layer.norm_weight)])
+        assert probe.kernel() == kernel
+    y = layer(dev(bits.view(np.int16)).view(torch.bfloat16))
+    assert tuple(y.shape) == (m, n) and y.dtype == torch.float32
+    yg = host(y)
+    g = host(layer.gamma)[0]
+    assert gamma_agrees(g, w)
+    codes = O.ternary_codes(w, g)
+
+    def ref_of(ms):
+        oq, os_ = O.quant_act(O.rmsnorm(xo, gain, np.float32(B.NORM_EPS_DEFAULT), ms))
+        return O.round_output(O.dequant(O.contract(oq, codes), g, os_, relu2), "f32")
+    ms, other = ms_candidates(xo)
+    ref = ref_of(ms)
+    for i, alt in enumerate(other):                # either rounding of an ambiguous mean square
+        if alt is not None:
+            ms2 = ms.copy()
+            ms2[i] = alt
+            r2 = ref_of(ms2)
+            if np.all(np.abs(yg[i] - r2[i]) <= 1e-5 * np.abs(r2[i])):
+                ref[i] = r2[i]
+    log(f"module k={k} n={n} m={m}")
+    assert_y_close(yg, ref, "f32", f"module {k}->{n} m={m}")
+
