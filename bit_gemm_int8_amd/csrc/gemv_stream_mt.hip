@@ -393,16 +393,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
       if (rowo != nullptr) rowo[u] = d0;
     }
   };
-  // the gain into LDS before any wave normalizes
-  if (NORM && have_w) {
-    uint4* g4 = reinterpret_cast<uint4*>(gl);
-#pragma unroll
-    for (int h = 0; h < GPT; ++h) {
-      const int i = (int)threadIdx.x + NT * h;
-      if (i < k / 4) g4[i] = gv[h];
-    }
-    __syncthreads();
-  }
   // y = fp32(fp32(x * r) * w) of held unit j (RMSNorm); past the row x is 0
   // and so is y
   auto normed = [&](int j, float rn, uint32_t (&v)[8]) __attribute__((always_inline)) {
@@ -422,34 +412,61 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
     for (int e = 0; e < EPU; ++e) v[e] = __float_as_uint(rms_apply(__uint_as_float(v[e]), rn, w[e]));
   };
 
-  for (int t = wave; t < mb; t += WAVES) {
+  // one token per wave (TBK <= WAVES): wave t's row was loaded at the start
+  static_assert(TBK <= WAVES, "one token per wave");
+  const int t = wave;
+  const bool has_tok = t < mb;
+  // 2. with RMSNorm, the fp64 sum of squares of the held row, before the
+  //    gain is needed.  bitlinear_rmsnorm_quant_act puts unit u on thread
+  //    u % 256 of 256, each thread adding its units' squares in order, then
+  //    sums each 64-thread wave by xor butterfly and the four waves in
+  //    order; lane l holds units l + 64 j, the units of thread l + 64 (j % 4)
+  //    in order, so four partial sums give the same fp64 total, bit for bit
+  //    (units past the row add +0).
+  float rn = 1.0f;
+  if (NORM && nrm && has_tok) {
+    double part[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int j = 0; j < XR; ++j) {
+      uint32_t v[8];
+      expand(xr[j], v);
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) {
+        const double d = (double)__uint_as_float(v[e]);
+        part[j & 3] += d * d;
+      }
+    }
+    // the four xor butterflies step by step together (each partial sum
+    // takes the same additions as a butterfly of its own; the four
+    // exchanges of a step are in flight at once), then added in order
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      double s[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[c] = __shfl_xor(part[c], o);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) part[c] += s[c];
+    }
+    rn = rms_factor(((part[0] + part[1]) + part[2]) + part[3], k, sg.norm_eps);
+  }
+  // the gain into LDS (its loads were issued first and have had the sums'
+  // time to arrive), before any wave normalizes
+  if (NORM && have_w) {
+    uint4* g4 = reinterpret_cast<uint4*>(gl);
+#pragma unroll
+    for (int h = 0; h < GPT; ++h) {
+      const int i = (int)threadIdx.x + NT * h;
+      if (i < k / 4) g4[i] = gv[h];
+    }
+    __syncthreads();
+  }
+  if (has_tok) {
     const bool out = first && sg.xq_out != nullptr;
     uint32_t* rowo = out ? reinterpret_cast<uint32_t*>(sg.xq_out + (int64_t)(tok0 + t) * kpad)
                          : nullptr;
     float sv;
     if (NORM && nrm) {
-      // 2-4 with RMSNorm from the held row.  bitlinear_rmsnorm_quant_act
-      // puts unit u on thread u % 256 of 256, each thread adding its units'
-      // squares in order, then sums each 64-thread wave by xor butterfly
-      // and the four waves in order; lane l holds units l + 64 j, the units
-      // of thread l + 64 (j % 4) in order, so four partial sums give the
-      // same fp64 total, bit for bit (units past the row add +0).
-      if (t != wave) load_row(t, xr);
-      double part[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int j = 0; j < XR; ++j) {
-        uint32_t v[8];
-        expand(xr[j], v);
-#pragma unroll
-        for (int e = 0; e < EPU; ++e) {
-          const double d = (double)__uint_as_float(v[e]);
-          part[j & 3] += d * d;
-        }
-      }
-      double tot = wave_sum_f64(part[0]);
-#pragma unroll
-      for (int c = 1; c < 4; ++c) tot += wave_sum_f64(part[c]);
-      const float rn = rms_factor(tot, k, sg.norm_eps);
+      // 3-4 with RMSNorm: beta = max|y|, then x~ of y
       uint32_t mx = 0;
 #pragma unroll
       for (int j = 0; j < XR; ++j) {
@@ -476,7 +493,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_mt_fused_kernel(
       }
     } else {
       // 3-4 from the held row
-      if (t != wave) load_row(t, xr);
       uint32_t acc[2] = {0u, 0u};
 #pragma unroll
       for (int j = 0; j < XR; ++j) unit_max(acc, xr[j]);
