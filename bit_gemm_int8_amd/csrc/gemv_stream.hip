@@ -101,13 +101,31 @@ __device__ __forceinline__ void stream_units(uint4 (&buf)[D], Cursor& cur, const
     }
     acc = bl_v4i{0, 0, 0, 0};
   };
+  // x~ of the unit being consumed, read from LDS one unit ahead so that the
+  // MFMAs do not wait for LDS (the read past the last unit is in range: it
+  // wraps to super-chunk 0)
+  auto x_addr = [&](int c) __attribute__((always_inline)) {
+    return r < M ? r * kp16 + c * 16 + g : zero_idx + g;
+  };
+  uint4 xn[4];
+  {
+    const int xa = x_addr(cc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xn[j] = xs[xa + 4 * j];
+  }
   auto consume = [&](const uint4& w) __attribute__((always_inline)) {
-    const int xa = r < M ? r * kp16 + cc * 16 + g : zero_idx + g;
+    uint4 xc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xc[j] = xn[j];
+    {
+      const int xa = x_addr(cc + 1 == nc ? 0 : cc + 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xn[j] = xs[xa + 4 * j];
+    }
     const uint32_t wj[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint4 x4 = xs[xa + 4 * j];
-      const bl_v4i xv = {(int)x4.x, (int)x4.y, (int)x4.z, (int)x4.w};
+      const bl_v4i xv = {(int)xc[j].x, (int)xc[j].y, (int)xc[j].z, (int)xc[j].w};
       const bl_v4i a = {(int)unpack_x64(wj[j], 0), (int)unpack_x64(wj[j], 1),
                         (int)unpack_x64(wj[j], 2), (int)unpack_x64(wj[j], 3)};
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, xv, acc, 0, 0, 0);
@@ -311,9 +329,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_fused_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) rn[m] = 1.0f;
   if (nrm) {
+    double ss[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      double ss = 0.0;
+      ss[m] = 0.0;
 #pragma unroll
       for (int j = 0; j < XR; ++j) {
         if ((int)threadIdx.x + NT * j < nu) {
@@ -322,12 +341,24 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_fused_kernel(
 #pragma unroll
           for (int e = 0; e < EPU; ++e) {
             const double d = (double)__uint_as_float(v[e]);
-            ss += d * d;
+            ss[m] += d * d;
           }
         }
       }
-      ss = wave_sum_f64(ss);
-      if (lane == 0) red64[wave][m] = ss;
+    }
+    // the tokens' xor butterflies step by step together (each token's sum
+    // takes the same additions as a butterfly of its own)
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      double s[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) s[m] = __shfl_xor(ss[m], o);
+#pragma unroll
+      for (int m = 0; m < M; ++m) ss[m] += s[m];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) red64[wave][m] = ss[m];
     }
     __syncthreads();
 #pragma unroll
