@@ -174,9 +174,25 @@ __host__ __device__ constexpr int stream_zero_idx(int m, int kp16, int nsub_allo
   return m * kp16 + nsub_alloc * m * 4;
 }
 
+// Whether a launch stages x~ before it requests any weight (XF).  At the
+// start of a launch every workgroup asks for its x~ and its first weight
+// units together: some 12 MB of weight requests queue at the memory
+// channels, and x~, which every workgroup needs before its first MFMA,
+// waits behind them.  On one-token rows of >= 64 super-chunks (x~ >= 16 KiB
+// per workgroup) that delay measured longer than what the early weight
+// requests save: workgroup timestamps put x~ in LDS 2.1-3.0 us after the
+// start on 8192 x 28672, and landing x~ first takes the launch from 12.5 to
+// 12.0 us (the fused form, whose activation row is 56 KiB, from 12.9 to
+// 12.45 us); on 28672 x 8192 (x~ 8 KiB) it measured 0.1-0.3 us slower.
+// (MI355X, medians of 25 graph replays over 11 rotating weight copies.)
+__host__ __device__ constexpr bool gemv_stream_xfirst(int m, int nc) { return m == 1 && nc >= 64; }
+
+// s_waitcnt immediate (gfx9 encoding) that waits for vmcnt = 0 only.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // ------------------------------------------------------------ plain GEMV --
 // x~ and s given.  Workgroup w owns sub-blocks [S w / G, S (w + 1) / G).
-template <int M, int WAVES, int D, int XR>
+template <int M, int WAVES, int D, int XR, bool XF>
 __global__ __launch_bounds__(64 * WAVES) void gemv_stream_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ scale,
     const uint4* __restrict__ packed, const float* __restrict__ gamma, int n, int nc, int S,
@@ -197,7 +213,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_kernel(
   const int zero_idx = stream_zero_idx(M, kp16, nsub_alloc);
 
   // x~ first (loads retire in issue order, so staging it then waits for it
-  // alone), clamped so that no load sits behind a branch
+  // alone), clamped so that no load sits behind a branch.  Without XF the
+  // first weight units are requested right behind it; with XF (long rows)
+  // x~ is in LDS before any weight is requested (see gemv_stream_xfirst).
   const int xu = M * kp16;
   const uint4* xg = reinterpret_cast<const uint4*>(xq);
   uint4 xr[XR];
@@ -205,7 +223,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_kernel(
   for (int j = 0; j < XR; ++j) xr[j] = xg[min((int)threadIdx.x + NT * j, xu - 1)];
   uint4 buf[D];
   Cursor cur = cursor_at(packed, nc, t0, u0, u1, g, r);
-  prefetch_units<D>(buf, cur, packed, nc, g, r);
+  if constexpr (!XF) prefetch_units<D>(buf, cur, packed, nc, g, r);
   const float gm = *gamma;
   float fac[M];
 #pragma unroll
@@ -217,6 +235,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_kernel(
     if (i < xu) lds[i] = xr[j];
   }
   for (int i = (int)threadIdx.x + NT * XR; i < xu; i += NT) lds[i] = xg[i];
+  if constexpr (XF) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch_units<D>(buf, cur, packed, nc, g, r);
+  }
   for (int i = threadIdx.x; i < nsub * M * 16; i += NT) sums[i] = 0;
   if (threadIdx.x < 16) lds[zero_idx + threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
@@ -234,7 +257,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_kernel(
 // quantizes its entry's whole activation rows into LDS before streaming:
 //   1. the activations are loaded first (XR 16-byte units per thread and
 //      token, clamped: the units past the row repeat the last one, which the
-//      max ignores), then the first D weight units;
+//      max ignores), then the first D weight units (on long one-token rows
+//      once the activations have arrived);
 //   2. beta = max|x| per token (absmax_bf16x2 / absmax_f32x2, DPP in the
 //      wave, LDS across waves) and s = fp32(127 / max(beta, eps)) exactly as
 //      bitlinear_quant_act computes it;
@@ -307,6 +331,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_stream_fused_kernel(
 #pragma unroll
       for (int h = 0; h < WPU; ++h)
         wr[j][h] = wsrc[min((int)threadIdx.x + NT * j, nu - 1) * WPU + h];
+  }
+  // one token with 8 units a thread (rows past 16384 inputs at 8 waves):
+  // the activations land before any weight is requested (gemv_stream_xfirst)
+  if constexpr (M == 1 && XR >= 8) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   uint4 buf[D];
   Cursor cur = cursor_at(packed, nc, t0, u0, u1, g, r);
@@ -492,9 +522,14 @@ template <int M, int WAVES, int D, int XR>
 void run_stream(const int8_t* xq, const float* scale, const uint32_t* packed,
                 const float* gamma, int n, int nc, int S, int G, int nsub_alloc, bool relu2,
                 bool bf16, void* y, int32_t* acc_out, size_t lds, hipStream_t stream) {
-  gemv_stream_kernel<M, WAVES, D, XR><<<G, 64 * WAVES, lds, stream>>>(
-      xq, scale, reinterpret_cast<const uint4*>(packed), gamma, n, nc, S, G, nsub_alloc,
-      relu2, bf16, y, acc_out);
+  if (gemv_stream_xfirst(M, nc))
+    gemv_stream_kernel<M, WAVES, D, XR, true><<<G, 64 * WAVES, lds, stream>>>(
+        xq, scale, reinterpret_cast<const uint4*>(packed), gamma, n, nc, S, G, nsub_alloc,
+        relu2, bf16, y, acc_out);
+  else
+    gemv_stream_kernel<M, WAVES, D, XR, false><<<G, 64 * WAVES, lds, stream>>>(
+        xq, scale, reinterpret_cast<const uint4*>(packed), gamma, n, nc, S, G, nsub_alloc,
+        relu2, bf16, y, acc_out);
 }
 
 template <int M, int WAVES, int D>
