@@ -182,10 +182,12 @@ __host__ __device__ constexpr int stream_zero_idx(int m, int kp16, int nsub_allo
 // per workgroup) that delay measured longer than what the early weight
 // requests save: workgroup timestamps put x~ in LDS 2.1-3.0 us after the
 // start on 8192 x 28672, and landing x~ first takes the launch from 12.5 to
-// 12.0 us (the fused form, whose activation row is 56 KiB, from 12.9 to
-// 12.45 us); on 28672 x 8192 (x~ 8 KiB) it measured 0.1-0.3 us slower.
-// (MI355X, medians of 25 graph replays over 11 rotating weight copies.)
-__host__ __device__ constexpr bool gemv_stream_xfirst(int m, int nc) { return m == 1 && nc >= 64; }
+// 12.0 us at one token, 13.0 to 12.4 us at two (the fused form at one token,
+// whose activation row is 56 KiB, from 12.9 to 12.45 us; at two tokens the
+// fused form did not move, so it keeps the early requests there); on
+// 28672 x 8192 (x~ 8 KiB) it measured 0.1-0.3 us slower.  (MI355X, medians
+// of 25 graph replays over 11 rotating weight copies.)
+__host__ __device__ constexpr bool gemv_stream_xfirst(int m, int nc) { return m <= 2 && nc >= 64; }
 
 // s_waitcnt immediate (gfx9 encoding) that waits for vmcnt = 0 only.
 constexpr int kWaitVmcnt0 = 0x0F70;
