@@ -178,9 +178,9 @@ __host__ __device__ constexpr int stream_zero_idx(int m, int kp16, int nsub_allo
 // start of a launch every workgroup asks for its x~ and its first weight
 // units together: some 12 MB of weight requests queue at the memory
 // channels, and x~, which every workgroup needs before its first MFMA,
-// waits behind them.  On one-token rows of >= 64 super-chunks (x~ >= 16 KiB
-// per workgroup) that delay measured longer than what the early weight
-// requests save: workgroup timestamps put x~ in LDS 2.1-3.0 us after the
+// waits behind them.  On rows of >= 64 super-chunks at one or two tokens
+// (x~ >= 16 KiB per workgroup) that delay measured longer than what the
+// early weight requests save: workgroup timestamps put x~ in LDS 2.1-3.0 us after the
 // start on 8192 x 28672, and landing x~ first takes the launch from 12.5 to
 // 12.0 us at one token, 13.0 to 12.4 us at two (the fused form at one token,
 // whose activation row is 56 KiB, from 12.9 to 12.45 us; at two tokens the
