@@ -581,8 +581,11 @@ void run_stream_fused_xr(int xr, const FusedArgs& args, const int (&wb)[14], int
   } else {
     if (xr <= 4)
       run_stream_fused<M, WAVES, D, 4, NORM>(args, wb, groups, lds, bf16, stream);
-    else
-      run_stream_fused<M, WAVES, D, 8, NORM>(args, wb, groups, lds, bf16, stream);
+    else  // 8 waves x 5 units on these long rows (100B-class down 12.57 -> 12.45 us
+          // against 6 in alternating runs on MI355X; 5 on the 8192-input rows
+          // made q/k/v and o slower)
+      run_stream_fused<M, WAVES, (WAVES == 8 && D == 6 ? 5 : D), 8, NORM>(args, wb, groups, lds,
+                                                                         bf16, stream);
   }
 }
 
@@ -616,9 +619,11 @@ void stream_shape(int m, int64_t nc, int* waves, int* depth) {
 
 // The fused form: 8 waves x 6 units in flight (wide = false), or 16 x 3 when
 // a token's activation row does not fit the registers of 8 waves (the plan
-// decides).  (Swept on MI355X over the 100B-class products and q/k/v at one
-// and two tokens: 8 x 6 against the plain shapes 2-3.5% faster at one token,
-// 7-14% at two.)
+// decides); one-token rows of 8 units a thread take 5 units in flight
+// (run_stream_fused_xr).  (Swept on MI355X over the 100B-class products and
+// q/k/v at one and two tokens: 8 x 6 against the plain shapes 2-3.5% faster
+// at one token, 7-14% at two; 8 x 5 and 8 x 7 against 8 x 6 on the whole
+// one-token layer step.)
 void stream_fused_shape(bool wide, int* waves, int* depth) {
   *waves = wide ? 16 : 8;
   *depth = wide ? 3 : 6;
