@@ -740,7 +740,9 @@ def pmc_driver(B, torch, args):
     """Launches to read counters or traces from.
     c5gemv: a plain copy of COPY_BYTES (the counter calibration), then the
             fused up and down launches of the headline, `steps` each, over
-            their rotating copies (one token);
+            their rotating copies (one token); with --graph one eager launch,
+            then graphs of one launch per copy, replayed steps // copies
+            times (the roofline leg's timing);
     step:   `steps` headline decode steps (eager);
     prefill: the two 2048-token prefill GEMMs, `steps` times each;
     mfma:   the copy calibration, then bitlinear_forward at --m tokens on the
@@ -799,8 +801,23 @@ def pmc_driver(B, torch, args):
     else:
         for nm in ("up", "down"):
             calls = [fused_call(B, W, X, (nm,), c, ws) for c in range(W.copies(nm))]
-            for i in range(args.steps):
-                calls[i % len(calls)]()
+            if args.graph:
+                # as the roofline leg times them: graphs of consecutive launches
+                # over the rotating copies, replayed (one eager launch first)
+                calls[0]()
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                s = torch.cuda.Stream()
+                with torch.cuda.graph(g, stream=s):
+                    for c in calls:
+                        c()
+                for _ in range(max(1, args.steps // len(calls))):
+                    g.replay()
+                torch.cuda.synchronize()
+                del g
+            else:
+                for i in range(args.steps):
+                    calls[i % len(calls)]()
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     print(json.dumps({"pmc_driver": args.pmc_driver, "steps": args.steps}))
@@ -963,6 +980,8 @@ def main():
                     choices=["c5gemv", "step", "prefill", "mfma", "c3"],
                     help="only launch what counters or traces are read from")
     ap.add_argument("--m", type=int, default=64, help="tokens for --pmc-driver mfma / c3")
+    ap.add_argument("--graph", action="store_true",
+                    help="--pmc-driver c5gemv: replay graphs of the launches instead of eager calls")
     ap.add_argument("--summarize", metavar="DIR", help="write profiles/ summaries from rocprofv3 CSVs")
     ap.add_argument("--name", default="gemv_fused_c5_updown",
                     help="kernel and workload the summaries are named for")
